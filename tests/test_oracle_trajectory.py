@@ -1,0 +1,100 @@
+"""Corollary 4 on the oracle's own compressed trajectories, and the byte accounting.
+
+Corollary 4 (picx.dev summary, "Open-Loop Error Bound (Corollary 4)"): with the same inputs
+driving both trajectories, |S~_t - S_t|_F <= eps_bar / (1 - g_bar^W), where eps_bar is the
+largest single compression error (the prefill-end one included) and g_bar the largest decay.
+W is read as the number of steps between compressions (= T).
+
+The byte accounting is pinned to the pages' state table (tests/golden/state_table.txt).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as orc
+import synth
+
+
+def _squeeze(xs):
+    return [{k: (v[0] if np.ndim(v) else v) for k, v in x.items()} for x in xs]
+
+
+def _run(kind, dk, dv, r, T, steps, prefill, seed):
+    w = synth.Workload("t", kind, 1, 1, dk, dv, r, T, steps, prefill, synth.F32, synth.F32)
+    xs = _squeeze(synth.sequence(w, seed, prefill + steps, units=1))
+    vbar = synth.head_consts(w, seed).vbar[0]
+    S0, _ = orc.run_dense(kind, np.zeros((dk, dv)), xs[:prefill])
+    return orc.run_compressed(kind, S0[-1], vbar, xs[prefill:], r, T), xs
+
+
+@pytest.mark.parametrize("kind,dk,dv,r,T", [
+    (orc.GDN, 64, 64, 8, 8),        # the small single-head GDN workload
+    (orc.GDN, 32, 32, 4, 4),
+    (orc.KDA, 32, 32, 6, 6),
+    (orc.MAMBA2, 32, 16, 4, 4),
+])
+def test_corollary4_bound_holds_along_the_trajectory(kind, dk, dv, r, T):
+    res, _ = _run(kind, dk, dv, r, T, steps=64, prefill=32, seed=17 + kind)
+    eps_bar = max(res["errs"])
+    g_bar = max(res["g_bound"])
+    bound = orc.corollary4_bound(eps_bar, g_bar, T)
+    errs = [np.linalg.norm(Sc - S) for Sc, S in zip(res["S_c"], res["S"])]
+    assert eps_bar > 0
+    assert max(errs) <= bound * (1 + 1e-9), (max(errs), bound)
+    # the bound does not grow with the number of compressions: errors stay flat in time
+    assert len(res["errs"]) == 1 + 64 // T
+
+
+def test_prefill_error_decays_without_further_compressions():
+    # with T beyond the horizon only the prefill-end error exists, and it shrinks by at most
+    # g_bar per step: |E_t| <= g_bar^t eps_0
+    res, _ = _run(orc.GDN, 16, 16, 3, 1000, steps=40, prefill=24, seed=5)
+    eps0 = res["errs"][0]
+    g_run = 1.0
+    for t, (Sc, S, gb) in enumerate(zip(res["S_c"], res["S"], res["g_bound"]), start=1):
+        g_run *= gb
+        assert np.linalg.norm(Sc - S) <= g_run * eps0 * (1 + 1e-9)
+
+
+def test_compressed_trajectory_compress_points_and_sink():
+    res, xs = _run(orc.GDN, 16, 16, 4, 4, steps=8, prefill=8, seed=3)
+    a, U, V = res["final"]
+    assert U.shape[1] == 4 and V.shape[1] == 4
+
+
+def _table(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "state_table.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            p = line.split()
+            rows.append((p[0], *map(float, p[1:5]), *map(int, p[5:8])))
+    return rows
+
+
+def test_state_bytes_reproduce_the_pages_state_table(golden_dir):
+    rows = _table(golden_dir)
+    assert len(rows) == 5
+    for name, dense, at_r, mean, peak, dk, dv, R in rows:
+        n0 = dense * 1e6 / (4 * dk * dv)
+        fits = []
+        for n in range(int(n0) - 3, int(n0) + 4):
+            if round(orc.dense_state_bytes(n, dk, dv) / 1e6, 1) != dense:
+                continue
+            got = [round(orc.state_bytes(n, dk, dv, m) / 1e6, 1) for m in (R, 1.5 * R, 2 * R)]
+            if got == [at_r, mean, peak]:
+                fits.append(n)
+        assert fits, f"{name}: no head count reproduces the printed row"
+        # and the compression ratio printed in the summary table (dense / at R)
+        assert round(dense / at_r, 1) in (3.9, 2.6, 2.0)
+
+
+def test_state_bytes_convention_is_discriminating(golden_dir):
+    # halving the bytes per value, or counting vbar, must break the fit for the first row
+    name, dense, at_r, mean, peak, dk, dv, R = _table(golden_dir)[0]
+    n = 1728
+    assert round(orc.state_bytes(n, dk, dv, R) / 1e6, 1) == at_r
+    assert round(orc.state_bytes(n, dk, dv, R, bytes_per=2) / 1e6, 1) != at_r
+    assert round((orc.state_bytes(n, dk, dv, R) + 4 * n * dv) / 1e6, 1) != at_r
