@@ -1,0 +1,183 @@
+/*
+ * seed.h - C ABI of the sink + rank-r recurrent decode state library (libseed.so, gfx950).
+ *
+ * Method (pages titled "Shallow Encoding Emits Deep Memories"):
+ *   - picx.dev summary, "SEED Architecture": each linear-attention / state-space head's
+ *     d_k x d_v recurrent state is held as S = a vbar^T + U V^T, where vbar (d_v) is a fixed
+ *     per-head direction, a (d_k) is the sink coefficient and U (d_k x m), V (d_v x m) are
+ *     content factors with r <= m <= r + T columns.
+ *   - picx.dev summary, "Exact Update (Lemma 2)": one decode step decays and projects a,
+ *     decays U and appends one column to each factor, exactly.
+ *   - thelatestinai.com figures & tables, overview table: the read-out and the update work on
+ *     the factors, and a compression brings them back to rank r every T steps; a state that
+ *     leaves the prefill is brought to the sink + rank-r form once.
+ *
+ * Kinds. kind selects the recurrence; the arguments map as
+ *     kind            g (decay)                 beta      kappa (key)   v (value)   q (query)
+ *     SEED_GDN        alpha, one per unit       beta      k             v           q
+ *     SEED_KDA        alpha, d_k per unit       beta      k             v           q
+ *     SEED_MAMBA2     exp(dt*A), one per unit   dt        B             x           C
+ * with the dense recurrences
+ *     GDN / KDA:  S+ = G S + beta kappa (v - (G S)^T kappa)^T,   G = g I or Diag(alpha)
+ *     Mamba-2:    S+ = g S + beta kappa v^T
+ * and the read-out o = S+^T q after the update.
+ *
+ * Conventions (every entry point):
+ *   - Units. A call processes units = batch * heads independent (request, head) states, unit
+ *     u = b * heads + h. Per-head constants (vbar) are indexed by h = u % heads. A layer stack
+ *     is driven with one call per layer.
+ *   - Memory. Every pointer is a device pointer owned by the caller. The library allocates
+ *     nothing, keeps no pointer after a call returns and holds no mutable global state.
+ *   - Streams. stream is a hipStream_t (NULL = the null stream). Every call only enqueues work
+ *     on it and never synchronises. Calls on different streams that touch disjoint buffers may
+ *     run concurrently.
+ *   - Errors. Functions return SEED_OK (0) or a negative status. Argument errors are detected
+ *     on the host before anything is launched, and then nothing is written. SEED_ERR_HIP
+ *     reports a launch failure from the HIP runtime. Device-side faults surface, as with any
+ *     HIP kernel, at the next synchronising call. seed_status_string() names a status.
+ *   - Column count m. The caller keeps m (uniform over the batch): seed_state_from_dense
+ *     leaves m = r; seed_decode_step takes m (r <= m < r + T) and leaves m + 1;
+ *     seed_compress takes m and leaves r (nothing is done when m <= r).
+ *   - Data types. factor_dtype selects the storage of U and V (fp32, or bf16 rounded to
+ *     nearest-even); io_dtype the storage of q, k, v and o. a, scale, beta, g, vbar and dense
+ *     states are always fp32. Arithmetic is fp32 throughout.
+ *   - Supported shapes: d_k, d_v in {64, 128}; rank >= 1, period >= 1, rank + period <= 64.
+ *     Other shapes return SEED_ERR_UNSUPPORTED.
+ */
+#ifndef SEED_H
+#define SEED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SEED_OK = 0,
+  SEED_ERR_ARG = -1,          /* null pointer, bad m, non-positive size, unknown enum       */
+  SEED_ERR_UNSUPPORTED = -2,  /* shape or dtype not compiled into this library             */
+  SEED_ERR_WORKSPACE = -3,    /* workspace pointer null or smaller than seed_workspace_bytes */
+  SEED_ERR_HIP = -4           /* the HIP runtime refused a launch                          */
+};
+
+enum { SEED_GDN = 0, SEED_KDA = 1, SEED_MAMBA2 = 2 };
+enum { SEED_F32 = 0, SEED_BF16 = 1 };
+enum { SEED_OP_COMPRESS = 0, SEED_OP_FROM_DENSE = 1 };
+
+typedef struct seed_shape {
+  int32_t kind;          /* SEED_GDN, SEED_KDA or SEED_MAMBA2                                */
+  int32_t batch, heads;  /* units = batch * heads                                            */
+  int32_t d_k, d_v;      /* d_k: key side (Mamba-2 d_state), the side of a; d_v: value side   */
+  int32_t rank, period;  /* r and T: compression back to r columns every T steps             */
+  int32_t factor_dtype;  /* SEED_F32 or SEED_BF16: storage of U and V                        */
+  int32_t io_dtype;      /* SEED_F32 or SEED_BF16: storage of q, k, v and o                  */
+} seed_shape;
+
+/*
+ * Factored state. With C = r + T column slots per unit and s = seed_scale_len(shape):
+ *   a      float [units][d_k]      sink coefficient.
+ *   U      [units][C][d_k]         slot j holds column j of U, contiguous over d_k (factor_dtype).
+ *   V      [units][C][d_v]         slot j holds column j of V, contiguous over d_v (factor_dtype).
+ *   scale  float [units][s]        lazy decay of U, so that U is never rewritten by a decay:
+ *            GDN, Mamba-2 (s = 1 + T): the true column j of U is scale[0] * U[j] for j < r and
+ *              scale[1 + j - r] * U[j] for j >= r.
+ *            KDA (s = d_k): the true column j of U is scale (elementwise, per key channel) times
+ *              U[j], for every j.
+ *          seed_state_from_dense and seed_compress reset the scales to 1.
+ * The true state is a vbar^T + sum_{j<m} U_true[:, j] V[:, j]^T.
+ */
+typedef struct seed_state {
+  float *a;
+  void *U;
+  void *V;
+  float *scale;
+} seed_state;
+
+/* Bytes of one unit's state buffers for this shape (a + U + V + scale, all C slots), or 0 if
+ * the shape is invalid. Host-only, pure. */
+size_t seed_state_bytes(const seed_shape *shape);
+
+/* Length s of one unit's scale vector (1 + T, or d_k for KDA), or 0 if the shape is invalid. */
+int32_t seed_scale_len(const seed_shape *shape);
+
+/* Workspace bytes that an operation needs (op = SEED_OP_COMPRESS or SEED_OP_FROM_DENSE);
+ * 0 means the operation needs none. Host-only, pure. */
+size_t seed_workspace_bytes(const seed_shape *shape, int32_t op);
+
+/*
+ * Prefill-end compression of dense states into the factored form (leaves m = r).
+ *   S      float [units][d_k][d_v] dense states, row i = key channel i (read only).
+ *   vbar   float [heads][d_v], every row non-zero (only its direction matters).
+ *   state  written: a = S vbar / |vbar|^2 (Lemma 1's sink split); U, V = the best rank-r
+ *          approximation of the content C = S - a vbar^T, with sqrt(sigma_i) on both factors,
+ *          and zero columns where C has rank below r; scales reset to 1.
+ *   ws     workspace of seed_workspace_bytes(shape, SEED_OP_FROM_DENSE) bytes (may be NULL
+ *          when that is 0).
+ * When min(d_k, d_v) <= 64 the truncation is exact up to fp32 rounding. For 128 x 128 states
+ * the leading 64-dimensional right singular subspace is first found by block subspace
+ * iteration on C^T C (fixed count, see seed_from_dense_iterations), then truncated exactly.
+ * Source: thelatestinai.com figures & tables, overview table (states leaving the prefill are
+ * compressed to the sink plus rank-r factors); picx.dev summary, Lemma 1.
+ */
+int seed_state_from_dense(const seed_shape *shape, const float *S, const float *vbar,
+                          const seed_state *state, void *ws, size_t ws_bytes, void *stream);
+
+/* Subspace-iteration count used by seed_state_from_dense for 128 x 128 states. */
+int32_t seed_from_dense_iterations(void);
+
+/*
+ * One factored decode step for every unit: read-out and exact update (Lemma 2).
+ *   m      columns held before the step, rank <= m < rank + period.
+ *   q, k   [units][d_k] (io_dtype); v [units][d_v] (io_dtype).
+ *   beta   float [units]. g: float [units] (GDN, Mamba-2) or float [units][d_k] (KDA).
+ *   vbar   float [heads][d_v].
+ *   o      written, [units][d_v] (io_dtype): o = vbar (a+^T q) + V+ (U+^T q).
+ *   state  a is decayed and projected, the scales take the decay, column m of U receives the
+ *          key and column m of V receives beta (eps - V (G U)^T kappa) (GDN, KDA) or beta eps
+ *          (Mamba-2), with omega = v^T vbar / |vbar|^2 and eps = v - omega vbar.
+ * Afterwards the caller holds m + 1 columns. Source: picx.dev summary, "Exact Update
+ * (Lemma 2)" and "SEED Architecture".
+ */
+int seed_decode_step(const seed_shape *shape, const seed_state *state, int32_t m,
+                     const void *q, const void *k, const void *v, const float *beta,
+                     const float *g, const float *vbar, void *o, void *stream);
+
+/*
+ * Compression of the content back to rank r (leaves m = r; nothing is done when m <= r).
+ * The content U V^T (m columns) is replaced by its best rank-r approximation, with
+ * sqrt(sigma_i) on both factors; a is not touched; scales reset to 1. Method: lazy decay
+ * folded into U; column pairs balanced; Grams G_U = U^T U and G_V = V^T V; pivoted Cholesky
+ * G_U ~ L L^T; the (k x k, k <= m) core B = L^T G_V L, whose eigenvalues are sigma_i^2,
+ * diagonalised by cyclic Jacobi; the top r eigenpairs give U' = U X_U and V' = V X_V.
+ * ws as for seed_state_from_dense with SEED_OP_COMPRESS.
+ * Source: picx.dev summary, "Open-Loop Error Bound (Corollary 4)" (periodic compressions)
+ * and thelatestinai.com figures & tables, overview table (compression back to rank r).
+ */
+int seed_compress(const seed_shape *shape, const seed_state *state, int32_t m, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/*
+ * Dense-state step (the uncompressed baseline): S <- the dense recurrence of `kind`, then
+ * o = S^T q.
+ *   S      float [units][d_k][d_v], read once and written once.
+ *   q, k, v, beta, g, o as for seed_decode_step (factor_dtype, rank and period are ignored).
+ * Source: picx.dev summary, "Introduction and Theoretical Foundation" (every decode step
+ * loads and stores the whole state) and "Exact Update (Lemma 2)".
+ */
+int seed_dense_decode_step(const seed_shape *shape, float *S, const void *q, const void *k,
+                           const void *v, const float *beta, const float *g, void *o,
+                           void *stream);
+
+/* Static text for a status code. */
+const char *seed_status_string(int status);
+
+/* Library version string. */
+const char *seed_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEED_H */

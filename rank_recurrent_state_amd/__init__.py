@@ -1,0 +1,30 @@
+"""Sink + rank-r recurrent decode state on MI355X (gfx950).
+
+The library (libseed.so, hand-written HIP kernels behind a C ABI declared in include/seed.h)
+holds each Gated DeltaNet, Kimi Delta Attention or Mamba-2 head's recurrent state as a sink
+a vbar^T plus rank-r factors U V^T, runs the fused read-out + exact update per decode step,
+compresses back to rank r every T steps, and provides the dense-state step as a baseline.
+
+This package is the thin Python binding over that C ABI (rank_recurrent_state_amd._lib). The
+binding is loaded on first use of any of its names, and raises ImportError if libseed.so has
+not been built (python -m rank_recurrent_state_amd.build): there is no fallback path.
+"""
+import importlib
+
+_NAMES = {
+    "EXPORTS", "LIB_PATH", "SEED_BF16", "SEED_ERR_ARG", "SEED_ERR_HIP", "SEED_ERR_UNSUPPORTED",
+    "SEED_ERR_WORKSPACE", "SEED_F32", "SEED_GDN", "SEED_KDA", "SEED_MAMBA2", "SEED_OK",
+    "SEED_OP_COMPRESS", "SEED_OP_FROM_DENSE", "SeedError", "State", "make_shape",
+    "seed_compress", "seed_decode_step", "seed_dense_decode_step", "seed_from_dense_iterations",
+    "seed_scale_len", "seed_shape", "seed_state", "seed_state_bytes", "seed_state_from_dense",
+    "seed_status_string", "seed_version", "seed_workspace_bytes",
+}
+
+
+def __getattr__(name):
+    if name in _NAMES:
+        return getattr(importlib.import_module("._lib", __name__), name)
+    raise AttributeError(name)
+
+
+__all__ = sorted(_NAMES)

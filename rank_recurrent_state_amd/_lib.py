@@ -1,0 +1,231 @@
+"""ctypes binding of libseed.so (argument marshalling only).
+
+The functions carry the C names. Tensors are torch tensors used only as device memory: their
+data pointers and the current HIP stream are handed to the library, and every step of the
+computation runs in the library's gfx950 kernels. There is no CPU fallback: if libseed.so is
+missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libseed.so")
+
+SEED_OK, SEED_ERR_ARG, SEED_ERR_UNSUPPORTED, SEED_ERR_WORKSPACE, SEED_ERR_HIP = 0, -1, -2, -3, -4
+SEED_GDN, SEED_KDA, SEED_MAMBA2 = 0, 1, 2
+SEED_F32, SEED_BF16 = 0, 1
+SEED_OP_COMPRESS, SEED_OP_FROM_DENSE = 0, 1
+
+EXPORTS = [
+    "seed_state_bytes", "seed_scale_len", "seed_workspace_bytes", "seed_state_from_dense",
+    "seed_from_dense_iterations", "seed_decode_step", "seed_compress", "seed_dense_decode_step",
+    "seed_status_string", "seed_version",
+]
+
+
+class seed_shape(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("period", ctypes.c_int32), ("factor_dtype", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32)]
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.heads
+
+    @property
+    def slots(self) -> int:
+        return self.rank + self.period
+
+
+class seed_state(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("U", ctypes.c_void_p), ("V", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p)]
+
+
+class SeedError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {seed_status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m rank_recurrent_state_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    Sp = ctypes.POINTER(seed_shape)
+    Stp = ctypes.POINTER(seed_state)
+    sig = {
+        "seed_state_bytes": (ctypes.c_size_t, [Sp]),
+        "seed_scale_len": (ctypes.c_int32, [Sp]),
+        "seed_workspace_bytes": (ctypes.c_size_t, [Sp, ctypes.c_int32]),
+        "seed_state_from_dense": (ctypes.c_int, [Sp, P, P, Stp, P, ctypes.c_size_t, P]),
+        "seed_from_dense_iterations": (ctypes.c_int32, []),
+        "seed_decode_step": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, P, P, P, P, P, P, P]),
+        "seed_compress": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, ctypes.c_size_t, P]),
+        "seed_dense_decode_step": (ctypes.c_int, [Sp, P, P, P, P, P, P, P, P]),
+        "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "seed_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def make_shape(kind: int, batch: int, heads: int, d_k: int, d_v: int, rank: int, period: int,
+               factor_dtype: int = SEED_F32, io_dtype: int | None = None) -> seed_shape:
+    return seed_shape(kind, batch, heads, d_k, d_v, rank, period, factor_dtype,
+                      factor_dtype if io_dtype is None else io_dtype)
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn: str, status: int):
+    if status != SEED_OK:
+        raise SeedError(fn, status)
+
+
+def seed_status_string(status: int) -> str:
+    return LIB.seed_status_string(status).decode()
+
+
+def seed_version() -> str:
+    return LIB.seed_version().decode()
+
+
+def seed_state_bytes(shape: seed_shape) -> int:
+    return int(LIB.seed_state_bytes(ctypes.byref(shape)))
+
+
+def seed_scale_len(shape: seed_shape) -> int:
+    return int(LIB.seed_scale_len(ctypes.byref(shape)))
+
+
+def seed_workspace_bytes(shape: seed_shape, op: int) -> int:
+    return int(LIB.seed_workspace_bytes(ctypes.byref(shape), op))
+
+
+def seed_from_dense_iterations() -> int:
+    return int(LIB.seed_from_dense_iterations())
+
+
+class State:
+    """Device buffers of a factored state (torch tensors used as memory only)."""
+
+    def __init__(self, a, U, V, scale):
+        self.a, self.U, self.V, self.scale = a, U, V, scale
+        self.c = seed_state(a.data_ptr(), U.data_ptr(), V.data_ptr(), scale.data_ptr())
+
+    @classmethod
+    def empty(cls, shape: seed_shape, device="cuda"):
+        import torch
+        fdt = torch.bfloat16 if shape.factor_dtype == SEED_BF16 else torch.float32
+        n = shape.units
+        a = torch.zeros((n, shape.d_k), dtype=torch.float32, device=device)
+        U = torch.zeros((n, shape.slots, shape.d_k), dtype=fdt, device=device)
+        V = torch.zeros((n, shape.slots, shape.d_v), dtype=fdt, device=device)
+        scale = torch.ones((n, seed_scale_len(shape)), dtype=torch.float32, device=device)
+        return cls(a, U, V, scale)
+
+    def tensors(self):
+        return self.a, self.U, self.V, self.scale
+
+
+def _state_c(state):
+    return ctypes.byref(state if isinstance(state, seed_state) else state.c)
+
+
+def _torch_dt(code):
+    import torch
+    return torch.bfloat16 if code == SEED_BF16 else torch.float32
+
+
+def _expect(name, t, numel, code=None):
+    """Marshalling check of a torch tensor: on a GPU, contiguous, right size and dtype.
+
+    Keeps a wrong buffer from ever reaching a kernel; objects that are not torch tensors (raw
+    pointer holders) are passed through unchecked.
+    """
+    if t is None or not hasattr(t, "is_cuda"):
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    if code is not None and t.dtype != _torch_dt(code):
+        raise ValueError(f"{name}: expected dtype {_torch_dt(code)}, got {t.dtype}")
+
+
+def _expect_state(shape, state):
+    if isinstance(state, State):
+        n = shape.units
+        _expect("state.a", state.a, n * shape.d_k, SEED_F32)
+        _expect("state.U", state.U, n * shape.slots * shape.d_k, shape.factor_dtype)
+        _expect("state.V", state.V, n * shape.slots * shape.d_v, shape.factor_dtype)
+        _expect("state.scale", state.scale, n * seed_scale_len(shape), SEED_F32)
+
+
+def _expect_io(shape, q, k, v, beta, g, o):
+    n = shape.units
+    _expect("q", q, n * shape.d_k, shape.io_dtype)
+    _expect("k", k, n * shape.d_k, shape.io_dtype)
+    _expect("v", v, n * shape.d_v, shape.io_dtype)
+    _expect("beta", beta, n, SEED_F32)
+    _expect("g", g, n * (shape.d_k if shape.kind == SEED_KDA else 1), SEED_F32)
+    _expect("o", o, n * shape.d_v, shape.io_dtype)
+
+
+def seed_state_from_dense(shape: seed_shape, S, vbar, state, ws=None, stream=None) -> None:
+    _expect("S", S, shape.units * shape.d_k * shape.d_v, SEED_F32)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    _expect_state(shape, state)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("seed_state_from_dense", LIB.seed_state_from_dense(
+        ctypes.byref(shape), _ptr(S), _ptr(vbar), _state_c(state), _ptr(ws), ws_bytes,
+        _stream_ptr(stream)))
+
+
+def seed_decode_step(shape: seed_shape, state, m: int, q, k, v, beta, g, vbar, o,
+                     stream=None) -> None:
+    _expect_state(shape, state)
+    _expect_io(shape, q, k, v, beta, g, o)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    _check("seed_decode_step", LIB.seed_decode_step(
+        ctypes.byref(shape), _state_c(state), m, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+        _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_compress(shape: seed_shape, state, m: int, ws=None, stream=None) -> None:
+    _expect_state(shape, state)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("seed_compress", LIB.seed_compress(
+        ctypes.byref(shape), _state_c(state), m, _ptr(ws), ws_bytes, _stream_ptr(stream)))
+
+
+def seed_dense_decode_step(shape: seed_shape, S, q, k, v, beta, g, o, stream=None) -> None:
+    _expect("S", S, shape.units * shape.d_k * shape.d_v, SEED_F32)
+    _expect_io(shape, q, k, v, beta, g, o)
+    _check("seed_dense_decode_step", LIB.seed_dense_decode_step(
+        ctypes.byref(shape), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(o),
+        _stream_ptr(stream)))

@@ -1,0 +1,174 @@
+// C ABI of libseed: argument validation, size queries and dispatch to the gfx950 kernels.
+// Every entry point validates on the host before anything is enqueued, never synchronises and
+// allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include "../../include/seed.h"
+#include "kernels.hpp"
+
+namespace seed {
+int32_t from_dense_iterations();
+}
+
+namespace {
+
+bool dtype_ok(int32_t d) { return d == SEED_F32 || d == SEED_BF16; }
+bool dim_ok(int32_t d) { return d == 64 || d == 128; }
+size_t dt_bytes(int32_t d) { return d == SEED_BF16 ? 2 : 4; }
+
+// 0: valid; SEED_ERR_ARG: malformed; SEED_ERR_UNSUPPORTED: well formed but not compiled.
+int check_shape(const seed_shape* sh) {
+  if (!sh) return SEED_ERR_ARG;
+  if (sh->kind != SEED_GDN && sh->kind != SEED_KDA && sh->kind != SEED_MAMBA2) return SEED_ERR_ARG;
+  if (sh->batch <= 0 || sh->heads <= 0 || sh->d_k <= 0 || sh->d_v <= 0) return SEED_ERR_ARG;
+  if (sh->rank <= 0 || sh->period <= 0) return SEED_ERR_ARG;
+  if (!dtype_ok(sh->factor_dtype) || !dtype_ok(sh->io_dtype)) return SEED_ERR_ARG;
+  if (!dim_ok(sh->d_k) || !dim_ok(sh->d_v)) return SEED_ERR_UNSUPPORTED;
+  if (sh->rank + sh->period > 64) return SEED_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(sh->batch) * sh->heads > (int64_t{1} << 31) - 1) return SEED_ERR_UNSUPPORTED;
+  return SEED_OK;
+}
+
+int64_t units_of(const seed_shape* sh) { return static_cast<int64_t>(sh->batch) * sh->heads; }
+
+int32_t scale_len(const seed_shape* sh) {
+  return sh->kind == SEED_KDA ? sh->d_k : 1 + sh->period;
+}
+
+bool state_ok(const seed_state* st) {
+  return st && st->a && st->U && st->V && st->scale;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SEED_OK : SEED_ERR_HIP; }
+
+seed::CompressArgs compress_args(const seed_shape* sh, const seed_state* st, int32_t m) {
+  seed::CompressArgs a{};
+  a.units = units_of(sh);
+  a.heads = sh->heads;
+  a.m = m;
+  a.rank = sh->rank;
+  a.slots = sh->rank + sh->period;
+  a.scale_len = scale_len(sh);
+  a.a = st->a;
+  a.U = st->U;
+  a.V = st->V;
+  a.scale = st->scale;
+  a.S = nullptr;
+  a.vbar = nullptr;
+  a.iters = seed::from_dense_iterations();
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t seed_state_bytes(const seed_shape* sh) {
+  if (check_shape(sh) != SEED_OK) return 0;
+  const size_t slots = static_cast<size_t>(sh->rank + sh->period);
+  const size_t f = dt_bytes(sh->factor_dtype);
+  return 4 * static_cast<size_t>(sh->d_k) + f * slots * (sh->d_k + sh->d_v) +
+         4 * static_cast<size_t>(scale_len(sh));
+}
+
+int32_t seed_scale_len(const seed_shape* sh) {
+  if (check_shape(sh) != SEED_OK) return 0;
+  return scale_len(sh);
+}
+
+size_t seed_workspace_bytes(const seed_shape* sh, int32_t op) {
+  (void)sh;
+  (void)op;
+  return 0;  // both operations keep their intermediates in LDS
+}
+
+int32_t seed_from_dense_iterations(void) { return seed::from_dense_iterations(); }
+
+int seed_state_from_dense(const seed_shape* sh, const float* S, const float* vbar,
+                          const seed_state* st, void* ws, size_t ws_bytes, void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!S || !vbar || !state_ok(st)) return SEED_ERR_ARG;
+  if (ws_bytes < seed_workspace_bytes(sh, SEED_OP_FROM_DENSE)) return SEED_ERR_WORKSPACE;
+  (void)ws;
+  seed::CompressArgs a = compress_args(sh, st, sh->rank);
+  a.S = S;
+  a.vbar = vbar;
+  return hip_status(seed::launch_from_dense(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
+int seed_decode_step(const seed_shape* sh, const seed_state* st, int32_t m, const void* q,
+                     const void* k, const void* v, const float* beta, const float* g,
+                     const float* vbar, void* o, void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st) || !q || !k || !v || !beta || !g || !vbar || !o) return SEED_ERR_ARG;
+  if (m < sh->rank || m >= sh->rank + sh->period) return SEED_ERR_ARG;
+  if (!seed::decode_supported(*sh)) return SEED_ERR_UNSUPPORTED;
+  seed::StepArgs a{};
+  a.units = units_of(sh);
+  a.heads = sh->heads;
+  a.m = m;
+  a.rank = sh->rank;
+  a.slots = sh->rank + sh->period;
+  a.scale_len = scale_len(sh);
+  a.a = st->a;
+  a.U = st->U;
+  a.V = st->V;
+  a.scale = st->scale;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.vbar = vbar;
+  a.o = o;
+  return hip_status(seed::launch_decode(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
+int seed_compress(const seed_shape* sh, const seed_state* st, int32_t m, void* ws, size_t ws_bytes,
+                  void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st)) return SEED_ERR_ARG;
+  if (m < 0 || m > sh->rank + sh->period) return SEED_ERR_ARG;
+  if (ws_bytes < seed_workspace_bytes(sh, SEED_OP_COMPRESS)) return SEED_ERR_WORKSPACE;
+  (void)ws;
+  if (!seed::compress_supported(*sh)) return SEED_ERR_UNSUPPORTED;
+  if (m <= sh->rank) return SEED_OK;
+  seed::CompressArgs a = compress_args(sh, st, m);
+  return hip_status(seed::launch_compress(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
+int seed_dense_decode_step(const seed_shape* sh, float* S, const void* q, const void* k,
+                           const void* v, const float* beta, const float* g, void* o,
+                           void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!S || !q || !k || !v || !beta || !g || !o) return SEED_ERR_ARG;
+  seed::DenseArgs a{};
+  a.units = units_of(sh);
+  a.S = S;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.o = o;
+  return hip_status(seed::launch_dense(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
+const char* seed_status_string(int status) {
+  switch (status) {
+    case SEED_OK: return "ok";
+    case SEED_ERR_ARG: return "invalid argument";
+    case SEED_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case SEED_ERR_WORKSPACE: return "workspace missing or too small";
+    case SEED_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+const char* seed_version(void) { return "libseed 0.1 (gfx950)"; }
+
+}  // extern "C"

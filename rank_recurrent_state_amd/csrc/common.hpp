@@ -1,0 +1,161 @@
+// Device helpers shared by the gfx950 kernels of libseed: storage types, 16-byte vector
+// loads/stores with conversion to fp32, and cross-lane sums inside a 64-wide wavefront.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace seed {
+
+constexpr int kWave = 64;
+
+// Storage type for a dtype code (0 = fp32, 1 = bf16 held as raw 16-bit words).
+template <int DT> struct Stor;
+template <> struct Stor<0> { using T = float; };
+template <> struct Stor<1> { using T = uint16_t; };
+template <int DT> using stor_t = typename Stor<DT>::T;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+template <int DT> __device__ __forceinline__ float to_f32(stor_t<DT> x);
+template <> __device__ __forceinline__ float to_f32<0>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<1>(uint16_t x) { return bf16_to_f32(x); }
+
+template <int DT> __device__ __forceinline__ stor_t<DT> from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<0>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f32<1>(float x) { return f32_to_bf16(x); }
+
+// Load N consecutive elements of storage dtype DT into fp32 registers. N * sizeof(T) must be
+// a multiple of 4 and the address aligned to it; wide accesses are used where possible.
+template <int DT, int N>
+__device__ __forceinline__ void load_f32(const stor_t<DT>* __restrict__ p, float (&out)[N]) {
+  if constexpr (DT == 0) {
+    static_assert(N % 4 == 0 || N == 1 || N == 2, "fp32 vector width");
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 4; ++c) {
+        float4 v = reinterpret_cast<const float4*>(p)[c];
+        out[4 * c + 0] = v.x; out[4 * c + 1] = v.y; out[4 * c + 2] = v.z; out[4 * c + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < N; ++e) out[e] = p[e];
+    }
+  } else {
+    static_assert(N % 2 == 0, "bf16 vector width");
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 8; ++c) {
+        uint4 v = reinterpret_cast<const uint4*>(p)[c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          out[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+          out[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      }
+    } else if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 4; ++c) {
+        uint2 v = reinterpret_cast<const uint2*>(p)[c];
+        out[4 * c + 0] = __uint_as_float(v.x << 16);
+        out[4 * c + 1] = __uint_as_float(v.x & 0xffff0000u);
+        out[4 * c + 2] = __uint_as_float(v.y << 16);
+        out[4 * c + 3] = __uint_as_float(v.y & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < N / 2; ++c) {
+        uint32_t v = reinterpret_cast<const uint32_t*>(p)[c];
+        out[2 * c] = __uint_as_float(v << 16);
+        out[2 * c + 1] = __uint_as_float(v & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// Store N fp32 values as storage dtype DT (bf16: round to nearest even).
+template <int DT, int N>
+__device__ __forceinline__ void store_f32(stor_t<DT>* __restrict__ p, const float (&in)[N]) {
+  if constexpr (DT == 0) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 4; ++c)
+        reinterpret_cast<float4*>(p)[c] =
+            make_float4(in[4 * c], in[4 * c + 1], in[4 * c + 2], in[4 * c + 3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < N; ++e) p[e] = in[e];
+    }
+  } else {
+    static_assert(N % 2 == 0, "bf16 vector width");
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int e = 0; e < N / 2; ++e)
+      w[e] = static_cast<uint32_t>(f32_to_bf16(in[2 * e])) |
+             (static_cast<uint32_t>(f32_to_bf16(in[2 * e + 1])) << 16);
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 8; ++c)
+        reinterpret_cast<uint4*>(p)[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+    } else if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 4; ++c) reinterpret_cast<uint2*>(p)[c] = make_uint2(w[2 * c], w[2 * c + 1]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < N / 2; ++c) reinterpret_cast<uint32_t*>(p)[c] = w[c];
+    }
+  }
+}
+
+// ---- cross-lane sums -------------------------------------------------------------------------
+// DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (i <-> 7 - i inside 8 lanes), row_mirror (i <-> 15 - i inside 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of W consecutive lanes; every lane of a group gets the group's sum.
+// Must be called with all 64 lanes active.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  if constexpr (W >= 2) v += dpp<0xB1>(v);
+  if constexpr (W >= 4) v += dpp<0x4E>(v);
+  if constexpr (W >= 8) v += dpp<0x141>(v);
+  if constexpr (W >= 16) v += dpp<0x140>(v);
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Sum over lanes that share (lane % W): i.e. across the 64 / W groups of width W.
+template <int W>
+__device__ __forceinline__ float across_groups_sum(float v) {
+  if constexpr (W <= 1) v += __shfl_xor(v, 1, 64);
+  if constexpr (W <= 2) v += __shfl_xor(v, 2, 64);
+  if constexpr (W <= 4) v += __shfl_xor(v, 4, 64);
+  if constexpr (W <= 8) v += __shfl_xor(v, 8, 64);
+  if constexpr (W <= 16) v += __shfl_xor(v, 16, 64);
+  if constexpr (W <= 32) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Orders LDS traffic between lanes of one wavefront (LDS operations of a wave execute in
+// order; this keeps the compiler from moving them across the exchange point).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace seed

@@ -1,0 +1,283 @@
+// Factored decode step: read-out and exact rank-one update of the sink + rank-r state.
+//
+// Method: pages titled "Shallow Encoding Emits Deep Memories", picx.dev summary, "SEED
+// Architecture" (S = a vbar^T + U V^T) and "Exact Update (Lemma 2)" (a+ = g a + beta (omega -
+// g kappa^T a) kappa, U+ = [g U, kappa], V+ = [V, beta (eps - g V U^T kappa)]), with KDA's
+// diagonal gate in place of g and Mamba-2 without the delta terms.
+//
+// Design (gfx950): one 64-lane wavefront per (request, head) unit, four units per 256-thread
+// workgroup. The step is HBM-bound: its bytes are the m columns of U and of V, read once.
+// Each lane owns a 16-byte slice of a column; a wave-wide load covers 64 / (lanes per column)
+// whole columns, so every load instruction streams a contiguous 1 KiB. All U and V loads of
+// the unit are issued before any arithmetic, which keeps up to 32 KiB per wave in flight.
+//   U pass: per column, x_j = (G U)_j . kappa and y_j = (G U)_j . q, reduced over the lanes of
+//           the column with DPP row operations. The decay is lazy: U is never rewritten, the
+//           per-column scales (GDN, Mamba-2) or per-channel Gamma (KDA) absorb it.
+//   V pass: V x and V y accumulated per lane, then summed across column groups.
+//   Epilogue: w = beta (eps - V x) (delta kinds) or beta eps (Mamba-2) becomes column m of V,
+//           the key becomes column m of U, and o = vbar (a+ . q) + V y + (kappa . q) w.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace seed {
+
+template <int FDT, int VF>
+__device__ __forceinline__ void unpack16(const uint4& r, float (&out)[VF]) {
+  if constexpr (FDT == 0) {
+    out[0] = __uint_as_float(r.x); out[1] = __uint_as_float(r.y);
+    out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
+  } else {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[2 * e] = __uint_as_float(w[e] << 16);
+      out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+}
+
+template <int KIND, int DK, int DV, int FDT, int IDT, int MAXC>
+__global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
+  using FT = stor_t<FDT>;
+  using IT = stor_t<IDT>;
+  constexpr int VF = 16 / sizeof(FT);      // factor elements per 16-byte lane slice
+  constexpr int LPU = DK / VF;             // lanes per U column
+  constexpr int CPU_ = kWave / LPU;        // U columns per wave-wide load
+  constexpr int LPV = DV / VF;
+  constexpr int CPV = kWave / LPV;
+  constexpr int NIU = (MAXC + CPU_ - 1) / CPU_;
+  constexpr int NIV = (MAXC + CPV - 1) / CPV;
+  constexpr bool DELTA = (KIND != SEED_MAMBA2);
+  constexpr bool DIAG = (KIND == SEED_KDA);
+  static_assert(LPU <= kWave && LPV <= kWave, "column wider than a wave");
+
+  __shared__ float xs[4][MAXC];
+  __shared__ float ys[4][MAXC];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+  if (unit >= A.units) return;  // whole wave leaves together
+  const int m = A.m, r = A.rank, C = A.slots;
+  const int head = static_cast<int>(unit % A.heads);
+
+  const int ug = lane / LPU, uo = (lane % LPU) * VF;  // U column group and d_k offset
+  const int vg = lane / LPV, vo = (lane % LPV) * VF;  // V column group and d_v offset
+
+  FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(C) * DK;
+  FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
+
+  // ---- 1. stream the factors: every U and V load of the unit is issued first -----------------
+  uint4 ur[NIU];
+  uint4 vr[NIV];
+#pragma unroll
+  for (int i = 0; i < NIU; ++i) {
+    const int j = i * CPU_ + ug;
+    ur[i] = (j < m) ? *reinterpret_cast<const uint4*>(Ub + static_cast<int64_t>(j) * DK + uo)
+                    : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < NIV; ++i) {
+    const int j = i * CPV + vg;
+    vr[i] = (j < m) ? *reinterpret_cast<const uint4*>(Vb + static_cast<int64_t>(j) * DV + vo)
+                    : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // ---- 2. per-unit vectors: key-side slices in U layout, value-side slices in V layout -------
+  float qv[VF], kv[VF], av[VF];
+  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.q) + unit * DK + uo, qv);
+  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.k) + unit * DK + uo, kv);
+  load_f32<0, VF>(A.a + unit * DK + uo, av);
+  const float beta = A.beta[unit];
+  float gv[VF];
+  float gs = 0.f;
+  if constexpr (DIAG) {
+    load_f32<0, VF>(A.g + unit * DK + uo, gv);
+  } else {
+    gs = A.g[unit];
+#pragma unroll
+    for (int e = 0; e < VF; ++e) gv[e] = gs;
+  }
+  float vv[VF], vb[VF];
+  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.v) + unit * DV + vo, vv);
+  load_f32<0, VF>(A.vbar + static_cast<int64_t>(head) * DV + vo, vb);
+
+  // lazy decay state
+  float* __restrict__ sc = A.scale + unit * A.scale_len;
+  float kt[VF], qt[VF], Gn[VF];
+  float cs[NIU];
+  float own_scale = 0.f;
+  if constexpr (DIAG) {
+    float Gm[VF];
+    load_f32<0, VF>(sc + uo, Gm);
+#pragma unroll
+    for (int e = 0; e < VF; ++e) {
+      Gn[e] = gv[e] * Gm[e];  // Gamma <- alpha . Gamma
+      kt[e] = Gn[e] * kv[e];
+      qt[e] = Gn[e] * qv[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VF; ++e) { kt[e] = kv[e]; qt[e] = qv[e]; }
+#pragma unroll
+    for (int i = 0; i < NIU; ++i) {
+      const int j = i * CPU_ + ug;
+      cs[i] = (j < m) ? gs * sc[j < r ? 0 : 1 + j - r] : 0.f;
+    }
+    if (lane <= m - r) own_scale = sc[lane];
+  }
+
+  // ---- 3. value split along vbar (omega, eps) --------------------------------------------------
+  float pvv = 0.f, pnn = 0.f;
+#pragma unroll
+  for (int e = 0; e < VF; ++e) { pvv += vv[e] * vb[e]; pnn += vb[e] * vb[e]; }
+  pvv = group_sum<LPV>(pvv);
+  pnn = group_sum<LPV>(pnn);
+  const float omega = pnn > 0.f ? pvv / pnn : 0.f;
+  float eps[VF];
+#pragma unroll
+  for (int e = 0; e < VF; ++e) eps[e] = vv[e] - omega * vb[e];
+
+  // ---- 4. sink: a_d = G a, a+ = a_d + beta (omega - kappa . a_d) kappa (Mamba-2: no kappa . a_d)
+  float ad[VF];
+  float pka = 0.f, pkq = 0.f;
+#pragma unroll
+  for (int e = 0; e < VF; ++e) {
+    ad[e] = gv[e] * av[e];
+    pka += kv[e] * ad[e];
+    pkq += kv[e] * qv[e];
+  }
+  const float ka = group_sum<LPU>(pka);
+  const float s = group_sum<LPU>(pkq);  // kappa . q: the new column's share of the read-out
+  const float coef = beta * (DELTA ? (omega - ka) : omega);
+  float an[VF];
+  float paq = 0.f;
+#pragma unroll
+  for (int e = 0; e < VF; ++e) {
+    an[e] = ad[e] + coef * kv[e];
+    paq += an[e] * qv[e];
+  }
+  const float aq = group_sum<LPU>(paq);
+
+  // ---- 5. U pass: x = (G U)^T kappa, y = (G U)^T q ----------------------------------------------
+#pragma unroll
+  for (int i = 0; i < NIU; ++i) {
+    float u[VF];
+    unpack16<FDT, VF>(ur[i], u);
+    float pk = 0.f, pq = 0.f;
+#pragma unroll
+    for (int e = 0; e < VF; ++e) {
+      if constexpr (DELTA) pk += u[e] * kt[e];
+      pq += u[e] * qt[e];
+    }
+    if constexpr (DELTA) pk = group_sum<LPU>(pk);
+    pq = group_sum<LPU>(pq);
+    const int j = i * CPU_ + ug;
+    if (j < m && (lane % LPU) == 0) {
+      const float c = DIAG ? 1.f : cs[i];
+      xs[wv][j] = c * pk;
+      ys[wv][j] = c * pq;
+    }
+  }
+  wave_lds_sync();
+
+  // ---- 6. V pass: V x and V y -------------------------------------------------------------------
+  float accx[VF], accy[VF];
+#pragma unroll
+  for (int e = 0; e < VF; ++e) { accx[e] = 0.f; accy[e] = 0.f; }
+#pragma unroll
+  for (int i = 0; i < NIV; ++i) {
+    const int j = i * CPV + vg;
+    const bool live = j < m;
+    const float xj = (DELTA && live) ? xs[wv][j] : 0.f;
+    const float yj = live ? ys[wv][j] : 0.f;
+    float vc[VF];
+    unpack16<FDT, VF>(vr[i], vc);
+#pragma unroll
+    for (int e = 0; e < VF; ++e) {
+      if constexpr (DELTA) accx[e] += xj * vc[e];
+      accy[e] += yj * vc[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VF; ++e) {
+    if constexpr (DELTA) accx[e] = across_groups_sum<LPV>(accx[e]);
+    accy[e] = across_groups_sum<LPV>(accy[e]);
+  }
+
+  // ---- 7. epilogue: append the column pair, write a+, o and the decay state --------------------
+  if (vg == 0) {
+    float w[VF], o[VF];
+#pragma unroll
+    for (int e = 0; e < VF; ++e) {
+      w[e] = beta * (DELTA ? (eps[e] - accx[e]) : eps[e]);
+      o[e] = vb[e] * aq + accy[e] + s * w[e];
+    }
+    store_f32<FDT, VF>(Vb + static_cast<int64_t>(m) * DV + vo, w);
+    store_f32<IDT, VF>(reinterpret_cast<IT*>(A.o) + unit * DV + vo, o);
+  }
+  if (ug == 0) {
+    float nu[VF];
+#pragma unroll
+    for (int e = 0; e < VF; ++e) nu[e] = DIAG ? kv[e] / Gn[e] : kv[e];
+    store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
+    store_f32<0, VF>(A.a + unit * DK + uo, an);
+    if constexpr (DIAG) store_f32<0, VF>(sc + uo, Gn);
+  }
+  if constexpr (!DIAG) {
+    // slot 0: the r columns kept by the last compression; slot 1 + i: column r + i
+    if (lane <= m - r) sc[lane] = gs * own_scale;
+    else if (lane == m - r + 1) sc[lane] = 1.f;
+  }
+}
+
+// ---- host-side dispatch ----------------------------------------------------------------------
+namespace {
+
+using DecodeFn = void (*)(const StepArgs);
+
+template <int KIND, int DK, int DV, int DT>
+DecodeFn pick_cols(int slots) {
+  if (slots <= 32) return k_decode<KIND, DK, DV, DT, DT, 32>;
+  return k_decode<KIND, DK, DV, DT, DT, 64>;
+}
+
+template <int KIND, int DK, int DV>
+DecodeFn pick_dt(int dt, int slots) {
+  return dt == SEED_BF16 ? pick_cols<KIND, DK, DV, 1>(slots) : pick_cols<KIND, DK, DV, 0>(slots);
+}
+
+template <int KIND>
+DecodeFn pick_dims(int dk, int dv, int dt, int slots) {
+  if (dk == 128 && dv == 128) return pick_dt<KIND, 128, 128>(dt, slots);
+  if (dk == 128 && dv == 64) return pick_dt<KIND, 128, 64>(dt, slots);
+  if (dk == 64 && dv == 128) return pick_dt<KIND, 64, 128>(dt, slots);
+  if (dk == 64 && dv == 64) return pick_dt<KIND, 64, 64>(dt, slots);
+  return nullptr;
+}
+
+DecodeFn pick_decode(const seed_shape& sh) {
+  if (sh.factor_dtype != sh.io_dtype) return nullptr;
+  const int slots = sh.rank + sh.period;
+  if (slots > 64) return nullptr;
+  switch (sh.kind) {
+    case SEED_GDN: return pick_dims<SEED_GDN>(sh.d_k, sh.d_v, sh.factor_dtype, slots);
+    case SEED_KDA: return pick_dims<SEED_KDA>(sh.d_k, sh.d_v, sh.factor_dtype, slots);
+    case SEED_MAMBA2: return pick_dims<SEED_MAMBA2>(sh.d_k, sh.d_v, sh.factor_dtype, slots);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+bool decode_supported(const seed_shape& sh) { return pick_decode(sh) != nullptr; }
+
+hipError_t launch_decode(const seed_shape& sh, const StepArgs& a, hipStream_t s) {
+  DecodeFn fn = pick_decode(sh);
+  if (!fn) return hipErrorInvalidValue;
+  const int64_t blocks = (a.units + 3) / 4;
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace seed

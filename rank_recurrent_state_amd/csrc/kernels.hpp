@@ -1,0 +1,68 @@
+// Internal launch interface between the C ABI (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/seed.h"
+
+namespace seed {
+
+struct StepArgs {
+  int64_t units;
+  int32_t heads;
+  int32_t m;          // columns held before the step
+  int32_t rank;       // r
+  int32_t slots;      // r + T: column slots per unit
+  int32_t scale_len;  // 1 + T (GDN, Mamba-2) or d_k (KDA)
+  float* a;
+  void* U;
+  void* V;
+  float* scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  const float* vbar;
+  void* o;
+};
+
+struct DenseArgs {
+  int64_t units;
+  float* S;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;
+  void* o;
+};
+
+struct CompressArgs {
+  int64_t units;
+  int32_t heads;
+  int32_t m;          // columns held (> r)
+  int32_t rank;
+  int32_t slots;
+  int32_t scale_len;
+  float* a;
+  void* U;
+  void* V;
+  float* scale;
+  const float* S;     // from_dense only: dense states
+  const float* vbar;  // from_dense only
+  int32_t iters;      // from_dense only: subspace iterations (128 x 128 states)
+};
+
+// Each returns hipSuccess or the launch error. Shapes are validated by the caller.
+hipError_t launch_decode(const seed_shape& sh, const StepArgs& a, hipStream_t s);
+hipError_t launch_dense(const seed_shape& sh, const DenseArgs& a, hipStream_t s);
+hipError_t launch_compress(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
+hipError_t launch_from_dense(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
+
+// Whether a compiled instance exists for this shape (host-side dispatch tables).
+bool decode_supported(const seed_shape& sh);
+bool compress_supported(const seed_shape& sh);
+
+}  // namespace seed

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/seed.h declares, answers size queries, and rejects bad arguments before launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "seed.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(seed_[a-z_]+)\s*\(", text)))
+
+
+def _lib():
+    rrs = pytest.importorskip("rank_recurrent_state_amd._lib",
+                              reason="libseed.so not built (python -m rank_recurrent_state_amd.build)")
+    return rrs
+
+
+def test_every_declared_symbol_is_exported():
+    rrs = _lib()
+    names = _declared()
+    assert names, "no declarations parsed"
+    lib = ctypes.CDLL(rrs.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in seed.h but not exported"
+    assert set(names) == set(rrs.EXPORTS)
+
+
+def test_size_queries():
+    rrs = _lib()
+    sh = rrs.make_shape(rrs.SEED_GDN, 64, 16, 128, 128, 16, 16, rrs.SEED_BF16)
+    # a (4 d_k) + U, V (2 bytes x 32 slots x (128 + 128)) + scale (4 (1 + T))
+    assert rrs.seed_state_bytes(sh) == 4 * 128 + 2 * 32 * 256 + 4 * 17
+    assert rrs.seed_scale_len(sh) == 17
+    kda = rrs.make_shape(rrs.SEED_KDA, 2, 2, 128, 128, 32, 32, rrs.SEED_F32)
+    assert rrs.seed_scale_len(kda) == 128
+    assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 128
+    assert rrs.seed_workspace_bytes(sh, rrs.SEED_OP_COMPRESS) == 0
+    assert rrs.seed_workspace_bytes(sh, rrs.SEED_OP_FROM_DENSE) == 0
+    assert rrs.seed_from_dense_iterations() >= 1
+    bad = rrs.make_shape(rrs.SEED_GDN, 1, 1, 96, 128, 16, 16)
+    assert rrs.seed_state_bytes(bad) == 0
+    assert "libseed" in rrs.seed_version()
+
+
+class _FakeState:
+    def __init__(self, rrs):
+        self.c = rrs.seed_state(8, 8, 8, 8)
+
+
+class _Fake:
+    """A stand-in tensor whose pointer is never dereferenced (validation fails first)."""
+
+    def __init__(self, p=8):
+        self.p = p
+
+    def data_ptr(self):
+        return self.p
+
+    def numel(self):
+        return 0
+
+    def element_size(self):
+        return 1
+
+
+def _codes(rrs):
+    f = _Fake()
+    st = _FakeState(rrs)
+
+    def decode(sh, m, **kw):
+        args = dict(q=f, k=f, v=f, beta=f, g=f, vbar=f, o=f)
+        args.update(kw)
+        try:
+            rrs.seed_decode_step(sh, st, m, args["q"], args["k"], args["v"], args["beta"],
+                                 args["g"], args["vbar"], args["o"], stream=0)
+        except rrs.SeedError as e:
+            return e.status
+        return 0
+
+    return decode
+
+
+def test_invalid_arguments_are_rejected_on_the_host():
+    rrs = _lib()
+    decode = _codes(rrs)
+    sh = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16)
+    assert decode(sh, 15) == rrs.SEED_ERR_ARG           # m < r
+    assert decode(sh, 32) == rrs.SEED_ERR_ARG           # m >= r + T: no free column slot
+    assert decode(sh, 16, q=_Fake(0)) == rrs.SEED_ERR_ARG
+    assert decode(rrs.make_shape(rrs.SEED_GDN, 4, 2, 96, 128, 16, 16), 16) == rrs.SEED_ERR_UNSUPPORTED
+    assert decode(rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 48, 32), 48) == rrs.SEED_ERR_UNSUPPORTED
+    assert decode(rrs.make_shape(7, 4, 2, 128, 128, 16, 16), 16) == rrs.SEED_ERR_ARG
+    assert decode(rrs.make_shape(rrs.SEED_GDN, 0, 2, 128, 128, 16, 16), 16) == rrs.SEED_ERR_ARG
+    assert decode(rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 0, 16), 16) == rrs.SEED_ERR_ARG
+    # mixed factor / io dtypes are not compiled for the decode step
+    mixed = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16, rrs.SEED_F32)
+    assert decode(mixed, 16) == rrs.SEED_ERR_UNSUPPORTED
+    st = _FakeState(rrs)
+    with pytest.raises(rrs.SeedError) as e:
+        rrs.seed_compress(sh, st, 33, stream=0)
+    assert e.value.status == rrs.SEED_ERR_ARG
+    # compress with m <= r is a no-op that touches nothing
+    rrs.seed_compress(sh, st, 16, stream=0)
+    with pytest.raises(rrs.SeedError) as e:
+        rrs.seed_state_from_dense(sh, _Fake(0), _Fake(), st, stream=0)
+    assert e.value.status == rrs.SEED_ERR_ARG
+    with pytest.raises(rrs.SeedError) as e:
+        rrs.seed_dense_decode_step(sh, _Fake(), _Fake(), _Fake(), _Fake(0), _Fake(), _Fake(), _Fake(), stream=0)
+    assert e.value.status == rrs.SEED_ERR_ARG
+    for code in (0, -1, -2, -3, -4, 5):
+        assert isinstance(rrs.seed_status_string(code), str)
