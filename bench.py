@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink + rank-r decode state on one MI355X.
+
+Metric: factored decode head-steps/s and achieved HBM GB/s (as a fraction of the 8 TB/s HBM3E
+roofline), against the dense-state kernel. Default workload: a deep hybrid decode stack of 36
+Gated DeltaNet layers x 32 heads x 128 requests, d_k = d_v = 128, sink + rank r = 32,
+compression every T = 32 steps, bf16 factors with fp32 arithmetic. Dense states are built from
+4096 seeded tokens and compressed at the end of the prefill (both untimed), then the decode is
+timed.
+
+One step = one decode step of every layer (one launch per layer, as in a served model where the
+rest of the layer stack runs between two steps of a layer), plus, every T-th step, the
+compression of every layer (one launch per layer). The timed region holds exactly --steps
+steps after --warmup untimed ones, bracketed by torch.cuda.synchronize(); inputs are resident
+in HBM (a pool of --pool steps of seeded inputs, cycled).
+
+Algorithmic bytes per unit-step of the decode at m columns (what the method must move):
+  read a (4 d_k), U and V (f (d_k + d_v) m), q, k, v (e (2 d_k + d_v)), beta and g (4 + 4 or
+  4 d_k); write a (4 d_k), the new column pair (f (d_k + d_v)) and o (e d_v). f = factor bytes,
+  e = activation bytes. The lazy decay scales and vbar are not credited.
+Dense step per unit: 8 d_k d_v (fp32 state read and written) + inputs + o.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "factored decode head-steps/s + achieved HBM GB/s (% roofline) vs dense-state kernel"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps first")
+    ap.add_argument("--workload", default="gdn-stack36")
+    ap.add_argument("--pool", type=int, default=64, help="steps of resident inputs, cycled")
+    ap.add_argument("--dense-steps", type=int, default=32, help="timed dense-baseline steps")
+    ap.add_argument("--prefill", type=int, default=None, help="override the prefill length")
+    ap.add_argument("--cpu-units", type=int, default=512, help="units in the oracle CPU sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--seed", type=int, default=1005)
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
+    return ap.parse_args()
+
+
+def decode_bytes(w, m: int) -> int:
+    f = 2 if w.factor_dtype else 4
+    e = 2 if w.io_dtype else 4
+    gb = 4 * w.d_k if w.kind == 1 else 4
+    return (4 * w.d_k + f * (w.d_k + w.d_v) * m + e * (2 * w.d_k + w.d_v) + 4 + gb
+            + 4 * w.d_k + f * (w.d_k + w.d_v) + e * w.d_v)
+
+
+def compress_bytes(w, m: int) -> int:
+    f = 2 if w.factor_dtype else 4
+    return f * (w.d_k + w.d_v) * (m + w.rank)
+
+
+def dense_bytes(w) -> int:
+    e = 2 if w.io_dtype else 4
+    gb = 4 * w.d_k if w.kind == 1 else 4
+    return 8 * w.d_k * w.d_v + e * (2 * w.d_k + w.d_v) + 4 + gb + e * w.d_v
+
+
+def cpu_worker(job):
+    """Oracle (fp64) on a shard of units: one compression window of decode steps plus the
+    compression, from host copies of the GPU's states and inputs."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as orc
+
+    kind, r, T, states, inputs, vbars = job
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        for (a, U, V), xs, vb in zip(states, inputs, vbars):
+            for x in xs:
+                a, U, V, _ = orc.factored_step(kind, a, U, V, vb, x["q"], x["k"], x["v"], x["beta"], x["g"])
+            U, V, _ = orc.compress(U, V, r)
+    _ = np
+    return time.perf_counter() - t0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
+              "data-parallel over independent units and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_recurrent_state_amd as rrs
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    prefill = w.prefill if args.prefill is None else args.prefill
+    L = w.layers
+    U1 = w.batch * w.heads           # units per launch (one layer)
+    N = L * U1
+    C = w.rank + w.period
+    io = torch.bfloat16 if w.io_dtype else torch.float32
+    fdt = torch.bfloat16 if w.factor_dtype else torch.float32
+    sh = rrs.make_shape(w.kind, w.batch, w.heads, w.d_k, w.d_v, w.rank, w.period,
+                        w.factor_dtype, w.io_dtype)
+    sh_all = rrs.make_shape(w.kind, w.batch * L, w.heads, w.d_k, w.d_v, w.rank, w.period,
+                            w.factor_dtype, w.io_dtype)
+    log(f"[bench] {w.describe()}; {N} units ({L} launches of {U1} per step); {rrs.seed_version()}")
+
+    # ---- setup (untimed): dense prefill, prefill-end compression, resident input pool -------
+    ds = synth.DeviceStream(w, args.seed, dev)
+    S = torch.zeros((N, w.d_k, w.d_v), dtype=torch.float32, device=dev)
+    o_all = torch.empty((N, w.d_v), dtype=io, device=dev)
+    t0 = time.time()
+    for t in range(prefill):
+        x = ds.step(io)
+        rrs.seed_dense_decode_step(sh_all, S, x["q"], x["k"], x["v"], x["beta"], x["g"], o_all)
+        if (t + 1) % 512 == 0:
+            torch.cuda.synchronize()
+            log(f"[bench] dense prefill {t + 1}/{prefill} tokens ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    log(f"[bench] dense prefill done in {time.time() - t0:.1f} s")
+
+    a = torch.zeros((N, w.d_k), dtype=torch.float32, device=dev)
+    Uf = torch.zeros((N, C, w.d_k), dtype=fdt, device=dev)
+    Vf = torch.zeros((N, C, w.d_v), dtype=fdt, device=dev)
+    scale = torch.ones((N, rrs.seed_scale_len(sh)), dtype=torch.float32, device=dev)
+    states = [rrs.State(a[l * U1:(l + 1) * U1], Uf[l * U1:(l + 1) * U1], Vf[l * U1:(l + 1) * U1],
+                        scale[l * U1:(l + 1) * U1]) for l in range(L)]
+    vbars = [ds.vbar(l) for l in range(L)]
+    t0 = time.time()
+    for l in range(L):
+        rrs.seed_state_from_dense(sh, S[l * U1:(l + 1) * U1], vbars[l], states[l])
+        if L > 1 and (l + 1) % 6 == 0:
+            torch.cuda.synchronize()
+            log(f"[bench] prefill-end compression {l + 1}/{L} layers ({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    t_from_dense = time.time() - t0
+    log(f"[bench] prefill-end compression done in {t_from_dense:.1f} s")
+
+    T = w.period
+    K = -(-args.steps // T) * T          # whole compression windows
+    Wu = -(-args.warmup // T) * T
+    if K != args.steps or Wu != args.warmup:
+        log(f"[bench] steps/warmup rounded up to whole windows of T={T}: {K}/{Wu}")
+    nwin = max(1, min(args.pool // T, (Wu + K) // T))
+    P = nwin * T
+    pool = []
+    for p in range(P):
+        x = ds.step(io)
+        pool.append([{k: v[l * U1:(l + 1) * U1].contiguous() for k, v in x.items()} for l in range(L)])
+    torch.cuda.synchronize()
+    o = [torch.empty((U1, w.d_v), dtype=io, device=dev) for _ in range(L)]
+    log(f"[bench] input pool: {P} steps resident ({nwin} windows)")
+
+    # host copies for the CPU baseline (taken before the decode touches the states)
+    cpu_job = None
+    if not args.no_cpu:
+        ns = min(args.cpu_units, U1)
+        idx = torch.arange(ns, device=dev)
+        ah = a[:ns].double().cpu().numpy()
+        Uh = Uf[:ns, :w.rank].double().cpu().numpy()
+        Vh = Vf[:ns, :w.rank].double().cpu().numpy()
+        xs_h = []
+        for p in range(T):
+            x = pool[p % P][0]
+            xs_h.append({k: v.index_select(0, idx).double().cpu().numpy() for k, v in x.items()})
+        vb_h = vbars[0].double().cpu().numpy()
+        cpu_job = (ah, Uh, Vh, xs_h, vb_h, ns)
+
+    def enqueue_window(wi):
+        """T decode steps (one launch per layer per step), columns r .. r+T-1 before each."""
+        for j in range(T):
+            xl = pool[wi * T + j]
+            for l in range(L):
+                x = xl[l]
+                rrs.seed_decode_step(sh, states[l], w.rank + j, x["q"], x["k"], x["v"], x["beta"],
+                                     x["g"], vbars[l], o[l])
+
+    def enqueue_compress():
+        for l in range(L):
+            rrs.seed_compress(sh, states[l], w.rank + T)
+
+    for i in range(Wu // T):               # eager warmup (also the first launch of every kernel)
+        enqueue_window(i % nwin)
+        enqueue_compress()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {Wu} steps done")
+
+    graphs = not args.eager
+    if graphs:
+        g_dec = []
+        for wi in range(nwin):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                enqueue_window(wi)
+            g_dec.append(g)
+        g_cmp = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_cmp):
+            enqueue_compress()
+        torch.cuda.synchronize()
+        log(f"[bench] captured {nwin} decode-window graphs ({T * L} launches each) and a "
+            f"compression graph ({L} launches)")
+
+    # ---- timed region: K steps = K / T windows of (T decode steps, then the compressions) ---
+    nw = K // T
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    evs = [(ev(), ev(), ev()) for _ in range(nw)]
+    e_begin, e_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e_begin.record()
+    for i in range(nw):
+        wi = (Wu // T + i) % nwin
+        evs[i][0].record()
+        if graphs:
+            g_dec[wi].replay()
+        else:
+            enqueue_window(wi)
+        evs[i][1].record()
+        if graphs:
+            g_cmp.replay()
+        else:
+            enqueue_compress()
+        evs[i][2].record()
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_total = e_begin.elapsed_time(e_end) / 1e3
+    t_dec = sum(a_.elapsed_time(b_) for a_, b_, _ in evs) / 1e3
+    t_cmp = sum(b_.elapsed_time(c_) for _, b_, c_ in evs) / 1e3
+    n_dec_launch = K * L
+    n_cmp_launch = nw * L
+    dec_bytes = nw * L * U1 * sum(decode_bytes(w, w.rank + j) for j in range(T))
+    cmp_bytes = n_cmp_launch * U1 * compress_bytes(w, w.rank + T)
+    head_steps = N * K
+    value = head_steps / t_total
+    dec_gbs = dec_bytes / t_dec / 1e9
+    used_cmp = list(range(nw))
+    log(f"[bench] timed {K} steps: {t_total * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms); decode "
+        f"{t_dec * 1e3:.1f} ms over {n_dec_launch} launches ({dec_gbs:.0f} GB/s), compress "
+        f"{t_cmp * 1e3:.1f} ms over {n_cmp_launch} launches")
+
+    # ---- dense-state baseline ----------------------------------------------------------------
+    KD = args.dense_steps
+    d_ev = [(ev(), ev()) for _ in range(KD)]
+    for i in range(2):  # warm
+        x = pool[i % P]
+        for l in range(L):
+            rrs.seed_dense_decode_step(sh, S[l * U1:(l + 1) * U1], x[l]["q"], x[l]["k"], x[l]["v"],
+                                       x[l]["beta"], x[l]["g"], o[l])
+    torch.cuda.synchronize()
+    for i in range(KD):
+        x = pool[i % P]
+        d_ev[i][0].record()
+        for l in range(L):
+            rrs.seed_dense_decode_step(sh, S[l * U1:(l + 1) * U1], x[l]["q"], x[l]["k"], x[l]["v"],
+                                       x[l]["beta"], x[l]["g"], o[l])
+        d_ev[i][1].record()
+    torch.cuda.synchronize()
+    t_dense = sum(a_.elapsed_time(b_) for a_, b_ in d_ev) / 1e3
+    dense_step_ms = t_dense / KD * 1e3
+    dense_gbs = KD * N * dense_bytes(w) / t_dense / 1e9
+    log(f"[bench] dense baseline: {dense_step_ms:.3f} ms/step ({dense_gbs:.0f} GB/s)")
+
+    # ---- oracle on the host cores (bounded sample) -------------------------------------------
+    cpu = None
+    if cpu_job is not None:
+        import multiprocessing as mp
+
+        ah, Uh, Vh, xs_h, vb_h, ns = cpu_job
+        cores = min(16, os.cpu_count() or 1)
+        states_h = [(ah[u], Uh[u].T.copy(), Vh[u].T.copy()) for u in range(ns)]
+        inputs_h = [[{k: x[k][u] for k in x} for x in xs_h] for u in range(ns)]
+        heads = [vb_h[u % w.heads] for u in range(ns)]
+        shards = [(w.kind, w.rank, w.period, states_h[i::cores], inputs_h[i::cores], heads[i::cores])
+                  for i in range(cores)]
+        c0 = time.perf_counter()
+        with mp.get_context("fork").Pool(cores) as pool_:
+            cpu_secs = pool_.map(cpu_worker, shards)
+        c_wall = time.perf_counter() - c0
+        cpu = {"value": ns * w.period / c_wall, "unit": "head-steps/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{ns} units of layer 0 x one compression window ({w.period} decode "
+                         f"steps + 1 compression), fp64 NumPy oracle, {sum(cpu_secs):.1f} s of "
+                         f"CPU work on {cores} processes"}
+        log(f"[bench] oracle CPU baseline: {cpu['value']:.0f} head-steps/s on {cores} cores")
+
+    # ---- report ------------------------------------------------------------------------------
+    f_b = 2 if w.factor_dtype else 4
+    mean_cols = w.rank + w.period / 2
+    state_ratio = (4 * w.d_k * w.d_v) / (4 * w.d_k + f_b * (w.d_k + w.d_v) * mean_cols)
+    step_ms = t_total / K * 1e3
+    dec_step_ms = t_dec / K * 1e3
+    avg_launch_us = t_dec / n_dec_launch * 1e6
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.describe()}", "units": N, "launch_units": U1,
+                   "layers": L, "factor_storage": "bf16" if w.factor_dtype else "fp32",
+                   "prefill_tokens": prefill},
+        "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_decode (factored read-out + update)",
+                     "bytes_per_launch": dec_bytes / n_dec_launch,
+                     "avg_launch_us": avg_launch_us},
+        "cpu_baseline": cpu,
+        "decode_only": {"head_steps_per_s": head_steps / t_dec, "ms_per_step": dec_step_ms,
+                        "gbs": dec_gbs},
+        "compress": {"launches": n_cmp_launch, "ms_per_compression": (t_cmp / max(1, len(used_cmp))) * 1e3,
+                     "amortised_ms_per_step": t_cmp / K * 1e3,
+                     "gbs": cmp_bytes / t_cmp / 1e9 if t_cmp > 0 else None},
+        "dense": {"ms_per_step": dense_step_ms, "gbs": dense_gbs,
+                  "head_steps_per_s": N / (dense_step_ms / 1e3)},
+        "speedup_vs_dense": {"with_compression": dense_step_ms / step_ms,
+                             "decode_only": dense_step_ms / dec_step_ms,
+                             "state_byte_ratio_target": state_ratio},
+        "setup_s": {"prefill_end_compression": t_from_dense},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

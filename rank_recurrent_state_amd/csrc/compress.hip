@@ -31,6 +31,7 @@
 // any output is written (the output overwrites the first r column slots in place).
 #include <float.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -776,9 +777,28 @@ KFn pick_from_dense(const seed_shape& sh, size_t* lds) {
   return nullptr;
 }
 
+// The dynamic-LDS limit is raised once per kernel and device (the first launch), so that
+// later launches, including those recorded into a HIP graph, issue nothing but the launch.
+hipError_t raise_lds_limit(KFn fn, size_t lds) {
+  struct Entry { KFn fn; int dev; };
+  static Entry done[64];
+  static int n_done = 0;
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n_done; ++i)
+    if (done[i].fn == fn && done[i].dev == dev) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  if (n_done < 64) done[n_done++] = Entry{fn, dev};
+  return hipSuccess;
+}
+
 hipError_t launch_big_lds(KFn fn, size_t lds, int64_t units, const CompressArgs& a, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipError_t e = raise_lds_limit(fn, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(units)), dim3(256), lds, s, a);
   return hipGetLastError();

@@ -88,12 +88,20 @@ class HeadConsts:
     A: np.ndarray       # [H] Mamba-2 A_h (zeros for the other kinds)
 
 
-def head_consts(w: Workload, seed: int) -> HeadConsts:
+def head_consts(w: Workload, seed: int, layers: int = 1) -> HeadConsts:
+    """Per-head constants; with layers > 1, layer l's heads are rows l*heads .. (l+1)*heads-1."""
     g = rng(seed * 7919 + 11)
-    u = g.standard_normal((w.heads, w.d_v))
+    nh = w.heads * layers
+    u = g.standard_normal((nh, w.d_v))
     vbar = u / np.linalg.norm(u, axis=1, keepdims=True)
-    A = -g.uniform(1.0, 16.0, size=w.heads) if w.kind == MAMBA2 else np.zeros(w.heads)
+    A = -g.uniform(1.0, 16.0, size=nh) if w.kind == MAMBA2 else np.zeros(nh)
     return HeadConsts(u, vbar, A)
+
+
+def unit_heads(w: Workload, units: int) -> np.ndarray:
+    """Head-constant row of each unit for units ordered [layer][batch][head]."""
+    i = np.arange(units)
+    return (i // (w.batch * w.heads)) * w.heads + i % w.heads
 
 
 def _softplus(x):
@@ -165,9 +173,9 @@ class DeviceStream:
         self.w = w
         self.n = w.units if units is None else units
         self.device = device
-        hc = head_consts(w, seed)
+        hc = head_consts(w, seed, layers=w.layers)
         self.hc = hc
-        self.unit_heads = torch.arange(self.n, device=device) % w.heads
+        self.unit_heads = torch.tensor(unit_heads(w, self.n), device=device)
         self.u = torch.tensor(hc.u, dtype=torch.float32, device=device)
         self.A = torch.tensor(hc.A, dtype=torch.float32, device=device)
         self.gens = {}
@@ -176,9 +184,12 @@ class DeviceStream:
             gg.manual_seed(seed * 1000 + i)
             self.gens[fam] = gg
 
-    def vbar(self, dtype=None):
+    def vbar(self, layer: int = 0):
+        """[heads, d_v] mean-value directions of one layer."""
         t = self.torch
-        return t.tensor(self.hc.vbar, dtype=t.float32, device=self.device)
+        h = self.w.heads
+        return t.tensor(self.hc.vbar[layer * h:(layer + 1) * h], dtype=t.float32,
+                        device=self.device).contiguous()
 
     def step(self, io_dtype, out: dict | None = None) -> dict:
         t = self.torch
@@ -217,5 +228,6 @@ def ceil_div(a: int, b: int) -> int:
 __all__ = [
     "GDN", "KDA", "MAMBA2", "F32", "BF16", "Workload", "WORKLOADS", "HeadConsts", "head_consts",
     "step_inputs", "sequence", "round_bf16", "DeviceStream", "rng", "bytes_of", "ceil_div",
+    "unit_heads",
     "KIND_NAMES",
 ]
