@@ -816,6 +816,9 @@ bool compress_supported(const seed_shape& sh) {
 }
 
 hipError_t launch_compress(const seed_shape& sh, const CompressArgs& a, hipStream_t s) {
+  bool used = false;
+  hipError_t te = launch_compress_tri(sh, a, s, &used);  // bf16 factors, r <= 32
+  if (used) return te;
   size_t lds = 0;
   KFn fn = pick_compress(sh, &lds);
   if (!fn) return hipErrorInvalidValue;
