@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--seed", type=int, default=1005)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (scales HBM byte counters under a profiler)")
     return ap.parse_args()
 
 
@@ -125,6 +127,16 @@ def main():
     sh_all = rrs.make_shape(w.kind, w.batch * L, w.heads, w.d_k, w.d_v, w.rank, w.period,
                             w.factor_dtype, w.io_dtype)
     log(f"[bench] {w.describe()}; {N} units ({L} launches of {U1} per step); {rrs.seed_version()}")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration copy: 1 GiB read + 1 GiB written")
 
     # ---- setup (untimed): dense prefill, prefill-end compression, resident input pool -------
     ds = synth.DeviceStream(w, args.seed, dev)
