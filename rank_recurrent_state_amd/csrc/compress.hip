@@ -817,7 +817,7 @@ bool compress_supported(const seed_shape& sh) {
 
 hipError_t launch_compress(const seed_shape& sh, const CompressArgs& a, hipStream_t s) {
   bool used = false;
-  hipError_t te = launch_compress_tri(sh, a, s, &used);  // bf16 factors, r <= 32
+  hipError_t te = launch_compress_wave(sh, a, s, &used);  // bf16 factors, r <= 32
   if (used) return te;
   size_t lds = 0;
   KFn fn = pick_compress(sh, &lds);

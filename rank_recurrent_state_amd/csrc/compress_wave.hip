@@ -1,0 +1,740 @@
+// Compression back to rank r, one wavefront per unit, with the core matrices in registers
+// (bf16 factors, r <= 32, r + T <= 64).
+//
+// Method: pages titled "Shallow Encoding Emits Deep Memories" (SEED architecture: every T
+// steps the rank r + T factors are truncated back to rank r by a Gram / QR step and a truncated
+// SVD of the small core). The factored reduction is the same as in compress.hip:
+//   G_U = U~^T U~, G_V = V~^T V~ of the decay-balanced columns; pivoted Cholesky G_U ~ L L^T;
+//   core B = L^T G_V L, whose eigenvalues are sigma_i^2 of U~ V~^T; with its r leading
+//   eigenvectors Y and eigenvalues lambda, V' = V~ L Y lambda^(-1/4) and U' = M V' lambda^(-1/2)
+//   (M = U~ V~^T, so U' V'^T = M times the projector on the kept right singular directions).
+//
+// Layout on gfx950: one 64-lane wavefront per unit, lane i owning row i of every 64 x 64 core
+// matrix (64 registers, two 32-wide vectors so that a wave-uniform index reaches a register
+// through the indirect-register mode). MFMA tiles move in and out of that layout with
+// v_permlane32_swap: a 32 x 32 accumulator tile keeps one column per lane pair (l, l + 32), and
+// swapping the upper half of tile (I, 0) with the lower half of tile (I, 1) leaves every lane
+// with its own column; for a symmetric matrix that is its row.
+//
+//   Grams                 MFMA 32x32x16 bf16 straight from the stored columns (fp32 sums);
+//   pivoted Cholesky      no row swaps: the L column of step s lands in the register of its
+//                         pivot column, so L is held as L P^T (the core below is permuted
+//                         alike, which changes neither its eigenvalues nor X_V);
+//   B = L^T G_V L         MFMA 32x32x2 fp32, G_V and then L^T G_V from registers, L from LDS;
+//   eigenpairs of B       Householder tridiagonalisation in registers (reflectors kept in the
+//                         registers they zero), the r largest eigenvalues by Sturm-count
+//                         trisection (two probes per eigenvalue, one per lane half), one
+//                         eigenvector per eigenvalue from a twisted factorisation (computed on
+//                         both lanes of the pair, each keeping the even or the odd entries),
+//                         modified Gram-Schmidt, back-transformation by the reflectors;
+//   X_V, V', U'           MFMA 32x32x2 fp32; W = V_s^T V' by MFMA 32x32x16 bf16 on the
+//                         rounded V' that is stored, so that U' = M V' / sigma holds for the
+//                         stored pair.
+// LDS holds L (64 x 65 fp32) and a few vectors, about 19.5 KB, so eight units share a CU.
+#include <float.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace seed {
+
+namespace cw {
+
+constexpr int N = 64;           // padded column count
+constexpr int RX = 32;          // maximum rank on this path
+constexpr int LDL = N + 1;      // LDS row stride of L (odd: row and column reads both conflict-free)
+constexpr int NTRI = 15;        // trisection steps (the bracket shrinks 3^15 ~ 1.4e7 times)
+constexpr float kPivTol = 1e-7f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// A 64 x 64 matrix held one row per lane: register c of lane i is element (i, c), kept in two
+// local 32-wide vectors NAME_lo, NAME_hi. The index is a compile-time constant after unrolling
+// or wave-uniform (indirect register access). The matrices stay plain locals touched only
+// through these macros, so that they live in registers; helpers pass them by value.
+#define MGET(M, c) ((c) < 32 ? M##_lo[(c) & 31] : M##_hi[(c) & 31])
+#define MSET(M, c, v)             \
+  do {                            \
+    if ((c) < 32)                 \
+      M##_lo[(c) & 31] = (v);     \
+    else                          \
+      M##_hi[(c) & 31] = (v);     \
+  } while (0)
+
+struct M64 {
+  f32x32 lo, hi;
+};
+
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float swap16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The value held by lane ^ 32.
+__device__ __forceinline__ float partner(float v) {
+  float x = v, y = v;
+  swap32(x, y);
+  return (threadIdx.x & 32) ? x : y;
+}
+
+__device__ __forceinline__ float wsum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  v = swap16_sum(v);
+  float x = v, y = v;
+  swap32(x, y);
+  return x + y;
+}
+
+__device__ __forceinline__ float wmax(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  float x = v, y = v;
+  swap32(x, y);
+  return fmaxf(x, y);
+}
+
+__device__ __forceinline__ float wmin(float v) { return -wmax(-v); }
+
+__device__ __forceinline__ float bcast(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+__device__ __forceinline__ float nz(float x) { return x == 0.f ? -FLT_MIN : x; }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) z[j] = 0.f;
+  return z;
+}
+
+// Accumulator tiles t[I][J] of a 64 x 64 product P -> lane L, register rho = P[rho][L].
+__device__ __forceinline__ M64 tiles_to_rows(const f32x16 (&t)[2][2]) {
+  f32x32 R_lo, R_hi;
+#pragma unroll
+  for (int I = 0; I < 2; ++I) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float x = t[I][0][j], y = t[I][1][j];
+      swap32(x, y);
+      const int rho = 32 * I + 8 * (j >> 2) + (j & 3);
+      MSET(R, rho, x);
+      MSET(R, rho + 4, y);
+    }
+  }
+  return M64{R_lo, R_hi};
+}
+
+// MFMA 32x32x2 operands of K-step s (k = 2s + lane / 32) from a row-per-lane matrix X: .x
+// serves row (or column) block 0, .y block 1; as A they give X, as B they give X^T.
+__device__ __forceinline__ float2 rows_operand(const f32x32 X_lo, const f32x32 X_hi, int s) {
+  float x = MGET(X, 2 * s), y = MGET(X, 2 * s + 1);
+  swap32(x, y);
+  return make_float2(x, y);
+}
+
+// One 32-row accumulator tile (rows 32 I + 8 q + 4 h + t, column lane % 32) -> MFMA 32x32x2 B
+// operands: out[16 I + 4 q + {0, 2, 1, 3}] hold rows 2 s + h of that column.
+__device__ __forceinline__ void tile_to_kops(const f32x16& acc, int I, float (&out)[32]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x0 = acc[4 * q + 0], y0 = acc[4 * q + 1];
+    swap32(x0, y0);
+    float x1 = acc[4 * q + 2], y1 = acc[4 * q + 3];
+    swap32(x1, y1);
+    out[16 * I + 4 * q + 0] = x0;
+    out[16 * I + 4 * q + 2] = y0;
+    out[16 * I + 4 * q + 1] = x1;
+    out[16 * I + 4 * q + 3] = y1;
+  }
+}
+
+// One 32-row accumulator tile -> per lane 16 consecutive rows in two halves: lane half h gets
+// rows 16 u + 8 h + (0..7) in o[u][0..7] (the MFMA 32x32x16 B-operand order and a contiguous
+// 16-byte run of the column).
+__device__ __forceinline__ void tile_to_runs(const f32x16& acc, float (&o)[2][8]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x = acc[4 * (2 * u) + t], y = acc[4 * (2 * u + 1) + t];
+      swap32(x, y);
+      o[u][t] = x;
+      o[u][4 + t] = y;
+    }
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+struct Smem {
+  float Lp[N * LDL];
+  float bv[N], bw[N];
+  float dg[N], e[N], e2[N], tau[N];
+  float bal[N], ibal[N], colsc[N];
+  float gam[128];
+};
+
+// Gram of the stored columns 0..m-1 (rows of length D, bf16), as row-per-lane registers. With
+// ROWSCALE the A operand carries gam^2 along d (KDA's per-channel lazy decay).
+template <int D, bool ROWSCALE>
+__device__ __forceinline__ M64 gram(const uint16_t* __restrict__ base, const int m, const float* __restrict__ gam) {
+  const int lane = threadIdx.x;
+  const int c0 = lane & 31, kh = lane >> 5;
+  const bool ok0 = c0 < m, ok1 = c0 + 32 < m;
+  const uint16_t* p0 = base + (ok0 ? c0 : 0) * D + 8 * kh;
+  const uint16_t* p1 = base + (ok1 ? c0 + 32 : 0) * D + 8 * kh;
+  f32x16 t[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
+#pragma unroll
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    uint4 u0 = *reinterpret_cast<const uint4*>(p0 + k0);
+    uint4 u1 = *reinterpret_cast<const uint4*>(p1 + k0);
+    if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
+    if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
+    const bf16x8 b0 = __builtin_bit_cast(bf16x8, u0);
+    const bf16x8 b1 = __builtin_bit_cast(bf16x8, u1);
+    bf16x8 a0 = b0, a1 = b1;
+    if constexpr (ROWSCALE) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float gj = gam[k0 + 8 * kh + j];
+        a0[j] = static_cast<__bf16>(static_cast<float>(b0[j]) * gj * gj);
+        a1[j] = static_cast<__bf16>(static_cast<float>(b1[j]) * gj * gj);
+      }
+    }
+    t[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, t[0][0], 0, 0, 0);
+    t[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, t[0][1], 0, 0, 0);
+    t[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, t[1][0], 0, 0, 0);
+    t[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, t[1][1], 0, 0, 0);
+  }
+  return tiles_to_rows(t);
+}
+
+// P = X * Lp (X row-per-lane in registers, Lp in LDS) -> P^T row-per-lane.
+__device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, const float* __restrict__ Lp) {
+  const int lane = threadIdx.x;
+  const int c = lane & 31, kh = lane >> 5;
+  f32x16 t[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
+#pragma unroll
+  for (int s = 0; s < N / 2; ++s) {
+    const float2 a = rows_operand(X_lo, X_hi, s);
+    const float a0 = a.x, a1 = a.y;
+    const float b0 = Lp[(2 * s + kh) * LDL + c];
+    const float b1 = Lp[(2 * s + kh) * LDL + 32 + c];
+    t[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, t[0][0], 0, 0, 0);
+    t[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, t[0][1], 0, 0, 0);
+    t[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, t[1][0], 0, 0, 0);
+    t[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, t[1][1], 0, 0, 0);
+  }
+  return tiles_to_rows(t);
+}
+
+// Y = F * X for F (D x 64, the stored bf16 columns 0..m-1 of a factor) and X given as MFMA
+// 32x32x2 B operands (rows 2 s + lane / 32 of column lane % 32). Tile I holds rows 32 I.. .
+template <int D>
+__device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, const int m, const float (&xop)[32],
+                                             f32x16 (&y)[D / 32]) {
+  const int lane = threadIdx.x;
+  const int c = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int I = 0; I < D / 32; ++I) y[I] = zero16();
+#pragma unroll
+  for (int s = 0; s < N / 2; ++s) {
+    const int col = 2 * s + kh;
+    const bool ok = col < m;
+    const uint16_t* p = base + (ok ? col : 0) * D + c;
+#pragma unroll
+    for (int I = 0; I < D / 32; ++I) {
+      const float a = ok ? bf16_to_f32(p[32 * I]) : 0.f;
+      y[I] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xop[s], y[I], 0, 0, 0);
+    }
+  }
+}
+
+// Sturm count: eigenvalues of the tridiagonal (dg, e2 = e^2) below x.
+__device__ __forceinline__ int sturm(const float* __restrict__ dg, const float* __restrict__ e2, const float x) {
+  float q = dg[0] - x;
+  int c = q < 0.f;
+#pragma unroll 4
+  for (int i = 1; i < N; ++i) {
+    q = (dg[i] - x) - e2[i - 1] * __builtin_amdgcn_rcpf(nz(q));
+    c += q < 0.f;
+  }
+  return c;
+}
+
+}  // namespace cw
+
+template <int DK, int DV, bool DIAG>
+__global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
+  using namespace cw;
+  __shared__ Smem S;
+  const int lane = threadIdx.x;
+  const int h = lane >> 5, c32 = lane & 31;
+  const int64_t unit = blockIdx.x;
+  const int m = A.m, r = A.rank, C = A.slots;
+  uint16_t* __restrict__ Ub = reinterpret_cast<uint16_t*>(A.U) + unit * static_cast<int64_t>(C) * DK;
+  uint16_t* __restrict__ Vb = reinterpret_cast<uint16_t*>(A.V) + unit * static_cast<int64_t>(C) * DV;
+  float* __restrict__ sc = A.scale + unit * A.scale_len;
+
+  // ---- column scales (lazy decay), KDA's channel scales ----------------------------------------
+  float csc;
+  if constexpr (DIAG) {
+    for (int i = lane; i < DK; i += 64) S.gam[i] = sc[i];
+    csc = lane < m ? 1.f : 0.f;
+  } else {
+    csc = lane < m ? sc[lane < r ? 0 : 1 + lane - r] : 0.f;
+  }
+  S.colsc[lane] = csc;
+  wave_lds_sync();
+
+  // ---- Grams of the stored columns -------------------------------------------------------------
+  f32x32 GU_lo, GU_hi, GV_lo, GV_hi;
+  {
+    const M64 gu = gram<DK, DIAG>(Ub, m, S.gam);
+    const M64 gv = gram<DV, false>(Vb, m, nullptr);
+    GU_lo = gu.lo; GU_hi = gu.hi; GV_lo = gv.lo; GV_hi = gv.hi;
+  }
+
+  // ---- balance each column pair, folding the decay scale in -----------------------------------
+  float du = 0.f, dv = 0.f;
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    if (lane == c) { du = MGET(GU, c); dv = MGET(GV, c); }
+  }
+  float bal = 0.f, ibal = 0.f;
+  if (du > 0.f && dv > 0.f && csc > 0.f) {
+    const float qu = sqrtf(sqrtf(du)), qv = sqrtf(sqrtf(dv)), sq = sqrtf(csc);
+    bal = sq * qv / qu;
+    ibal = sq * qu / qv;
+  }
+  S.bal[lane] = bal;
+  S.ibal[lane] = ibal;
+  wave_lds_sync();
+#pragma unroll
+  for (int c4 = 0; c4 < N / 4; ++c4) {
+    const float4 b4 = reinterpret_cast<const float4*>(S.bal)[c4];
+    const float4 i4 = reinterpret_cast<const float4*>(S.ibal)[c4];
+    const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ii[4] = {i4.x, i4.y, i4.z, i4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 4 * c4 + e;
+      MSET(GU, c, MGET(GU, c) * (bal * bb[e]));
+      MSET(GV, c, MGET(GV, c) * (ibal * ii[e]));
+    }
+  }
+
+  // ---- pivoted Cholesky of G_U in place (L column s in the register of pivot p_s) --------------
+  float d = du * (bal * bal);
+  uint64_t chosen = 0;
+  {
+    const float tol = kPivTol * wmax(d);
+    for (int s = 0; s < N; ++s) {
+      const bool was = (chosen >> lane) & 1ull;
+      const float cand = was ? -1.f : d;
+      const float vmax = wmax(cand);
+      if (!(vmax > tol) || !(tol > 0.f)) break;  // uniform
+      const uint64_t hit = __ballot(cand == vmax);
+      const int p = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
+      const float piv = sqrtf(vmax);
+      const float rp = 1.f / piv;
+      const float col = MGET(GU, p);
+      float l = was ? 0.f : col * rp;
+      if (lane == p) l = piv;
+      S.bv[lane] = l;
+      wave_lds_sync();
+#pragma unroll
+      for (int c4 = 0; c4 < N / 4; ++c4) {
+        const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 4 * c4 + e;
+          MSET(GU, c, MGET(GU, c) - l * bb[e]);
+        }
+      }
+      MSET(GU, p, l);
+      d -= l * l;
+      chosen |= 1ull << p;
+      wave_lds_sync();
+    }
+  }
+  const int k = __builtin_popcountll(chosen);
+  // columns never chosen hold Schur residue below the tolerance: L has zeros there
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    const bool keep = (chosen >> c) & 1ull;
+    S.Lp[lane * LDL + c] = keep ? MGET(GU, c) : 0.f;
+  }
+  wave_lds_sync();
+
+  // ---- core B = L^T G_V L (in pivot-column order) ------------------------------------------------
+  f32x32 Bm_lo, Bm_hi;
+  {
+    const M64 rt = times_L(GV_lo, GV_hi, S.Lp);   // (G_V L)^T = L^T G_V, row per lane
+    const M64 bt = times_L(rt.lo, rt.hi, S.Lp);   // (L^T G_V L)^T, symmetric up to rounding
+    Bm_lo = bt.lo; Bm_hi = bt.hi;
+  }
+
+  // ---- Householder tridiagonalisation, the reflectors kept in the registers they zero ---------
+  for (int j = 0; j < N - 2; ++j) {
+    const float colj = MGET(Bm, j);
+    const bool tr = lane > j;
+    const float x = tr ? colj : 0.f;
+    const float sig = wsum(x * x);
+    const float x0 = bcast(x, j + 1);
+    const float djj = bcast(colj, j);
+    float t = 0.f, ej = x0, v = x;
+    if (sig - x0 * x0 > 1e-30f * sig && sig > 0.f) {  // uniform
+      const float al = x0 >= 0.f ? -sqrtf(sig) : sqrtf(sig);
+      const float v0 = x0 - al;
+      t = 2.f / (sig - x0 * x0 + v0 * v0);
+      ej = al;
+      v = (lane == j + 1) ? v0 : x;
+    }
+    MSET(Bm, j, v);
+    if (lane == 0) { S.dg[j] = djj; S.e[j] = ej; S.tau[j] = t; }
+    if (t == 0.f) continue;  // uniform
+    S.bv[lane] = v;
+    wave_lds_sync();
+    float p = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < N / 4; ++c4) {
+      const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
+      p += MGET(Bm, 4 * c4 + 0) * b4.x + MGET(Bm, 4 * c4 + 1) * b4.y + MGET(Bm, 4 * c4 + 2) * b4.z +
+           MGET(Bm, 4 * c4 + 3) * b4.w;
+    }
+    p = tr ? p * t : 0.f;
+    const float K = 0.5f * t * wsum(p * v);
+    const float w = tr ? p - K * v : 0.f;
+    S.bw[lane] = w;
+    wave_lds_sync();
+#pragma unroll
+    for (int c4 = 0; c4 < N / 4; ++c4) {
+      const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
+      const float4 w4 = reinterpret_cast<const float4*>(S.bw)[c4];
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 4 * c4 + e;
+        MSET(Bm, c, MGET(Bm, c) - (v * ww[e] + w * bb[e]));
+      }
+    }
+    wave_lds_sync();
+  }
+  {
+    // the last 2 x 2 block (readlane outside any branch: every lane active)
+    const float b62 = MGET(Bm, N - 2), b63 = MGET(Bm, N - 1);
+    const float d62 = bcast(b62, N - 2), d63 = bcast(b63, N - 1), e62 = bcast(b63, N - 2);
+    if (lane == 0) {
+      S.dg[N - 2] = d62;
+      S.dg[N - 1] = d63;
+      S.e[N - 2] = e62;
+      S.e[N - 1] = 0.f;
+      S.tau[N - 2] = 0.f;
+      S.tau[N - 1] = 0.f;
+    }
+  }
+  wave_lds_sync();
+
+  // ---- the rr largest eigenvalues by Sturm-count trisection --------------------------------------
+  const int rr = r < k ? r : k;
+  float lam;
+  {
+    const float di = S.dg[lane], ei = S.e[lane], em = lane > 0 ? S.e[lane - 1] : 0.f;
+    S.e2[lane] = ei * ei;
+    float lo = wmin(di - fabsf(em) - fabsf(ei));
+    float hi = wmax(di + fabsf(em) + fabsf(ei));
+    const float pad = 1e-6f * fmaxf(fabsf(lo), fabsf(hi)) + FLT_MIN;
+    lo -= pad;
+    hi += pad;
+    wave_lds_sync();
+    const int target = N - 1 - c32;  // the c32-th largest is the (N - 1 - c32)-th smallest
+    for (int it = 0; it < NTRI; ++it) {
+      const float x = lo + static_cast<float>(h + 1) * (hi - lo) * (1.f / 3.f);
+      const int cnt = sturm(S.dg, S.e2, x);
+      const float clo = cnt <= target ? x : -FLT_MAX;
+      const float chi = cnt > target ? x : FLT_MAX;
+      lo = fmaxf(lo, fmaxf(clo, partner(clo)));
+      hi = fminf(hi, fminf(chi, partner(chi)));
+    }
+    lam = 0.5f * (lo + hi);
+  }
+
+  // ---- eigenvectors of the tridiagonal: twisted factorisation per eigenvalue ------------------
+  // Both lanes of a pair compute vector c32; lane half h keeps entries 2 s + h in Y[s].
+  float Y[32];
+  {
+    float rm[N], rp[N];
+    float dm = S.dg[N - 1] - lam;
+#pragma unroll
+    for (int i = N - 2; i >= 0; --i) {   // bottom-up pivots D-_i; rm[i] = e_i / D-_{i+1}
+      const float ei = S.e[i];
+      const float q = ei * __builtin_amdgcn_rcpf(nz(dm));
+      rm[i] = q;
+      dm = (S.dg[i] - lam) - ei * q;
+    }
+    rm[N - 1] = 0.f;
+    float dp = S.dg[0] - lam, best = FLT_MAX;
+    int kb = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {        // top-down pivots D+_i; rp[i] = e_i / D+_i; twist
+      const float ei = S.e[i];
+      const float gm = (i < N - 1) ? dp - ei * rm[i] : dp;
+      if (fabsf(gm) < best) { best = fabsf(gm); kb = i; }
+      if (i < N - 1) {
+        const float q = ei * __builtin_amdgcn_rcpf(nz(dp));
+        rp[i] = q;
+        dp = (S.dg[i + 1] - lam) - ei * q;
+      }
+    }
+    rp[N - 1] = 0.f;
+    // above the twist z_i = -rp[i] z_{i+1} (into rp), below z_{i+1} = -rm[i] z_i (into rm)
+    float zc = 1.f;
+#pragma unroll
+    for (int i = N - 1; i >= 0; --i) {
+      zc = (i == kb) ? 1.f : (i < kb ? -rp[i] * zc : 0.f);
+      rp[i] = zc;
+    }
+    // below: z_i lands in rm[i - 1], the slot its own step has just consumed
+    zc = 1.f;
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      zc = (i - 1 == kb) ? -rm[i - 1] : (i > kb ? -rm[i - 1] * zc : 0.f);
+      rm[i - 1] = zc;
+    }
+    float nn = 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const float ze = (2 * s <= kb) ? rp[2 * s] : rm[s > 0 ? 2 * s - 1 : 0];
+      const float zo = (2 * s + 1 <= kb) ? rp[2 * s + 1] : rm[2 * s];
+      Y[s] = h ? zo : ze;
+      nn += Y[s] * Y[s];
+    }
+    nn += partner(nn);
+    const bool ok = nn > 0.f && nn < FLT_MAX;
+    const float inv = ok ? 1.f / sqrtf(nn) : 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) Y[s] = ok ? Y[s] * inv : ((2 * s + h) == kb ? 1.f : 0.f);
+  }
+
+  // ---- modified Gram-Schmidt across the rr vectors (norms applied at the end) ------------------
+  float ys = 1.f;
+  for (int c = 0; c < rr; ++c) {
+    float nn = 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) nn += Y[s] * Y[s];
+    nn += partner(nn);
+    float* buf = h ? S.bw : S.bv;
+    if (c32 == c) {
+#pragma unroll
+      for (int s4 = 0; s4 < 8; ++s4)
+        reinterpret_cast<float4*>(buf)[s4] = make_float4(Y[4 * s4], Y[4 * s4 + 1], Y[4 * s4 + 2], Y[4 * s4 + 3]);
+    }
+    wave_lds_sync();
+    const float nc = bcast(nn, c);
+    const float f2 = nc > 0.f ? 1.f / nc : 0.f;
+    float yc[32];
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) {
+      const float4 v4 = reinterpret_cast<const float4*>(buf)[s4];
+      yc[4 * s4] = v4.x; yc[4 * s4 + 1] = v4.y; yc[4 * s4 + 2] = v4.z; yc[4 * s4 + 3] = v4.w;
+    }
+    float hd = 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) hd += Y[s] * yc[s];
+    hd += partner(hd);
+    hd = c32 > c ? hd * f2 : 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) Y[s] -= hd * yc[s];
+    if (c32 == c) ys = nc > 0.f ? 1.f / sqrtf(nc) : 0.f;
+    wave_lds_sync();
+  }
+#pragma unroll
+  for (int s = 0; s < 32; ++s) Y[s] = c32 < rr ? Y[s] * ys : 0.f;
+
+  // ---- back-transformation Y <- H_0 H_1 ... H_{N-3} Y -------------------------------------------
+  for (int j = N - 3; j >= 0; --j) {
+    const float tj = S.tau[j];
+    if (tj == 0.f) continue;  // uniform
+    const float vj = MGET(Bm, j);
+    S.bv[(lane & 1) * 32 + (lane >> 1)] = vj;
+    wave_lds_sync();
+    float vv[32];
+#pragma unroll
+    for (int s4 = 0; s4 < 8; ++s4) {
+      const float4 v4 = reinterpret_cast<const float4*>(S.bv + 32 * h)[s4];
+      vv[4 * s4] = v4.x; vv[4 * s4 + 1] = v4.y; vv[4 * s4 + 2] = v4.z; vv[4 * s4 + 3] = v4.w;
+    }
+    float hd = 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) hd += vv[s] * Y[s];
+    hd = tj * (hd + partner(hd));
+#pragma unroll
+    for (int s = 0; s < 32; ++s) Y[s] -= hd * vv[s];
+    wave_lds_sync();
+  }
+
+  // eigenvalue floor: tiny or negative eigenvalues give zero columns
+  const float lmax = wmax(c32 < rr ? lam : 0.f);
+  const bool live = c32 < rr && lam > lmax * 1e-14f;
+  const float q4 = live ? sqrtf(sqrtf(lam)) : 1.f;
+  const float qv = live ? 1.f / q4 : 0.f;          // lambda^(-1/4)
+  const float qu = live ? 1.f / (q4 * q4) : 0.f;   // lambda^(-1/2)
+
+  // ---- X_V = diag(ibal) L Y lambda^(-1/4) (m x r) ----------------------------------------------
+  float xop[32];
+  {
+    f32x16 xv[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const float a0 = S.Lp[c32 * LDL + 2 * s + h];
+      const float a1 = S.Lp[(32 + c32) * LDL + 2 * s + h];
+      xv[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, Y[s], xv[0], 0, 0, 0);
+      xv[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, Y[s], xv[1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int I = 0; I < 2; ++I) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 i4 = reinterpret_cast<const float4*>(S.ibal)[8 * I + 2 * q + h];
+        xv[I][4 * q + 0] *= i4.x * qv;
+        xv[I][4 * q + 1] *= i4.y * qv;
+        xv[I][4 * q + 2] *= i4.z * qv;
+        xv[I][4 * q + 3] *= i4.w * qv;
+      }
+      tile_to_kops(xv[I], I, xop);
+    }
+  }
+
+  // ---- V' = V_s X_V (d_v x r), rounded to bf16; W = V_s^T V' -------------------------------------
+  constexpr int TV = DV / 32, TU = DK / 32;
+  uint4 vpk[TV][2];
+  {
+    f32x16 vt[TV];
+    factor_times<DV>(Vb, m, xop, vt);
+#pragma unroll
+    for (int I = 0; I < TV; ++I) {
+      float o[2][8];
+      tile_to_runs(vt[I], o);
+      vpk[I][0] = pack8(o[0]);
+      vpk[I][1] = pack8(o[1]);
+    }
+  }
+  {
+    f32x16 w[2] = {zero16(), zero16()};
+    const bool ok0 = c32 < m, ok1 = c32 + 32 < m;
+    const uint16_t* p0 = Vb + (ok0 ? c32 : 0) * DV + 8 * h;
+    const uint16_t* p1 = Vb + (ok1 ? c32 + 32 : 0) * DV + 8 * h;
+#pragma unroll
+    for (int s = 0; s < DV / 16; ++s) {
+      uint4 u0 = *reinterpret_cast<const uint4*>(p0 + 16 * s);
+      uint4 u1 = *reinterpret_cast<const uint4*>(p1 + 16 * s);
+      if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
+      if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, vpk[s >> 1][s & 1]);
+      w[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u0), bop, w[0], 0, 0, 0);
+      w[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u1), bop, w[1], 0, 0, 0);
+    }
+    // X_U = diag(colsc) W lambda^(-1/2) (U' = U_s D_c V_s^T V' / sigma), as B operands
+#pragma unroll
+    for (int I = 0; I < 2; ++I) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 c4 = reinterpret_cast<const float4*>(S.colsc)[8 * I + 2 * q + h];
+        w[I][4 * q + 0] *= c4.x * qu;
+        w[I][4 * q + 1] *= c4.y * qu;
+        w[I][4 * q + 2] *= c4.z * qu;
+        w[I][4 * q + 3] *= c4.w * qu;
+      }
+      tile_to_kops(w[I], I, xop);
+    }
+  }
+
+  // ---- U' = U_s X_U (d_k x r) (KDA: rows times Gamma) ---------------------------------------------
+  uint4 upk[TU][2];
+  {
+    f32x16 ut[TU];
+    factor_times<DK>(Ub, m, xop, ut);
+#pragma unroll
+    for (int I = 0; I < TU; ++I) {
+      float o[2][8];
+      tile_to_runs(ut[I], o);
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float4 g0 = reinterpret_cast<const float4*>(S.gam)[8 * I + 4 * u + 2 * h];
+          const float4 g1 = reinterpret_cast<const float4*>(S.gam)[8 * I + 4 * u + 2 * h + 1];
+          o[u][0] *= g0.x; o[u][1] *= g0.y; o[u][2] *= g0.z; o[u][3] *= g0.w;
+          o[u][4] *= g1.x; o[u][5] *= g1.y; o[u][6] *= g1.z; o[u][7] *= g1.w;
+        }
+      }
+      upk[I][0] = pack8(o[0]);
+      upk[I][1] = pack8(o[1]);
+    }
+  }
+
+  // ---- write the r kept columns (every read of U_s and V_s is above) ------------------------------
+  if (c32 < r) {
+#pragma unroll
+    for (int I = 0; I < TV; ++I) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<uint4*>(Vb + c32 * DV + 32 * I + 16 * u + 8 * h) = vpk[I][u];
+    }
+#pragma unroll
+    for (int I = 0; I < TU; ++I) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<uint4*>(Ub + c32 * DK + 32 * I + 16 * u + 8 * h) = upk[I][u];
+    }
+  }
+  for (int i = lane; i < A.scale_len; i += 64) sc[i] = 1.f;
+}
+
+namespace {
+using WaveFn = void (*)(const CompressArgs);
+
+WaveFn pick_compress_wave(const seed_shape& sh) {
+  if (sh.factor_dtype != SEED_BF16 || sh.rank > cw::RX || sh.rank + sh.period > cw::N) return nullptr;
+  const bool diag = sh.kind == SEED_KDA;
+  if (sh.d_k == 128 && sh.d_v == 128) return diag ? k_compress_wave<128, 128, true> : k_compress_wave<128, 128, false>;
+  if (sh.d_k == 128 && sh.d_v == 64) return diag ? k_compress_wave<128, 64, true> : k_compress_wave<128, 64, false>;
+  if (sh.d_k == 64 && sh.d_v == 128) return diag ? k_compress_wave<64, 128, true> : k_compress_wave<64, 128, false>;
+  if (sh.d_k == 64 && sh.d_v == 64) return diag ? k_compress_wave<64, 64, true> : k_compress_wave<64, 64, false>;
+  return nullptr;
+}
+}  // namespace
+
+hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used) {
+  WaveFn fn = pick_compress_wave(sh);
+  *used = fn != nullptr;
+  if (!fn) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(a.units)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace seed

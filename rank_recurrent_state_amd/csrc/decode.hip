@@ -55,7 +55,8 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   __shared__ float ys[4][MAXC];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x >> 6;
+  // the wave index is uniform: keep it (and every per-unit address) in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * 4 + wv;
   if (unit >= A.units) return;  // whole wave leaves together
   const int m = A.m, r = A.rank, C = A.slots;
@@ -68,19 +69,20 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
 
   // ---- 1. stream the factors: every U and V load of the unit is issued first -----------------
+  // Loads are unconditional so that none of them waits on another: a lane whose column is past
+  // the live ones (j >= m) re-reads column m - 1, which the same instruction already fetches, and
+  // its contribution is dropped below. Columns m..slots-1 may hold anything, even NaN.
   uint4 ur[NIU];
   uint4 vr[NIV];
 #pragma unroll
   for (int i = 0; i < NIU; ++i) {
-    const int j = i * CPU_ + ug;
-    ur[i] = (j < m) ? *reinterpret_cast<const uint4*>(Ub + static_cast<int64_t>(j) * DK + uo)
-                    : make_uint4(0u, 0u, 0u, 0u);
+    const int j = min(i * CPU_ + ug, m - 1);
+    ur[i] = *reinterpret_cast<const uint4*>(Ub + j * DK + uo);
   }
 #pragma unroll
   for (int i = 0; i < NIV; ++i) {
-    const int j = i * CPV + vg;
-    vr[i] = (j < m) ? *reinterpret_cast<const uint4*>(Vb + static_cast<int64_t>(j) * DV + vo)
-                    : make_uint4(0u, 0u, 0u, 0u);
+    const int j = min(i * CPV + vg, m - 1);
+    vr[i] = *reinterpret_cast<const uint4*>(Vb + j * DV + vo);
   }
 
   // ---- 2. per-unit vectors: key-side slices in U layout, value-side slices in V layout -------
@@ -119,12 +121,13 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   } else {
 #pragma unroll
     for (int e = 0; e < VF; ++e) { kt[e] = kv[e]; qt[e] = qv[e]; }
+    // one load per lane: lane l holds slot min(l, m - r); column j's scale comes from its slot
+    own_scale = sc[min(lane, m - r)];
 #pragma unroll
     for (int i = 0; i < NIU; ++i) {
       const int j = i * CPU_ + ug;
-      cs[i] = (j < m) ? gs * sc[j < r ? 0 : 1 + j - r] : 0.f;
+      cs[i] = gs * __shfl(own_scale, j < r ? 0 : min(1 + j - r, m - r));
     }
-    if (lane <= m - r) own_scale = sc[lane];
   }
 
   // ---- 3. value split along vbar (omega, eps) --------------------------------------------------
@@ -189,8 +192,10 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   for (int i = 0; i < NIV; ++i) {
     const int j = i * CPV + vg;
     const bool live = j < m;
-    const float xj = (DELTA && live) ? xs[wv][j] : 0.f;
-    const float yj = live ? ys[wv][j] : 0.f;
+    const float xr = DELTA ? xs[wv][j] : 0.f;
+    const float yr = ys[wv][j];
+    const float xj = live ? xr : 0.f;
+    const float yj = live ? yr : 0.f;
     float vc[VF];
     unpack16<FDT, VF>(vr[i], vc);
 #pragma unroll

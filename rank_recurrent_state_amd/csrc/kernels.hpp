@@ -62,6 +62,8 @@ hipError_t launch_compress(const seed_shape& sh, const CompressArgs& a, hipStrea
 hipError_t launch_from_dense(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
 // Tridiagonal-core compression (bf16 factors, r <= 32); *used tells whether it took the call.
 hipError_t launch_compress_tri(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used);
+// One-wavefront-per-unit compression with the core in registers (bf16 factors, r <= 32).
+hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used);
 
 // Whether a compiled instance exists for this shape (host-side dispatch tables).
 bool decode_supported(const seed_shape& sh);
