@@ -23,13 +23,14 @@
 //   B = L^T G_V L         MFMA 32x32x2 fp32, G_V and then L^T G_V from registers, L from LDS;
 //   eigenpairs of B       Householder tridiagonalisation in registers (reflectors kept in the
 //                         registers they zero), the r largest eigenvalues by Sturm-count
-//                         trisection (two probes per eigenvalue, one per lane half), one
+//                         5-section (four probes per eigenvalue, two per lane), one
 //                         eigenvector per eigenvalue from a twisted factorisation (computed on
 //                         both lanes of the pair, each keeping the even or the odd entries),
 //                         modified Gram-Schmidt, back-transformation by the reflectors;
-//   X_V, V', U'           MFMA 32x32x2 fp32; W = V_s^T V' by MFMA 32x32x16 bf16 on the
-//                         rounded V' that is stored, so that U' = M V' / sigma holds for the
-//                         stored pair.
+//   X_V, V', U'           MFMA 32x32x2 fp32 (the rows of a factor tile interleaved, d = NT i +
+//                         I, so that each lane loads NT consecutive elements of a column);
+//                         W = V_s^T V' by MFMA 32x32x16 bf16 on the rounded V' that is stored,
+//                         so that U' = M V' / sigma holds for the stored pair.
 // LDS holds L (64 x 65 fp32) and a few vectors, about 19.5 KB, so eight units share a CU.
 #include <float.h>
 
@@ -43,7 +44,7 @@ namespace cw {
 constexpr int N = 64;           // padded column count
 constexpr int RX = 32;          // maximum rank on this path
 constexpr int LDL = N + 1;      // LDS row stride of L (odd: row and column reads both conflict-free)
-constexpr int NTRI = 15;        // trisection steps (the bracket shrinks 3^15 ~ 1.4e7 times)
+constexpr int NSEC = 10;        // multisection steps (the bracket shrinks 5^10 ~ 9.8e6 times)
 constexpr float kPivTol = 1e-7f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -112,6 +113,12 @@ __device__ __forceinline__ float wmax(float v) {
 
 __device__ __forceinline__ float wmin(float v) { return -wmax(-v); }
 
+// A value every lane holds (a wave reduction's result), moved to a scalar register so that the
+// compiler treats branches on it as uniform.
+__device__ __forceinline__ float uni(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 __device__ __forceinline__ float bcast(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
@@ -166,28 +173,8 @@ __device__ __forceinline__ void tile_to_kops(const f32x16& acc, int I, float (&o
   }
 }
 
-// One 32-row accumulator tile -> per lane 16 consecutive rows in two halves: lane half h gets
-// rows 16 u + 8 h + (0..7) in o[u][0..7] (the MFMA 32x32x16 B-operand order and a contiguous
-// 16-byte run of the column).
-__device__ __forceinline__ void tile_to_runs(const f32x16& acc, float (&o)[2][8]) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float x = acc[4 * (2 * u) + t], y = acc[4 * (2 * u + 1) + t];
-      swap32(x, y);
-      o[u][t] = x;
-      o[u][4 + t] = y;
-    }
-  }
-}
-
-__device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    w[e] = static_cast<uint32_t>(f32_to_bf16(v[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * e + 1])) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
 struct Smem {
@@ -252,44 +239,66 @@ __device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, con
   return tiles_to_rows(t);
 }
 
-// Y = F * X for F (D x 64, the stored bf16 columns 0..m-1 of a factor) and X given as MFMA
-// 32x32x2 B operands (rows 2 s + lane / 32 of column lane % 32). Tile I holds rows 32 I.. .
+// Y = F X for F (D x 64: the stored bf16 columns 0..m-1 of a factor) and X given as MFMA
+// 32x32x2 B operands (rows 2 s + lane / 32 of column lane % 32). With NT = D / 32 tiles, row i
+// of tile I is d = NT i + I, so that one lane's A operands of a column are NT consecutive
+// elements (one load per K-step). Output: y[I][j] is Y[d][lane % 32] with
+// d = NT (8 (j / 4) + 4 (lane / 32) + j % 4) + I.
 template <int D>
 __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, const int m, const float (&xop)[32],
                                              f32x16 (&y)[D / 32]) {
+  constexpr int NT = D / 32;
+  static_assert(NT == 2 || NT == 4, "d of 64 or 128");
   const int lane = threadIdx.x;
   const int c = lane & 31, kh = lane >> 5;
 #pragma unroll
-  for (int I = 0; I < D / 32; ++I) y[I] = zero16();
+  for (int I = 0; I < NT; ++I) y[I] = zero16();
 #pragma unroll
   for (int s = 0; s < N / 2; ++s) {
     const int col = 2 * s + kh;
     const bool ok = col < m;
-    const uint16_t* p = base + (ok ? col : 0) * D + c;
+    const uint16_t* p = base + (ok ? col : 0) * D + NT * c;
+    uint32_t w[2];
+    if constexpr (NT == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      w[0] = ok ? u.x : 0u;
+      w[1] = ok ? u.y : 0u;
+    } else {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+      w[0] = ok ? u : 0u;
+      w[1] = 0u;
+    }
 #pragma unroll
-    for (int I = 0; I < D / 32; ++I) {
-      const float a = ok ? bf16_to_f32(p[32 * I]) : 0.f;
+    for (int I = 0; I < NT; ++I) {
+      const uint32_t wi = w[I >> 1];
+      const float a = __uint_as_float((I & 1) ? (wi & 0xffff0000u) : (wi << 16));
       y[I] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xop[s], y[I], 0, 0, 0);
     }
   }
 }
 
-// Sturm count: eigenvalues of the tridiagonal (dg, e2 = e^2) below x.
-__device__ __forceinline__ int sturm(const float* __restrict__ dg, const float* __restrict__ e2, const float x) {
-  float q = dg[0] - x;
-  int c = q < 0.f;
-#pragma unroll 4
+// Sturm counts at two shifts: eigenvalues of the tridiagonal (dg, e2 = e^2) below x1 and x2
+// (two independent recurrences interleaved).
+__device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float* __restrict__ e2, const float x1,
+                                       const float x2, int& c1, int& c2) {
+  // a zero pivot is taken as -FLT_MIN: it counts as negative and the recurrence goes on
+  float q1 = nz(dg[0] - x1), q2 = nz(dg[0] - x2);
+  c1 = q1 < 0.f;
+  c2 = q2 < 0.f;
+#pragma unroll 8
   for (int i = 1; i < N; ++i) {
-    q = (dg[i] - x) - e2[i - 1] * __builtin_amdgcn_rcpf(nz(q));
-    c += q < 0.f;
+    const float di = dg[i], ei = e2[i - 1];
+    q1 = nz((di - x1) - ei * __builtin_amdgcn_rcpf(q1));
+    q2 = nz((di - x2) - ei * __builtin_amdgcn_rcpf(q2));
+    c1 += q1 < 0.f;
+    c2 += q2 < 0.f;
   }
-  return c;
 }
 
 }  // namespace cw
 
 template <int DK, int DV, bool DIAG>
-__global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_compress_wave(const CompressArgs A) {
   using namespace cw;
   __shared__ Smem S;
   const int lane = threadIdx.x;
@@ -351,16 +360,16 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   float d = du * (bal * bal);
   uint64_t chosen = 0;
   {
-    const float tol = kPivTol * wmax(d);
+    const float tol = uni(kPivTol * wmax(d));
     for (int s = 0; s < N; ++s) {
       const bool was = (chosen >> lane) & 1ull;
       const float cand = was ? -1.f : d;
-      const float vmax = wmax(cand);
+      const float vmax = uni(wmax(cand));
       if (!(vmax > tol) || !(tol > 0.f)) break;  // uniform
       const uint64_t hit = __ballot(cand == vmax);
       const int p = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
-      const float piv = sqrtf(vmax);
-      const float rp = 1.f / piv;
+      const float rp = __builtin_amdgcn_rsqf(vmax);
+      const float piv = vmax * rp;
       const float col = MGET(GU, p);
       float l = was ? 0.f : col * rp;
       if (lane == p) l = piv;
@@ -400,50 +409,59 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   }
 
   // ---- Householder tridiagonalisation, the reflectors kept in the registers they zero ---------
-  for (int j = 0; j < N - 2; ++j) {
-    const float colj = MGET(Bm, j);
-    const bool tr = lane > j;
-    const float x = tr ? colj : 0.f;
-    const float sig = wsum(x * x);
-    const float x0 = bcast(x, j + 1);
-    const float djj = bcast(colj, j);
-    float t = 0.f, ej = x0, v = x;
-    if (sig - x0 * x0 > 1e-30f * sig && sig > 0.f) {  // uniform
-      const float al = x0 >= 0.f ? -sqrtf(sig) : sqrtf(sig);
-      const float v0 = x0 - al;
-      t = 2.f / (sig - x0 * x0 + v0 * v0);
-      ej = al;
-      v = (lane == j + 1) ? v0 : x;
-    }
-    MSET(Bm, j, v);
-    if (lane == 0) { S.dg[j] = djj; S.e[j] = ej; S.tau[j] = t; }
-    if (t == 0.f) continue;  // uniform
-    S.bv[lane] = v;
-    wave_lds_sync();
-    float p = 0.f;
+  // From step 32 on, v and w vanish on lanes (and registers) 0..31, so the second half of the
+  // steps works on the upper 32 registers only.
 #pragma unroll
-    for (int c4 = 0; c4 < N / 4; ++c4) {
-      const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
-      p += MGET(Bm, 4 * c4 + 0) * b4.x + MGET(Bm, 4 * c4 + 1) * b4.y + MGET(Bm, 4 * c4 + 2) * b4.z +
-           MGET(Bm, 4 * c4 + 3) * b4.w;
-    }
-    p = tr ? p * t : 0.f;
-    const float K = 0.5f * t * wsum(p * v);
-    const float w = tr ? p - K * v : 0.f;
-    S.bw[lane] = w;
-    wave_lds_sync();
-#pragma unroll
-    for (int c4 = 0; c4 < N / 4; ++c4) {
-      const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
-      const float4 w4 = reinterpret_cast<const float4*>(S.bw)[c4];
-      const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ww[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = 4 * c4 + e;
-        MSET(Bm, c, MGET(Bm, c) - (v * ww[e] + w * bb[e]));
+  for (int half = 0; half < 2; ++half) {
+    const int c0 = half ? 8 : 0;                 // first float4 block of registers touched
+    for (int j = half ? 32 : 0; j < (half ? N - 2 : 32); ++j) {
+      const float colj = MGET(Bm, j);
+      const bool tr = lane > j;
+      const float x = tr ? colj : 0.f;
+      const float sig = uni(wsum(x * x));
+      const float x0 = bcast(x, j + 1);
+      const float djj = bcast(colj, j);
+      float t = 0.f, ej = x0, v = x;
+      if (sig - x0 * x0 > 1e-30f * sig && sig > 0.f) {  // uniform
+        const float al = x0 >= 0.f ? -sqrtf(sig) : sqrtf(sig);
+        const float v0 = x0 - al;
+        t = 2.f * __builtin_amdgcn_rcpf(sig - x0 * x0 + v0 * v0);
+        ej = al;
+        v = (lane == j + 1) ? v0 : x;
       }
+      MSET(Bm, j, v);
+      if (lane == 0) { S.dg[j] = djj; S.e[j] = ej; S.tau[j] = t; }
+      if (t == 0.f) continue;  // uniform
+      S.bv[lane] = v;
+      wave_lds_sync();
+      float p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c4 = c0; c4 < N / 4; ++c4) {
+        const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
+        p4[0] += MGET(Bm, 4 * c4 + 0) * b4.x;
+        p4[1] += MGET(Bm, 4 * c4 + 1) * b4.y;
+        p4[2] += MGET(Bm, 4 * c4 + 2) * b4.z;
+        p4[3] += MGET(Bm, 4 * c4 + 3) * b4.w;
+      }
+      float p = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      p = tr ? p * t : 0.f;
+      const float K = 0.5f * t * uni(wsum(p * v));
+      const float w = tr ? p - K * v : 0.f;
+      S.bw[lane] = w;
+      wave_lds_sync();
+#pragma unroll
+      for (int c4 = c0; c4 < N / 4; ++c4) {
+        const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
+        const float4 w4 = reinterpret_cast<const float4*>(S.bw)[c4];
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = 4 * c4 + e;
+          MSET(Bm, c, MGET(Bm, c) - (v * ww[e] + w * bb[e]));
+        }
+      }
+      wave_lds_sync();
     }
-    wave_lds_sync();
   }
   {
     // the last 2 x 2 block (readlane outside any branch: every lane active)
@@ -460,7 +478,7 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   }
   wave_lds_sync();
 
-  // ---- the rr largest eigenvalues by Sturm-count trisection --------------------------------------
+  // ---- the rr largest eigenvalues by Sturm-count multisection --------------------------------------
   const int rr = r < k ? r : k;
   float lam;
   {
@@ -473,11 +491,15 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
     hi += pad;
     wave_lds_sync();
     const int target = N - 1 - c32;  // the c32-th largest is the (N - 1 - c32)-th smallest
-    for (int it = 0; it < NTRI; ++it) {
-      const float x = lo + static_cast<float>(h + 1) * (hi - lo) * (1.f / 3.f);
-      const int cnt = sturm(S.dg, S.e2, x);
-      const float clo = cnt <= target ? x : -FLT_MAX;
-      const float chi = cnt > target ? x : FLT_MAX;
+    for (int it = 0; it < NSEC; ++it) {
+      // four interior points of the bracket: lane half h probes points 2 h + 1 and 2 h + 2
+      const float step = (hi - lo) * 0.2f;
+      const float x1 = lo + static_cast<float>(2 * h + 1) * step;
+      const float x2 = lo + static_cast<float>(2 * h + 2) * step;
+      int n1, n2;
+      sturm2(S.dg, S.e2, x1, x2, n1, n2);
+      const float clo = fmaxf(n1 <= target ? x1 : -FLT_MAX, n2 <= target ? x2 : -FLT_MAX);
+      const float chi = fminf(n1 > target ? x1 : FLT_MAX, n2 > target ? x2 : FLT_MAX);
       lo = fmaxf(lo, fmaxf(clo, partner(clo)));
       hi = fminf(hi, fminf(chi, partner(chi)));
     }
@@ -485,55 +507,63 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   }
 
   // ---- eigenvectors of the tridiagonal: twisted factorisation per eigenvalue ------------------
-  // Both lanes of a pair compute vector c32; lane half h keeps entries 2 s + h in Y[s].
+  // Both lanes of a pair compute vector c32; lane half h keeps entries 2 s + h in Y[s]. One
+  // register array serves both sweeps: slot i holds e_i / D-_{i+1} (bottom-up pivots) for
+  // i >= kb and e_i / D+_i (top-down pivots, recomputed once the twist kb is known) for i < kb;
+  // each z then overwrites the slot its own step consumed.
   float Y[32];
   {
-    float rm[N], rp[N];
+    float rt[N];
     float dm = S.dg[N - 1] - lam;
 #pragma unroll
-    for (int i = N - 2; i >= 0; --i) {   // bottom-up pivots D-_i; rm[i] = e_i / D-_{i+1}
+    for (int i = N - 2; i >= 0; --i) {
       const float ei = S.e[i];
       const float q = ei * __builtin_amdgcn_rcpf(nz(dm));
-      rm[i] = q;
+      rt[i] = q;
       dm = (S.dg[i] - lam) - ei * q;
     }
-    rm[N - 1] = 0.f;
+    rt[N - 1] = 0.f;
     float dp = S.dg[0] - lam, best = FLT_MAX;
     int kb = 0;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {        // top-down pivots D+_i; rp[i] = e_i / D+_i; twist
+    for (int i = 0; i < N; ++i) {        // twist: argmin |gamma_i|, gamma_i = D+_i - e_i^2 / D-_{i+1}
       const float ei = S.e[i];
-      const float gm = (i < N - 1) ? dp - ei * rm[i] : dp;
+      const float gm = (i < N - 1) ? dp - ei * rt[i] : dp;
       if (fabsf(gm) < best) { best = fabsf(gm); kb = i; }
-      if (i < N - 1) {
-        const float q = ei * __builtin_amdgcn_rcpf(nz(dp));
-        rp[i] = q;
-        dp = (S.dg[i + 1] - lam) - ei * q;
-      }
+      if (i < N - 1) dp = (S.dg[i + 1] - lam) - ei * (ei * __builtin_amdgcn_rcpf(nz(dp)));
     }
-    rp[N - 1] = 0.f;
-    // above the twist z_i = -rp[i] z_{i+1} (into rp), below z_{i+1} = -rm[i] z_i (into rm)
+    dp = S.dg[0] - lam;
+#pragma unroll
+    for (int i = 0; i < N - 1; ++i) {    // e_i / D+_i into the slots above the twist
+      const float ei = S.e[i];
+      const float q = ei * __builtin_amdgcn_rcpf(nz(dp));
+      if (i < kb) rt[i] = q;
+      dp = (S.dg[i + 1] - lam) - ei * q;
+    }
+    // below the twist z_{i+1} = -rt[i] z_i (into rt[i]); above it z_i = -rt[i] z_{i+1} (into rt[i])
     float zc = 1.f;
 #pragma unroll
-    for (int i = N - 1; i >= 0; --i) {
-      zc = (i == kb) ? 1.f : (i < kb ? -rp[i] * zc : 0.f);
-      rp[i] = zc;
+    for (int i = 0; i < N - 1; ++i) {
+      zc = (i == kb) ? -rt[i] : (i > kb ? -rt[i] * zc : 0.f);
+      if (i >= kb) rt[i] = zc;
     }
-    // below: z_i lands in rm[i - 1], the slot its own step has just consumed
     zc = 1.f;
 #pragma unroll
-    for (int i = 1; i < N; ++i) {
-      zc = (i - 1 == kb) ? -rm[i - 1] : (i > kb ? -rm[i - 1] * zc : 0.f);
-      rm[i - 1] = zc;
+    for (int i = N - 2; i >= 0; --i) {
+      zc = (i == kb - 1) ? -rt[i] : (i < kb - 1 ? -rt[i] * zc : 0.f);
+      if (i < kb) rt[i] = zc;
     }
-    float nn = 0.f;
+    // z_j = rt[j] (j < kb), 1 (j = kb), rt[j - 1] (j > kb)
+    float nn0 = 0.f, nn1 = 0.f;
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
-      const float ze = (2 * s <= kb) ? rp[2 * s] : rm[s > 0 ? 2 * s - 1 : 0];
-      const float zo = (2 * s + 1 <= kb) ? rp[2 * s + 1] : rm[2 * s];
+      const int je = 2 * s, jo = 2 * s + 1;
+      const float ze = je < kb ? rt[je] : (je == kb ? 1.f : rt[je > 0 ? je - 1 : 0]);
+      const float zo = jo < kb ? rt[jo] : (jo == kb ? 1.f : rt[jo - 1]);
       Y[s] = h ? zo : ze;
-      nn += Y[s] * Y[s];
+      if (s & 1) nn1 += Y[s] * Y[s]; else nn0 += Y[s] * Y[s];
     }
+    float nn = nn0 + nn1;
     nn += partner(nn);
     const bool ok = nn > 0.f && nn < FLT_MAX;
     const float inv = ok ? 1.f / sqrtf(nn) : 0.f;
@@ -544,9 +574,10 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   // ---- modified Gram-Schmidt across the rr vectors (norms applied at the end) ------------------
   float ys = 1.f;
   for (int c = 0; c < rr; ++c) {
-    float nn = 0.f;
+    float n4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) nn += Y[s] * Y[s];
+    for (int s = 0; s < 32; ++s) n4[s & 3] += Y[s] * Y[s];
+    float nn = (n4[0] + n4[1]) + (n4[2] + n4[3]);
     nn += partner(nn);
     float* buf = h ? S.bw : S.bv;
     if (c32 == c) {
@@ -563,9 +594,10 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
       const float4 v4 = reinterpret_cast<const float4*>(buf)[s4];
       yc[4 * s4] = v4.x; yc[4 * s4 + 1] = v4.y; yc[4 * s4 + 2] = v4.z; yc[4 * s4 + 3] = v4.w;
     }
-    float hd = 0.f;
+    float h4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) hd += Y[s] * yc[s];
+    for (int s = 0; s < 32; ++s) h4[s & 3] += Y[s] * yc[s];
+    float hd = (h4[0] + h4[1]) + (h4[2] + h4[3]);
     hd += partner(hd);
     hd = c32 > c ? hd * f2 : 0.f;
 #pragma unroll
@@ -589,9 +621,10 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
       const float4 v4 = reinterpret_cast<const float4*>(S.bv + 32 * h)[s4];
       vv[4 * s4] = v4.x; vv[4 * s4 + 1] = v4.y; vv[4 * s4 + 2] = v4.z; vv[4 * s4 + 3] = v4.w;
     }
-    float hd = 0.f;
+    float h4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) hd += vv[s] * Y[s];
+    for (int s = 0; s < 32; ++s) h4[s & 3] += vv[s] * Y[s];
+    float hd = (h4[0] + h4[1]) + (h4[2] + h4[3]);
     hd = tj * (hd + partner(hd));
 #pragma unroll
     for (int s = 0; s < 32; ++s) Y[s] -= hd * vv[s];
@@ -599,7 +632,7 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   }
 
   // eigenvalue floor: tiny or negative eigenvalues give zero columns
-  const float lmax = wmax(c32 < rr ? lam : 0.f);
+  const float lmax = uni(wmax(c32 < rr ? lam : 0.f));
   const bool live = c32 < rr && lam > lmax * 1e-14f;
   const float q4 = live ? sqrtf(sqrtf(lam)) : 1.f;
   const float qv = live ? 1.f / q4 : 0.f;          // lambda^(-1/4)
@@ -631,31 +664,35 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   }
 
   // ---- V' = V_s X_V (d_v x r), rounded to bf16; W = V_s^T V' -------------------------------------
-  constexpr int TV = DV / 32, TU = DK / 32;
-  uint4 vpk[TV][2];
+  // V' of lane (c, h) is kept as bf16 pairs: word j NT/2 + e holds d = NT i_j + 2 e, + 1 with
+  // i_j = 8 (j / 4) + 4 h + j % 4. Words 4 s .. 4 s + 3 are then the MFMA 32x32x16 B operand of
+  // K-step s for d = 8 NT q + 4 NT h + 8 u + (0..7), q = s / (NT / 2), u = s % (NT / 2).
+  constexpr int NV = DV / 32, NU = DK / 32;
+  uint32_t vw[16 * NV / 2];
   {
-    f32x16 vt[TV];
+    f32x16 vt[NV];
     factor_times<DV>(Vb, m, xop, vt);
 #pragma unroll
-    for (int I = 0; I < TV; ++I) {
-      float o[2][8];
-      tile_to_runs(vt[I], o);
-      vpk[I][0] = pack8(o[0]);
-      vpk[I][1] = pack8(o[1]);
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+      for (int e = 0; e < NV / 2; ++e) vw[j * NV / 2 + e] = pack2(vt[2 * e][j], vt[2 * e + 1][j]);
     }
   }
   {
     f32x16 w[2] = {zero16(), zero16()};
     const bool ok0 = c32 < m, ok1 = c32 + 32 < m;
-    const uint16_t* p0 = Vb + (ok0 ? c32 : 0) * DV + 8 * h;
-    const uint16_t* p1 = Vb + (ok1 ? c32 + 32 : 0) * DV + 8 * h;
+    const uint16_t* p0 = Vb + (ok0 ? c32 : 0) * DV + 4 * NV * h;
+    const uint16_t* p1 = Vb + (ok1 ? c32 + 32 : 0) * DV + 4 * NV * h;
 #pragma unroll
     for (int s = 0; s < DV / 16; ++s) {
-      uint4 u0 = *reinterpret_cast<const uint4*>(p0 + 16 * s);
-      uint4 u1 = *reinterpret_cast<const uint4*>(p1 + 16 * s);
+      const int q = s / (NV / 2), u = s % (NV / 2);
+      const int off = 8 * NV * q + 8 * u;
+      uint4 u0 = *reinterpret_cast<const uint4*>(p0 + off);
+      uint4 u1 = *reinterpret_cast<const uint4*>(p1 + off);
       if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
       if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
-      const bf16x8 bop = __builtin_bit_cast(bf16x8, vpk[s >> 1][s & 1]);
+      const uint4 bw4 = make_uint4(vw[4 * s], vw[4 * s + 1], vw[4 * s + 2], vw[4 * s + 3]);
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, bw4);
       w[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u0), bop, w[0], 0, 0, 0);
       w[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u1), bop, w[1], 0, 0, 0);
     }
@@ -675,41 +712,38 @@ __global__ __launch_bounds__(64) void k_compress_wave(const CompressArgs A) {
   }
 
   // ---- U' = U_s X_U (d_k x r) (KDA: rows times Gamma) ---------------------------------------------
-  uint4 upk[TU][2];
+  uint32_t uw[16 * NU / 2];
   {
-    f32x16 ut[TU];
+    f32x16 ut[NU];
     factor_times<DK>(Ub, m, xop, ut);
 #pragma unroll
-    for (int I = 0; I < TU; ++I) {
-      float o[2][8];
-      tile_to_runs(ut[I], o);
+    for (int j = 0; j < 16; ++j) {
+      const int i = 8 * (j >> 2) + 4 * h + (j & 3);
+      float g[NU];
+#pragma unroll
+      for (int I = 0; I < NU; ++I) g[I] = 1.f;
       if constexpr (DIAG) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float4 g0 = reinterpret_cast<const float4*>(S.gam)[8 * I + 4 * u + 2 * h];
-          const float4 g1 = reinterpret_cast<const float4*>(S.gam)[8 * I + 4 * u + 2 * h + 1];
-          o[u][0] *= g0.x; o[u][1] *= g0.y; o[u][2] *= g0.z; o[u][3] *= g0.w;
-          o[u][4] *= g1.x; o[u][5] *= g1.y; o[u][6] *= g1.z; o[u][7] *= g1.w;
-        }
+        for (int I = 0; I < NU; ++I) g[I] = S.gam[NU * i + I];
       }
-      upk[I][0] = pack8(o[0]);
-      upk[I][1] = pack8(o[1]);
+#pragma unroll
+      for (int e = 0; e < NU / 2; ++e) uw[j * NU / 2 + e] = pack2(ut[2 * e][j] * g[2 * e], ut[2 * e + 1][j] * g[2 * e + 1]);
     }
   }
 
   // ---- write the r kept columns (every read of U_s and V_s is above) ------------------------------
   if (c32 < r) {
 #pragma unroll
-    for (int I = 0; I < TV; ++I) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<uint4*>(Vb + c32 * DV + 32 * I + 16 * u + 8 * h) = vpk[I][u];
-    }
-#pragma unroll
-    for (int I = 0; I < TU; ++I) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<uint4*>(Ub + c32 * DK + 32 * I + 16 * u + 8 * h) = upk[I][u];
+    for (int j = 0; j < 16; ++j) {
+      const int i = 8 * (j >> 2) + 4 * h + (j & 3);
+      if constexpr (NV == 4)
+        *reinterpret_cast<uint2*>(Vb + c32 * DV + NV * i) = make_uint2(vw[2 * j], vw[2 * j + 1]);
+      else
+        *reinterpret_cast<uint32_t*>(Vb + c32 * DV + NV * i) = vw[j];
+      if constexpr (NU == 4)
+        *reinterpret_cast<uint2*>(Ub + c32 * DK + NU * i) = make_uint2(uw[2 * j], uw[2 * j + 1]);
+      else
+        *reinterpret_cast<uint32_t*>(Ub + c32 * DK + NU * i) = uw[j];
     }
   }
   for (int i = lane; i < A.scale_len; i += 64) sc[i] = 1.f;
