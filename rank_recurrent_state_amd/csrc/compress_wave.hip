@@ -17,13 +17,13 @@
 // with its own column; for a symmetric matrix that is its row.
 //
 //   Grams                 MFMA 32x32x16 bf16 straight from the stored columns (fp32 sums);
-//   pivoted Cholesky      no row swaps: the L column of step s lands in the register of its
-//                         pivot column, so L is held as L P^T (the core below is permuted
-//                         alike, which changes neither its eigenvalues nor X_V);
+//   pivoted Cholesky      no row swaps: the L column of step s lands in column p_s of its LDS
+//                         copy, so L is held as L P^T (the core below is permuted alike,
+//                         which changes neither its eigenvalues nor X_V);
 //   B = L^T G_V L         MFMA 32x32x2 fp32, G_V and then L^T G_V from registers, L from LDS;
 //   eigenpairs of B       Householder tridiagonalisation in registers (reflectors kept in the
-//                         registers they zero), the r largest eigenvalues by Sturm-count
-//                         5-section (four probes per eigenvalue, two per lane), one
+//                         registers they zero), the r largest eigenvalues by Sturm counts
+//                         (a 128-point grid shared by all, then 5-section), one
 //                         eigenvector per eigenvalue from a twisted factorisation (computed on
 //                         both lanes of the pair, each keeping the even or the odd entries),
 //                         modified Gram-Schmidt, back-transformation by the reflectors;
@@ -44,7 +44,7 @@ namespace cw {
 constexpr int N = 64;           // padded column count
 constexpr int RX = 32;          // maximum rank on this path
 constexpr int LDL = N + 1;      // LDS row stride of L (odd: row and column reads both conflict-free)
-constexpr int NSEC = 10;        // multisection steps (the bracket shrinks 5^10 ~ 9.8e6 times)
+constexpr int NSEC = 7;         // 5-section steps after the 128-point grid (129 * 5^7 ~ 1e7)
 constexpr float kPivTol = 1e-7f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -113,6 +113,25 @@ __device__ __forceinline__ float wmax(float v) {
 
 __device__ __forceinline__ float wmin(float v) { return -wmax(-v); }
 
+// Maximum over the wave of non-negative int keys (the bit patterns of non-negative floats
+// order like the floats).
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wmax_key(int v) {
+  v = max(v, dppi<0xB1>(v));
+  v = max(v, dppi<0x4E>(v));
+  v = max(v, dppi<0x141>(v));
+  v = max(v, dppi<0x140>(v));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+    v = max(static_cast<int>(r[0]), static_cast<int>(r[1]));
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+  return max(static_cast<int>(r[0]), static_cast<int>(r[1]));
+}
+
 // A value every lane holds (a wave reduction's result), moved to a scalar register so that the
 // compiler treats branches on it as uniform.
 __device__ __forceinline__ float uni(float v) {
@@ -178,11 +197,17 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 }
 
 struct Smem {
-  float Lp[N * LDL];
-  float bv[N], bw[N];
-  float dg[N], e[N], e2[N], tau[N];
-  float bal[N], ibal[N], colsc[N];
-  float gam[128];
+  alignas(16) float Lp[N * LDL];
+  alignas(16) float bvw[2 * N];    // broadcast vectors (v, w); the second vector of a pair
+  alignas(16) float y2[2 * N];     // Gram-Schmidt / back-transformation: one vector, even then odd entries
+  alignas(16) float dg[N];
+  alignas(16) float e[N];
+  alignas(16) float e2[N];
+  alignas(16) float tau[N];
+  alignas(16) float bal[N];
+  alignas(16) float ibal[N];
+  alignas(16) float colsc[N];
+  alignas(16) float gam[128];
 };
 
 // Gram of the stored columns 0..m-1 (rows of length D, bf16), as row-per-lane registers. With
@@ -278,21 +303,23 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
 }
 
 // Sturm counts at two shifts: eigenvalues of the tridiagonal (dg, e2 = e^2) below x1 and x2
-// (two independent recurrences interleaved).
+// (two independent recurrences interleaved). e2 is floored at FLT_MIN, so a zero pivot gives an
+// infinite next pivot of the opposite sign (IEEE arithmetic) instead of NaN; pivots are counted
+// by their sign bit, so that +0 followed by -inf and -0 followed by +inf count once each.
 __device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float* __restrict__ e2, const float x1,
                                        const float x2, int& c1, int& c2) {
-  // a zero pivot is taken as -FLT_MIN: it counts as negative and the recurrence goes on
-  float q1 = nz(dg[0] - x1), q2 = nz(dg[0] - x2);
-  c1 = q1 < 0.f;
-  c2 = q2 < 0.f;
+  float q1 = dg[0] - x1, q2 = dg[0] - x2;
+  uint32_t n1 = __float_as_uint(q1) >> 31, n2 = __float_as_uint(q2) >> 31;
 #pragma unroll 8
   for (int i = 1; i < N; ++i) {
     const float di = dg[i], ei = e2[i - 1];
-    q1 = nz((di - x1) - ei * __builtin_amdgcn_rcpf(q1));
-    q2 = nz((di - x2) - ei * __builtin_amdgcn_rcpf(q2));
-    c1 += q1 < 0.f;
-    c2 += q2 < 0.f;
+    q1 = (di - x1) - ei * __builtin_amdgcn_rcpf(q1);
+    q2 = (di - x2) - ei * __builtin_amdgcn_rcpf(q2);
+    n1 += __float_as_uint(q1) >> 31;
+    n2 += __float_as_uint(q2) >> 31;
   }
+  c1 = static_cast<int>(n1);
+  c2 = static_cast<int>(n2);
 }
 
 }  // namespace cw
@@ -363,21 +390,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const float tol = uni(kPivTol * wmax(d));
     for (int s = 0; s < N; ++s) {
       const bool was = (chosen >> lane) & 1ull;
-      const float cand = was ? -1.f : d;
-      const float vmax = uni(wmax(cand));
-      if (!(vmax > tol) || !(tol > 0.f)) break;  // uniform
-      const uint64_t hit = __ballot(cand == vmax);
+      const int key = (!was && d > 0.f) ? __float_as_int(d) : -1;   // d is finite
+      const int kmax = __builtin_amdgcn_readfirstlane(wmax_key(key));
+      const float vmax = __int_as_float(kmax);
+      if (kmax < 0 || !(vmax > tol) || !(tol > 0.f)) break;  // uniform
+      const uint64_t hit = __ballot(key == kmax);
       const int p = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
       const float rp = __builtin_amdgcn_rsqf(vmax);
       const float piv = vmax * rp;
       const float col = MGET(GU, p);
       float l = was ? 0.f : col * rp;
       if (lane == p) l = piv;
-      S.bv[lane] = l;
+      S.bvw[lane] = l;
       wave_lds_sync();
 #pragma unroll
       for (int c4 = 0; c4 < N / 4; ++c4) {
-        const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
+        const float4 b4 = reinterpret_cast<const float4*>(S.bvw)[c4];
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -385,18 +413,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
           MSET(GU, c, MGET(GU, c) - l * bb[e]);
         }
       }
-      MSET(GU, p, l);
+      S.Lp[lane * LDL + p] = l;     // L column s lands in column p (the register keeps ~0)
       d -= l * l;
       chosen |= 1ull << p;
       wave_lds_sync();
     }
   }
   const int k = __builtin_popcountll(chosen);
-  // columns never chosen hold Schur residue below the tolerance: L has zeros there
+  // columns never chosen (Schur residue below the tolerance) are zero in L
 #pragma unroll
   for (int c = 0; c < N; ++c) {
-    const bool keep = (chosen >> c) & 1ull;
-    S.Lp[lane * LDL + c] = keep ? MGET(GU, c) : 0.f;
+    if (!((chosen >> c) & 1ull)) S.Lp[lane * LDL + c] = 0.f;
   }
   wave_lds_sync();
 
@@ -409,12 +436,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   }
 
   // ---- Householder tridiagonalisation, the reflectors kept in the registers they zero ---------
-  // From step 32 on, v and w vanish on lanes (and registers) 0..31, so the second half of the
-  // steps works on the upper 32 registers only.
+  // From step 16 qt on, v and w vanish on lanes (and registers) below 16 qt, so quarter qt of
+  // the steps works on registers 16 qt.. only.
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int c0 = half ? 8 : 0;                 // first float4 block of registers touched
-    for (int j = half ? 32 : 0; j < (half ? N - 2 : 32); ++j) {
+  for (int qt = 0; qt < 4; ++qt) {
+    const int c0 = 4 * qt;                       // first float4 block of registers touched
+    for (int j = 16 * qt; j < (qt == 3 ? N - 2 : 16 * qt + 16); ++j) {
       const float colj = MGET(Bm, j);
       const bool tr = lane > j;
       const float x = tr ? colj : 0.f;
@@ -432,12 +459,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       MSET(Bm, j, v);
       if (lane == 0) { S.dg[j] = djj; S.e[j] = ej; S.tau[j] = t; }
       if (t == 0.f) continue;  // uniform
-      S.bv[lane] = v;
+      S.bvw[lane] = v;
       wave_lds_sync();
       float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c4 = c0; c4 < N / 4; ++c4) {
-        const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
+        const float4 b4 = reinterpret_cast<const float4*>(S.bvw)[c4];
         p4[0] += MGET(Bm, 4 * c4 + 0) * b4.x;
         p4[1] += MGET(Bm, 4 * c4 + 1) * b4.y;
         p4[2] += MGET(Bm, 4 * c4 + 2) * b4.z;
@@ -447,17 +474,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       p = tr ? p * t : 0.f;
       const float K = 0.5f * t * uni(wsum(p * v));
       const float w = tr ? p - K * v : 0.f;
-      S.bw[lane] = w;
+      (S.bvw + N)[lane] = w;
       wave_lds_sync();
 #pragma unroll
       for (int c4 = c0; c4 < N / 4; ++c4) {
-        const float4 b4 = reinterpret_cast<const float4*>(S.bv)[c4];
-        const float4 w4 = reinterpret_cast<const float4*>(S.bw)[c4];
+        const float4 b4 = reinterpret_cast<const float4*>(S.bvw)[c4];
+        const float4 w4 = reinterpret_cast<const float4*>((S.bvw + N))[c4];
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ww[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = 4 * c4 + e;
-          MSET(Bm, c, MGET(Bm, c) - (v * ww[e] + w * bb[e]));
+          MSET(Bm, c, fmaf(-w, bb[e], fmaf(-v, ww[e], MGET(Bm, c))));
         }
       }
       wave_lds_sync();
@@ -483,7 +510,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   float lam;
   {
     const float di = S.dg[lane], ei = S.e[lane], em = lane > 0 ? S.e[lane - 1] : 0.f;
-    S.e2[lane] = ei * ei;
+    S.e2[lane] = fmaxf(ei * ei, FLT_MIN);
     float lo = wmin(di - fabsf(em) - fabsf(ei));
     float hi = wmax(di + fabsf(em) + fabsf(ei));
     const float pad = 1e-6f * fmaxf(fabsf(lo), fabsf(hi)) + FLT_MIN;
@@ -491,6 +518,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     hi += pad;
     wave_lds_sync();
     const int target = N - 1 - c32;  // the c32-th largest is the (N - 1 - c32)-th smallest
+    {
+      // first bracket from a shared grid of 128 points (two per lane, increasing with the lane):
+      // the points with at most t eigenvalues below them are a prefix of the grid
+      const float step = (hi - lo) * (1.f / 129.f);
+      const float x1 = lo + static_cast<float>(2 * lane + 1) * step;
+      const float x2 = lo + static_cast<float>(2 * lane + 2) * step;
+      int n1, n2;
+      sturm2(S.dg, S.e2, x1, x2, n1, n2);
+      float nlo = lo, nhi = hi;
+      for (int g = 0; g < rr; ++g) {
+        const int t = N - 1 - g;
+        const int cnt = __builtin_popcountll(__ballot(n1 <= t)) + __builtin_popcountll(__ballot(n2 <= t));
+        const float glo = cnt > 0 ? lo + static_cast<float>(cnt) * step : lo;
+        const float ghi = cnt < 2 * N ? lo + static_cast<float>(cnt + 1) * step : hi;
+        if (c32 == g) { nlo = glo; nhi = ghi; }
+      }
+      lo = nlo;
+      hi = nhi;
+    }
     for (int it = 0; it < NSEC; ++it) {
       // four interior points of the bracket: lane half h probes points 2 h + 1 and 2 h + 2
       const float step = (hi - lo) * 0.2f;
@@ -571,64 +617,108 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     for (int s = 0; s < 32; ++s) Y[s] = ok ? Y[s] * inv : ((2 * s + h) == kb ? 1.f : 0.f);
   }
 
-  // ---- modified Gram-Schmidt across the rr vectors (norms applied at the end) ------------------
+  // ---- modified Gram-Schmidt across the rr vectors, two at a time (norms applied at the end) ---
+  // For the pair (y_c, y_c+1) with a = |y_c|^2, b = y_c . y_c+1, d = |y_c+1|^2, mu = b / a and
+  // nu^2 = d - mu b: y_c+1 <- y_c+1 - mu y_c (scaled by 1 / nu at the end), y_c scaled by
+  // 1 / sqrt(a); a later z with h1 = z . y_c, h2 = z . y_c+1 loses a2 = (h2 - mu h1) / nu^2
+  // times y_c+1 and h1 / a - mu a2 times y_c.
   float ys = 1.f;
-  for (int c = 0; c < rr; ++c) {
+  for (int c = 0; c < rr; c += 2) {
+    const bool pair = c + 1 < rr;  // uniform
     float n4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 32; ++s) n4[s & 3] += Y[s] * Y[s];
     float nn = (n4[0] + n4[1]) + (n4[2] + n4[3]);
     nn += partner(nn);
-    float* buf = h ? S.bw : S.bv;
-    if (c32 == c) {
+    if (c32 == c || c32 == c + 1) {
+      float* buf = (c32 == c ? S.y2 : S.bvw) + N * h;
 #pragma unroll
       for (int s4 = 0; s4 < 8; ++s4)
         reinterpret_cast<float4*>(buf)[s4] = make_float4(Y[4 * s4], Y[4 * s4 + 1], Y[4 * s4 + 2], Y[4 * s4 + 3]);
     }
     wave_lds_sync();
-    const float nc = bcast(nn, c);
-    const float f2 = nc > 0.f ? 1.f / nc : 0.f;
-    float yc[32];
+    float ya[32], yb[32];
 #pragma unroll
     for (int s4 = 0; s4 < 8; ++s4) {
-      const float4 v4 = reinterpret_cast<const float4*>(buf)[s4];
-      yc[4 * s4] = v4.x; yc[4 * s4 + 1] = v4.y; yc[4 * s4 + 2] = v4.z; yc[4 * s4 + 3] = v4.w;
+      const float4 a4 = reinterpret_cast<const float4*>(S.y2 + N * h)[s4];
+      const float4 b4 = reinterpret_cast<const float4*>(S.bvw + N * h)[s4];
+      ya[4 * s4] = a4.x; ya[4 * s4 + 1] = a4.y; ya[4 * s4 + 2] = a4.z; ya[4 * s4 + 3] = a4.w;
+      yb[4 * s4] = b4.x; yb[4 * s4 + 1] = b4.y; yb[4 * s4 + 2] = b4.z; yb[4 * s4 + 3] = b4.w;
     }
-    float h4[4] = {0.f, 0.f, 0.f, 0.f};
+    float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) h4[s & 3] += Y[s] * yc[s];
-    float hd = (h4[0] + h4[1]) + (h4[2] + h4[3]);
-    hd += partner(hd);
-    hd = c32 > c ? hd * f2 : 0.f;
+    for (int s = 0; s < 32; ++s) {
+      p4[s & 3] += Y[s] * ya[s];
+      q4[s & 3] += Y[s] * yb[s];
+    }
+    float h1 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+    float h2 = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+    h1 += partner(h1);
+    h2 += partner(h2);
+    const float a = bcast(nn, c);
+    const float d = pair ? bcast(nn, c + 1) : 0.f;
+    const float b = pair ? bcast(h1, c + 1) : 0.f;
+    const float ia = a > 0.f ? 1.f / a : 0.f;
+    const float mu = b * ia;
+    const float nu2 = d - mu * b;
+    const float inu2 = pair && nu2 > 0.f ? 1.f / nu2 : 0.f;
+    float f1 = 0.f, f2 = 0.f;
+    if (c32 > c + 1 || (!pair && c32 > c)) {
+      f2 = pair ? (h2 - mu * h1) * inu2 : 0.f;
+      f1 = h1 * ia - mu * f2;
+    } else if (pair && c32 == c + 1) {
+      f1 = mu;
+    }
 #pragma unroll
-    for (int s = 0; s < 32; ++s) Y[s] -= hd * yc[s];
-    if (c32 == c) ys = nc > 0.f ? 1.f / sqrtf(nc) : 0.f;
+    for (int s = 0; s < 32; ++s) Y[s] -= f1 * ya[s] + f2 * yb[s];
+    if (c32 == c) ys = a > 0.f ? 1.f / sqrtf(a) : 0.f;
+    if (pair && c32 == c + 1) ys = nu2 > 0.f ? 1.f / sqrtf(nu2) : 0.f;
     wave_lds_sync();
   }
 #pragma unroll
   for (int s = 0; s < 32; ++s) Y[s] = c32 < rr ? Y[s] * ys : 0.f;
 
-  // ---- back-transformation Y <- H_0 H_1 ... H_{N-3} Y -------------------------------------------
-  for (int j = N - 3; j >= 0; --j) {
-    const float tj = S.tau[j];
-    if (tj == 0.f) continue;  // uniform
-    const float vj = MGET(Bm, j);
-    S.bv[(lane & 1) * 32 + (lane >> 1)] = vj;
-    wave_lds_sync();
-    float vv[32];
+  // ---- back-transformation Y <- H_0 H_1 ... H_{N-3} Y, two reflectors at a time --------------
+  // H_{j-1} H_j Y = Y - t_j v_j g1 - t_{j-1} v_{j-1} (g0 - t_j kappa g1) with g1 = v_j^T Y,
+  // g0 = v_{j-1}^T Y and kappa = v_{j-1}^T v_j. Vectors go through LDS with entry i at
+  // (i % 2) 32 + i / 2, so that each lane half reads its parity as 8 float4.
+  {
+    const int pos = (lane & 1) * 32 + (lane >> 1);
+    for (int j = N - 3; j >= 0; j -= 2) {
+      const bool two = j >= 1;  // uniform
+      const float t1 = S.tau[j];
+      const float t0 = two ? S.tau[j - 1] : 0.f;
+      if (t1 == 0.f && t0 == 0.f) continue;  // uniform
+      const float v1 = MGET(Bm, j);
+      const float v0 = two ? MGET(Bm, j - 1) : 0.f;
+      const float kap = uni(wsum(v0 * v1));
+      S.y2[pos] = v1;
+      S.bvw[pos] = v0;
+      wave_lds_sync();
+      float a1[32], a0[32];
 #pragma unroll
-    for (int s4 = 0; s4 < 8; ++s4) {
-      const float4 v4 = reinterpret_cast<const float4*>(S.bv + 32 * h)[s4];
-      vv[4 * s4] = v4.x; vv[4 * s4 + 1] = v4.y; vv[4 * s4 + 2] = v4.z; vv[4 * s4 + 3] = v4.w;
+      for (int s4 = 0; s4 < 8; ++s4) {
+        const float4 x4 = reinterpret_cast<const float4*>(S.y2 + 32 * h)[s4];
+        const float4 z4 = reinterpret_cast<const float4*>(S.bvw + 32 * h)[s4];
+        a1[4 * s4] = x4.x; a1[4 * s4 + 1] = x4.y; a1[4 * s4 + 2] = x4.z; a1[4 * s4 + 3] = x4.w;
+        a0[4 * s4] = z4.x; a0[4 * s4 + 1] = z4.y; a0[4 * s4 + 2] = z4.z; a0[4 * s4 + 3] = z4.w;
+      }
+      float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 32; ++s) {
+        p4[s & 3] += a1[s] * Y[s];
+        q4[s & 3] += a0[s] * Y[s];
+      }
+      float g1 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+      float g0 = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+      g1 += partner(g1);
+      g0 += partner(g0);
+      const float f1 = t1 * g1;
+      const float f0 = t0 * (g0 - kap * f1);
+#pragma unroll
+      for (int s = 0; s < 32; ++s) Y[s] -= f1 * a1[s] + f0 * a0[s];
+      wave_lds_sync();
     }
-    float h4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 32; ++s) h4[s & 3] += vv[s] * Y[s];
-    float hd = (h4[0] + h4[1]) + (h4[2] + h4[3]);
-    hd = tj * (hd + partner(hd));
-#pragma unroll
-    for (int s = 0; s < 32; ++s) Y[s] -= hd * vv[s];
-    wave_lds_sync();
   }
 
   // eigenvalue floor: tiny or negative eigenvalues give zero columns
