@@ -383,11 +383,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
   }
 
-  // ---- pivoted Cholesky of G_U in place (L column s in the register of pivot p_s) --------------
+  // ---- pivoted Cholesky of G_U (L column s into column p_s of the LDS copy) --------------------
+  // The rank-one update of step s - 1 is applied to the registers during step s (its vector read
+  // back from the other LDS buffer), so that it overlaps the next pivot search; the pivot column
+  // of step s gets that update on its own: col = G[:, p] - l_{s-1} l_{s-1}[p].
   float d = du * (bal * bal);
   uint64_t chosen = 0;
   {
     const float tol = uni(kPivTol * wmax(d));
+    float lprev = 0.f;
     for (int s = 0; s < N; ++s) {
       const bool was = (chosen >> lane) & 1ull;
       const int key = (!was && d > 0.f) ? __float_as_int(d) : -1;   // d is finite
@@ -398,24 +402,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const int p = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
       const float rp = __builtin_amdgcn_rsqf(vmax);
       const float piv = vmax * rp;
-      const float col = MGET(GU, p);
+      const float col = MGET(GU, p) - lprev * bcast(lprev, p);
       float l = was ? 0.f : col * rp;
       if (lane == p) l = piv;
-      S.bvw[lane] = l;
-      wave_lds_sync();
+      S.bvw[N * (s & 1) + lane] = l;
+      S.Lp[lane * LDL + p] = l;
+      if (s > 0) {  // uniform: the deferred update of step s - 1
+        const float* prv = S.bvw + N * ((s - 1) & 1);
 #pragma unroll
-      for (int c4 = 0; c4 < N / 4; ++c4) {
-        const float4 b4 = reinterpret_cast<const float4*>(S.bvw)[c4];
-        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        for (int c4 = 0; c4 < N / 4; ++c4) {
+          const float4 b4 = reinterpret_cast<const float4*>(prv)[c4];
+          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = 4 * c4 + e;
-          MSET(GU, c, MGET(GU, c) - l * bb[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int c = 4 * c4 + e;
+            MSET(GU, c, fmaf(-lprev, bb[e], MGET(GU, c)));
+          }
         }
       }
-      S.Lp[lane * LDL + p] = l;     // L column s lands in column p (the register keeps ~0)
       d -= l * l;
       chosen |= 1ull << p;
+      lprev = l;
       wave_lds_sync();
     }
   }
@@ -670,7 +677,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       f1 = mu;
     }
 #pragma unroll
-    for (int s = 0; s < 32; ++s) Y[s] -= f1 * ya[s] + f2 * yb[s];
+    for (int s = 0; s < 32; ++s) Y[s] = fmaf(-f2, yb[s], fmaf(-f1, ya[s], Y[s]));
     if (c32 == c) ys = a > 0.f ? 1.f / sqrtf(a) : 0.f;
     if (pair && c32 == c + 1) ys = nu2 > 0.f ? 1.f / sqrtf(nu2) : 0.f;
     wave_lds_sync();
@@ -716,7 +723,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const float f1 = t1 * g1;
       const float f0 = t0 * (g0 - kap * f1);
 #pragma unroll
-      for (int s = 0; s < 32; ++s) Y[s] -= f1 * a1[s] + f0 * a0[s];
+      for (int s = 0; s < 32; ++s) Y[s] = fmaf(-f0, a0[s], fmaf(-f1, a1[s], Y[s]));
       wave_lds_sync();
     }
   }
