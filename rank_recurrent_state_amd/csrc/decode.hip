@@ -9,7 +9,8 @@
 // workgroup. The step is HBM-bound: its bytes are the m columns of U and of V, read once.
 // Each lane owns a 16-byte slice of a column; a wave-wide load covers 64 / (lanes per column)
 // whole columns, so every load instruction streams a contiguous 1 KiB. All U and V loads of
-// the unit are issued before any arithmetic, which keeps up to 32 KiB per wave in flight.
+// the unit are issued before any arithmetic, which keeps up to 32 KiB per wave in flight. With
+// bf16 factors and inputs the U pass uses packed bf16 dot products (v_dot2_f32_bf16).
 //   U pass: per column, x_j = (G U)_j . kappa and y_j = (G U)_j . q, reduced over the lanes of
 //           the column with DPP row operations. The decay is lazy: U is never rewritten, the
 //           per-column scales (GDN, Mamba-2) or per-channel Gamma (KDA) absorb it.
@@ -20,6 +21,11 @@
 #include "kernels.hpp"
 
 namespace seed {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Third word of a raw buffer resource on gfx9-family chips (32-bit data, no swizzle).
+constexpr int kRawBufferWord3 = 0x00020000;
 
 template <int FDT, int VF>
 __device__ __forceinline__ void unpack16(const uint4& r, float (&out)[VF]) {
@@ -69,26 +75,45 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
 
   // ---- 1. stream the factors: every U and V load of the unit is issued first -----------------
-  // Loads are unconditional so that none of them waits on another: a lane whose column is past
-  // the live ones (j >= m) re-reads column m - 1, which the same instruction already fetches, and
-  // its contribution is dropped below. Columns m..slots-1 may hold anything, even NaN.
+  // Buffer loads whose range ends at column m: a lane whose column is past the live ones reads
+  // zeros (the range check covers the lane offset and the immediate, so the column offset is
+  // kept there), and no load waits on another. Columns m..slots-1 may hold anything, even NaN.
+  const __amdgpu_buffer_rsrc_t ru =
+      __builtin_amdgcn_make_buffer_rsrc(Ub, 0, m * DK * static_cast<int>(sizeof(FT)), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(Vb, 0, m * DV * static_cast<int>(sizeof(FT)), kRawBufferWord3);
+  const int uoff = (ug * DK + uo) * static_cast<int>(sizeof(FT));
+  const int voff = (vg * DV + vo) * static_cast<int>(sizeof(FT));
   uint4 ur[NIU];
   uint4 vr[NIV];
 #pragma unroll
   for (int i = 0; i < NIU; ++i) {
-    const int j = min(i * CPU_ + ug, m - 1);
-    ur[i] = *reinterpret_cast<const uint4*>(Ub + j * DK + uo);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(ru, uoff + i * CPU_ * DK * static_cast<int>(sizeof(FT)), 0, 0);
+    ur[i] = make_uint4(x[0], x[1], x[2], x[3]);
   }
 #pragma unroll
   for (int i = 0; i < NIV; ++i) {
-    const int j = min(i * CPV + vg, m - 1);
-    vr[i] = *reinterpret_cast<const uint4*>(Vb + j * DV + vo);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + i * CPV * DV * static_cast<int>(sizeof(FT)), 0, 0);
+    vr[i] = make_uint4(x[0], x[1], x[2], x[3]);
   }
+  // keep every factor load ahead of the first wait (the scheduler would otherwise sink the V
+  // loads below the U pass to save registers, serialising the two latencies)
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- 2. per-unit vectors: key-side slices in U layout, value-side slices in V layout -------
+  // bf16 factors with bf16 inputs (no channel gate): the U pass takes packed bf16 dot products
+  constexpr bool DOT2 = (FDT == 1) && (IDT == 1) && !DIAG;
   float qv[VF], kv[VF], av[VF];
-  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.q) + unit * DK + uo, qv);
-  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.k) + unit * DK + uo, kv);
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u), kraw = qraw;
+  if constexpr (DOT2) {
+    qraw = *reinterpret_cast<const uint4*>(reinterpret_cast<const IT*>(A.q) + unit * DK + uo);
+    kraw = *reinterpret_cast<const uint4*>(reinterpret_cast<const IT*>(A.k) + unit * DK + uo);
+    unpack16<1, VF>(qraw, qv);
+    unpack16<1, VF>(kraw, kv);
+  } else {
+    load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.q) + unit * DK + uo, qv);
+    load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.k) + unit * DK + uo, kv);
+  }
   load_f32<0, VF>(A.a + unit * DK + uo, av);
   const float beta = A.beta[unit];
   float gv[VF];
@@ -165,13 +190,25 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   // ---- 5. U pass: x = (G U)^T kappa, y = (G U)^T q ----------------------------------------------
 #pragma unroll
   for (int i = 0; i < NIU; ++i) {
-    float u[VF];
-    unpack16<FDT, VF>(ur[i], u);
     float pk = 0.f, pq = 0.f;
+    if constexpr (DOT2) {
+      const uint32_t uw[4] = {ur[i].x, ur[i].y, ur[i].z, ur[i].w};
+      const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+      const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
 #pragma unroll
-    for (int e = 0; e < VF; ++e) {
-      if constexpr (DELTA) pk += u[e] * kt[e];
-      pq += u[e] * qt[e];
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 ue = __builtin_bit_cast(bf16x2, uw[e]);
+        if constexpr (DELTA) pk = __builtin_amdgcn_fdot2_f32_bf16(ue, __builtin_bit_cast(bf16x2, kw[e]), pk, false);
+        pq = __builtin_amdgcn_fdot2_f32_bf16(ue, __builtin_bit_cast(bf16x2, qw[e]), pq, false);
+      }
+    } else {
+      float u[VF];
+      unpack16<FDT, VF>(ur[i], u);
+#pragma unroll
+      for (int e = 0; e < VF; ++e) {
+        if constexpr (DELTA) pk += u[e] * kt[e];
+        pq += u[e] * qt[e];
+      }
     }
     if constexpr (DELTA) pk = group_sum<LPU>(pk);
     pq = group_sum<LPU>(pq);
