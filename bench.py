@@ -35,6 +35,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Measured HBM traffic of the decode kernel (two rocprofv3 counter runs, scaled by a calibration
+# copy); used only while the kernel sources still hash to the digest recorded with it.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_gdn-stack36_hbm_traffic.txt")
+DECODE_SOURCES = ("rank_recurrent_state_amd/csrc/decode.hip", "rank_recurrent_state_amd/csrc/common.hpp",
+                  "rank_recurrent_state_amd/csrc/kernels.hpp")
 METRIC = "factored decode head-steps/s + achieved HBM GB/s (% roofline) vs dense-state kernel"
 
 
@@ -55,9 +60,36 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--seed", type=int, default=1005)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--source-digest", action="store_true",
+                    help="print the digest of the decode kernel sources and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (scales HBM byte counters under a profiler)")
     return ap.parse_args()
+
+
+def decode_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """Bytes per decode launch from the counter profile, if it matches the current sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_sha256") != decode_source_digest() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def decode_bytes(w, m: int) -> int:
@@ -100,6 +132,9 @@ def cpu_worker(job):
 
 def main():
     args = parse()
+    if args.source_digest:
+        print(decode_source_digest())
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is "
               "data-parallel over independent units and has no multi-GPU mode.", file=sys.stderr)
@@ -341,7 +376,7 @@ def main():
                    "layers": L, "factor_storage": "bf16" if w.factor_dtype else "fp32",
                    "prefill_tokens": prefill},
         "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
                      "kernel": "k_decode (factored read-out + update)",
                      "bytes_per_launch": dec_bytes / n_dec_launch,
                      "avg_launch_us": avg_launch_us},

@@ -60,9 +60,8 @@ hipError_t launch_decode(const seed_shape& sh, const StepArgs& a, hipStream_t s)
 hipError_t launch_dense(const seed_shape& sh, const DenseArgs& a, hipStream_t s);
 hipError_t launch_compress(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
 hipError_t launch_from_dense(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
-// Tridiagonal-core compression (bf16 factors, r <= 32); *used tells whether it took the call.
-hipError_t launch_compress_tri(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used);
-// One-wavefront-per-unit compression with the core in registers (bf16 factors, r <= 32).
+// One-wavefront-per-unit compression with the core in registers (bf16 factors, r <= 32,
+// r + T <= 64); *used tells whether it took the call.
 hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used);
 
 // Whether a compiled instance exists for this shape (host-side dispatch tables).
