@@ -46,6 +46,7 @@ constexpr int RX = 32;          // maximum rank on this path
 constexpr int LDL = N + 1;      // LDS row stride of L (odd: row and column reads both conflict-free)
 constexpr int NSEC = 7;         // 5-section steps after the 128-point grid (129 * 5^7 ~ 1e7)
 constexpr float kPivTol = 1e-7f;
+constexpr float kReduceFloor = 1e-30f;  // squared column norm below which no reflector is built
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
@@ -142,7 +143,10 @@ __device__ __forceinline__ float bcast(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 
-__device__ __forceinline__ float nz(float x) { return x == 0.f ? -FLT_MIN : x; }
+// A pivot of a shifted factorisation that is zero or tiny is replaced by -kPivFloor (B is
+// scaled to entries <= 1, so the replacement is far below any meaningful pivot).
+constexpr float kPivFloor = 1e-30f;
+__device__ __forceinline__ float nz(float x) { return fabsf(x) < kPivFloor ? -kPivFloor : x; }
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -441,6 +445,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const M64 bt = times_L(rt.lo, rt.hi, S.Lp);   // (L^T G_V L)^T, symmetric up to rounding
     Bm_lo = bt.lo; Bm_hi = bt.hi;
   }
+  // The eigen phase works on B / bs (bs = largest |entry|): entries of order one keep every
+  // intermediate (reflector norms, pivots of the shifted factorisations) far from the denormal
+  // range, where the hardware reciprocal flushes to zero. Eigenvalues are scaled back below.
+  float bs;
+  {
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < N; ++c) mx = fmaxf(mx, fabsf(MGET(Bm, c)));
+    bs = uni(wmax(mx));
+    const float ibs = bs > 0.f ? 1.f / bs : 0.f;
+#pragma unroll
+    for (int c = 0; c < N; ++c) MSET(Bm, c, MGET(Bm, c) * ibs);
+  }
 
   // ---- Householder tridiagonalisation, the reflectors kept in the registers they zero ---------
   // From step 16 qt on, v and w vanish on lanes (and registers) below 16 qt, so quarter qt of
@@ -456,7 +473,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const float x0 = bcast(x, j + 1);
       const float djj = bcast(colj, j);
       float t = 0.f, ej = x0, v = x;
-      if (sig - x0 * x0 > 1e-30f * sig && sig > 0.f) {  // uniform
+      // below the floor the column is already reduced (B is scaled to entries <= 1)
+      if (sig - x0 * x0 > 1e-30f * sig && sig > kReduceFloor) {  // uniform
         const float al = x0 >= 0.f ? -sqrtf(sig) : sqrtf(sig);
         const float v0 = x0 - al;
         t = 2.f * __builtin_amdgcn_rcpf(sig - x0 * x0 + v0 * v0);
@@ -731,7 +749,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   // eigenvalue floor: tiny or negative eigenvalues give zero columns
   const float lmax = uni(wmax(c32 < rr ? lam : 0.f));
   const bool live = c32 < rr && lam > lmax * 1e-14f;
-  const float q4 = live ? sqrtf(sqrtf(lam)) : 1.f;
+  const float q4 = live ? sqrtf(sqrtf(lam * bs)) : 1.f;   // of the unscaled eigenvalue
   const float qv = live ? 1.f / q4 : 0.f;          // lambda^(-1/4)
   const float qu = live ? 1.f / (q4 * q4) : 0.f;   // lambda^(-1/2)
 

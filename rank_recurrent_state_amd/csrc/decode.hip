@@ -42,6 +42,22 @@ __device__ __forceinline__ void unpack16(const uint4& r, float (&out)[VF]) {
   }
 }
 
+template <int FDT, int VF>
+__device__ __forceinline__ uint4 pack16(const float (&in)[VF]) {
+  if constexpr (FDT == 0) {
+    return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]), __float_as_uint(in[3]));
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = static_cast<uint32_t>(f32_to_bf16(in[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(in[2 * e + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// KDA: a channel's cumulative gate below this is folded into the stored factors (2^-40).
+constexpr float kFoldFloor = 9.094947e-13f;
+
 template <int KIND, int DK, int DV, int FDT, int IDT, int MAXC>
 __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   using FT = stor_t<FDT>;
@@ -137,9 +153,37 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   if constexpr (DIAG) {
     float Gm[VF];
     load_f32<0, VF>(sc + uo, Gm);
+    bool tiny = false;
 #pragma unroll
     for (int e = 0; e < VF; ++e) {
       Gn[e] = gv[e] * Gm[e];  // Gamma <- alpha . Gamma
+      tiny |= !(Gn[e] >= kFoldFloor);
+    }
+    if (__ballot(tiny) != 0) {
+      // A channel whose Gamma fell below the floor (a zero gate included) is folded into the
+      // stored columns now, U_s[d][:] *= Gamma_d, and restarts at Gamma_d = 1, so that the new
+      // column kappa / Gamma stays finite. Rare (uniform branch); the fold is exact up to the
+      // rounding of the rewritten factors.
+      float f[VF];
+#pragma unroll
+      for (int e = 0; e < VF; ++e) {
+        const bool fold = !(Gn[e] >= kFoldFloor);
+        f[e] = fold ? Gn[e] : 1.f;
+        Gn[e] = fold ? 1.f : Gn[e];
+      }
+#pragma unroll
+      for (int i = 0; i < NIU; ++i) {
+        const int j = i * CPU_ + ug;
+        float u[VF];
+        unpack16<FDT, VF>(ur[i], u);
+#pragma unroll
+        for (int e = 0; e < VF; ++e) u[e] *= f[e];
+        if (j < m) store_f32<FDT, VF>(Ub + static_cast<int64_t>(j) * DK + uo, u);
+        ur[i] = pack16<FDT, VF>(u);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VF; ++e) {
       kt[e] = Gn[e] * kv[e];
       qt[e] = Gn[e] * qv[e];
     }

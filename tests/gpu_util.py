@@ -71,6 +71,14 @@ def relF(A, B):
     return float(np.linalg.norm(A - B) / nb) if nb > 0 else float(np.linalg.norm(A))
 
 
+def rel_out(o_gpu, o_ref, S_ref, q) -> float:
+    """Relative error of a read-out o = S^T q. The denominator is |o_ref|, floored at
+    1e-2 |S|_F |q|: when q is nearly orthogonal to the state, the output is a cancellation far
+    below its natural scale and no fp32 evaluation can hold it to a relative bound."""
+    den = max(float(np.linalg.norm(o_ref)), 1e-2 * float(np.linalg.norm(S_ref)) * float(np.linalg.norm(q)))
+    return float(np.linalg.norm(o_gpu - o_ref) / den) if den > 0 else float(np.linalg.norm(o_gpu))
+
+
 def tolerance(w_or_dtype) -> float:
     code = w_or_dtype.factor_dtype if hasattr(w_or_dtype, "factor_dtype") else w_or_dtype
     return 2e-2 if code == synth.BF16 else 1e-5
@@ -96,3 +104,61 @@ def compare_compression(C_before, a, vbar, U_gpu, V_gpu, r, code, a_ref=None):
         ok = orc.truncation_is_optimal(C, U_gpu @ V_gpu.T, r, tolerance(code), abs_tol=tolerance(code) ** 2)
         return "optimal", (0.0 if ok else float("inf")), relF(S_gpu, S_ref)
     return "product", relF(S_gpu, S_ref), relF(S_gpu, S_ref)
+
+
+def check_decode_call(rrs, sh, st, m, dx, vbar_dev, vbar_np, heads, units, o):
+    """One teacher-forced decode call on the GPU, compared with the oracle's Lemma 2 step on
+    `units`. Returns (max rel error of S~, max rel error of o)."""
+    import torch
+    pre = host_state(sh, st, units, m)
+    rrs.seed_decode_step(sh, st, m, dx["q"], dx["k"], dx["v"], dx["beta"], dx["g"], vbar_dev, o)
+    post = host_state(sh, st, units, m + 1)
+    og = o.index_select(0, torch.as_tensor(list(units), device=o.device)).double().cpu().numpy()
+    hx = host_inputs(dx, units)
+    eS = eo = 0.0
+    for i, u in enumerate(units):
+        vb = vbar_np[u % heads]
+        X = hx[i]
+        a1, U1, V1, o1 = orc.factored_step(sh.kind, *pre[i], vb, X["q"], X["k"], X["v"], X["beta"], X["g"])
+        S1 = orc.reconstruct(a1, vb, U1, V1)
+        eS = max(eS, relF(orc.reconstruct(post[i][0], vb, post[i][1], post[i][2]), S1))
+        eo = max(eo, rel_out(og[i], o1, S1, X["q"]))
+    return eS, eo
+
+
+def check_compress_call(rrs, sh, st, m, vbar_np, heads, units, code):
+    """One compression call on the GPU, compared with the oracle's exact truncation of the
+    same content on `units`. Returns (worst error per compare_compression, near-tie count)."""
+    pre = host_state(sh, st, units, m)
+    rrs.seed_compress(sh, st, m)
+    post = host_state(sh, st, units, sh.rank)
+    worst, ties, raw = 0.0, 0, 0.0
+    for i, u in enumerate(units):
+        vb = vbar_np[u % heads]
+        kind, err, rw = compare_compression((pre[i][1], pre[i][2]), post[i][0], vb, post[i][1],
+                                            post[i][2], sh.rank, code, a_ref=pre[i][0])
+        worst = max(worst, err)
+        raw = max(raw, rw)
+        ties += kind == "optimal"
+    check_compress_call.last_raw = raw
+    return worst, ties
+
+
+def check_from_dense_call(rrs, sh, S, vbar_dev, vbar_np, heads, units, code):
+    """seed_state_from_dense on the GPU against the oracle's split + truncation of the same
+    dense states. Returns (state, worst error, near-tie count)."""
+    import torch
+    st = rrs.State.empty(sh)
+    rrs.seed_state_from_dense(sh, S, vbar_dev, st)
+    Sg = S.index_select(0, torch.as_tensor(list(units), device=S.device)).double().cpu().numpy()
+    post = host_state(sh, st, units, sh.rank)
+    worst, ties = 0.0, 0
+    for i, u in enumerate(units):
+        vb = vbar_np[u % heads]
+        a_o, _, _, _ = orc.from_dense(Sg[i], vb, sh.rank)
+        _, C = orc.sink_split(Sg[i], vb)
+        kind, err, _ = compare_compression(C, post[i][0], vb, post[i][1], post[i][2], sh.rank, code,
+                                           a_ref=a_o)
+        worst = max(worst, err)
+        ties += kind == "optimal"
+    return st, worst, ties
