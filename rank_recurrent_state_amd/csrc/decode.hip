@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
 
   __shared__ float xs[4][MAXC];
   __shared__ float ys[4][MAXC];
+  __shared__ float cscl[4][MAXC];  // per-column decay scale (GDN, Mamba-2)
 
   const int lane = threadIdx.x & (kWave - 1);
   // the wave index is uniform: keep it (and every per-unit address) in scalar registers
@@ -148,7 +149,6 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   // lazy decay state
   float* __restrict__ sc = A.scale + unit * A.scale_len;
   float kt[VF], qt[VF], Gn[VF];
-  float cs[NIU];
   float own_scale = 0.f;
   if constexpr (DIAG) {
     float Gm[VF];
@@ -190,13 +190,12 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   } else {
 #pragma unroll
     for (int e = 0; e < VF; ++e) { kt[e] = kv[e]; qt[e] = qv[e]; }
-    // one load per lane: lane l holds slot min(l, m - r); column j's scale comes from its slot
+    // one load per lane: lane l holds slot min(l, m - r); column l's scale comes from its slot
+    // (columns past the live ones get a finite stand-in: their loads read zeros)
     own_scale = sc[min(lane, m - r)];
-#pragma unroll
-    for (int i = 0; i < NIU; ++i) {
-      const int j = i * CPU_ + ug;
-      cs[i] = gs * __shfl(own_scale, j < r ? 0 : min(1 + j - r, m - r));
-    }
+    const float cl = gs * __shfl(own_scale, lane < r ? 0 : min(1 + lane - r, m - r));
+    if (lane < MAXC) cscl[wv][lane] = cl;
+    wave_lds_sync();
   }
 
   // ---- 3. value split along vbar (omega, eps) --------------------------------------------------
@@ -257,8 +256,9 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
     if constexpr (DELTA) pk = group_sum<LPU>(pk);
     pq = group_sum<LPU>(pq);
     const int j = i * CPU_ + ug;
-    if (j < m && (lane % LPU) == 0) {
-      const float c = DIAG ? 1.f : cs[i];
+    // every column slot is written (zero past the live columns), so the V pass needs no mask
+    if ((lane % LPU) == 0) {
+      const float c = DIAG ? 1.f : cscl[wv][j];
       xs[wv][j] = c * pk;
       ys[wv][j] = c * pq;
     }
@@ -272,11 +272,8 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
 #pragma unroll
   for (int i = 0; i < NIV; ++i) {
     const int j = i * CPV + vg;
-    const bool live = j < m;
-    const float xr = DELTA ? xs[wv][j] : 0.f;
-    const float yr = ys[wv][j];
-    const float xj = live ? xr : 0.f;
-    const float yj = live ? yr : 0.f;
+    const float xj = DELTA ? xs[wv][j] : 0.f;
+    const float yj = ys[wv][j];
     float vc[VF];
     unpack16<FDT, VF>(vr[i], vc);
 #pragma unroll
