@@ -27,6 +27,25 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Third word of a raw buffer resource on gfx9-family chips (32-bit data, no swizzle).
 constexpr int kRawBufferWord3 = 0x00020000;
 
+// NI wave-wide loads of 16 bytes per lane over consecutive KiB of a unit's factor columns, with
+// the bytes past `bytes` (the columns at and after m) reading as zeros. Each resource covers
+// four loads, so one lane offset and the immediate field serve them all and the range check sees
+// the whole offset (the buffer range check covers the lane offset and the immediate only).
+template <int NI>
+__device__ __forceinline__ void load_columns(const void* base, int bytes, int lane_off, uint4 (&out)[NI]) {
+#pragma unroll
+  for (int g = 0; g < (NI + 3) / 4; ++g) {
+    const int rest = bytes - g * 4096;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(base)) + g * 4096, 0, rest > 0 ? rest : 0, kRawBufferWord3);
+#pragma unroll
+    for (int k = 0; k < 4 && 4 * g + k < NI; ++k) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + k * 1024, 0, 0);
+      out[4 * g + k] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+  }
+}
+
 template <int FDT, int VF>
 __device__ __forceinline__ void unpack16(const uint4& r, float (&out)[VF]) {
   if constexpr (FDT == 0) {
@@ -58,19 +77,38 @@ __device__ __forceinline__ uint4 pack16(const float (&in)[VF]) {
 // KDA: a channel's cumulative gate below this is folded into the stored factors (2^-40).
 constexpr float kFoldFloor = 9.094947e-13f;
 
+// Lane geometry of one unit, and how its factors are staged. A lane owns a 16-byte slice of a
+// column; NIU (NIV) wave-wide loads cover MAXC columns of U (V). When both sets together would
+// hold more than 96 registers per lane, V is loaded only after the U pass has consumed U, so a
+// wave needs half the registers and twice as many waves are resident.
+template <int DK, int DV, int FDT, int MAXC>
+struct DecodeGeom {
+  static constexpr int VF = FDT == 0 ? 4 : 8;
+  static constexpr int LPU = DK / VF, CPU_ = kWave / LPU, LPV = DV / VF, CPV = kWave / LPV;
+  static constexpr int NIU = (MAXC + CPU_ - 1) / CPU_, NIV = (MAXC + CPV - 1) / CPV;
+  static constexpr bool SPLIT = (NIU + NIV) * 4 > 96;
+  static constexpr int DATA = 4 * (SPLIT ? (NIU > NIV ? NIU : NIV) : NIU + NIV);
+  // waves per SIMD the register budget is cut for (512 registers per lane per SIMD)
+  static constexpr int WAVES = DATA <= 64 ? 4 : (DATA <= 128 ? 2 : 1);
+};
+
 template <int KIND, int DK, int DV, int FDT, int IDT, int MAXC>
-__global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeGeom<DK, DV, FDT, MAXC>::WAVES)))
+void k_decode(const StepArgs A) {
   using FT = stor_t<FDT>;
   using IT = stor_t<IDT>;
-  constexpr int VF = 16 / sizeof(FT);      // factor elements per 16-byte lane slice
-  constexpr int LPU = DK / VF;             // lanes per U column
-  constexpr int CPU_ = kWave / LPU;        // U columns per wave-wide load
-  constexpr int LPV = DV / VF;
-  constexpr int CPV = kWave / LPV;
-  constexpr int NIU = (MAXC + CPU_ - 1) / CPU_;
-  constexpr int NIV = (MAXC + CPV - 1) / CPV;
+  using Geo = DecodeGeom<DK, DV, FDT, MAXC>;
+  constexpr int VF = Geo::VF;       // factor elements per 16-byte lane slice
+  constexpr int LPU = Geo::LPU;     // lanes per U column
+  constexpr int CPU_ = Geo::CPU_;   // U columns per wave-wide load
+  constexpr int LPV = Geo::LPV;
+  constexpr int CPV = Geo::CPV;
+  constexpr int NIU = Geo::NIU;
+  constexpr int NIV = Geo::NIV;
+  constexpr bool SPLIT = Geo::SPLIT;
   constexpr bool DELTA = (KIND != SEED_MAMBA2);
   constexpr bool DIAG = (KIND == SEED_KDA);
+  static_assert(VF * sizeof(FT) == 16, "16-byte lane slices");
   static_assert(LPU <= kWave && LPV <= kWave, "column wider than a wave");
 
   __shared__ float xs[4][MAXC];
@@ -91,67 +129,45 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
   FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(C) * DK;
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
 
-  // ---- 1. stream the factors: every U and V load of the unit is issued first -----------------
+  // ---- 1. stream the factors ------------------------------------------------------------------
   // Buffer loads whose range ends at column m: a lane whose column is past the live ones reads
   // zeros (the range check covers the lane offset and the immediate, so the column offset is
   // kept there), and no load waits on another. Columns m..slots-1 may hold anything, even NaN.
-  const __amdgpu_buffer_rsrc_t ru =
-      __builtin_amdgcn_make_buffer_rsrc(Ub, 0, m * DK * static_cast<int>(sizeof(FT)), kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(Vb, 0, m * DV * static_cast<int>(sizeof(FT)), kRawBufferWord3);
+  static_assert(CPU_ * DK * sizeof(FT) == 1024 && CPV * DV * sizeof(FT) == 1024, "1 KiB per load");
   const int uoff = (ug * DK + uo) * static_cast<int>(sizeof(FT));
   const int voff = (vg * DV + vo) * static_cast<int>(sizeof(FT));
   uint4 ur[NIU];
   uint4 vr[NIV];
-#pragma unroll
-  for (int i = 0; i < NIU; ++i) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(ru, uoff + i * CPU_ * DK * static_cast<int>(sizeof(FT)), 0, 0);
-    ur[i] = make_uint4(x[0], x[1], x[2], x[3]);
-  }
-#pragma unroll
-  for (int i = 0; i < NIV; ++i) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + i * CPV * DV * static_cast<int>(sizeof(FT)), 0, 0);
-    vr[i] = make_uint4(x[0], x[1], x[2], x[3]);
-  }
-  // keep every factor load ahead of the first wait (the scheduler would otherwise sink the V
-  // loads below the U pass to save registers, serialising the two latencies)
+  auto load_v = [&]() { load_columns<NIV>(Vb, m * DV * static_cast<int>(sizeof(FT)), voff, vr); };
+  load_columns<NIU>(Ub, m * DK * static_cast<int>(sizeof(FT)), uoff, ur);
+  if constexpr (!SPLIT) load_v();
+  // keep the factor loads ahead of the first wait (the scheduler would otherwise sink them
+  // below the U pass to save registers, serialising the latencies)
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. per-unit vectors: key-side slices in U layout, value-side slices in V layout -------
+  // ---- 2. key-side vectors (U layout) and the lazy decay state ----------------------------------
   // bf16 factors with bf16 inputs (no channel gate): the U pass takes packed bf16 dot products
   constexpr bool DOT2 = (FDT == 1) && (IDT == 1) && !DIAG;
-  float qv[VF], kv[VF], av[VF];
+  const IT* __restrict__ qp = reinterpret_cast<const IT*>(A.q) + unit * DK + uo;
+  const IT* __restrict__ kp = reinterpret_cast<const IT*>(A.k) + unit * DK + uo;
   uint4 qraw = make_uint4(0u, 0u, 0u, 0u), kraw = qraw;
+  float kt[VF], qt[VF];  // the U pass's operands (KDA: Gamma . kappa, Gamma . q)
   if constexpr (DOT2) {
-    qraw = *reinterpret_cast<const uint4*>(reinterpret_cast<const IT*>(A.q) + unit * DK + uo);
-    kraw = *reinterpret_cast<const uint4*>(reinterpret_cast<const IT*>(A.k) + unit * DK + uo);
-    unpack16<1, VF>(qraw, qv);
-    unpack16<1, VF>(kraw, kv);
+    qraw = *reinterpret_cast<const uint4*>(qp);
+    kraw = *reinterpret_cast<const uint4*>(kp);
   } else {
-    load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.q) + unit * DK + uo, qv);
-    load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.k) + unit * DK + uo, kv);
+    load_f32<IDT, VF>(qp, qt);
+    load_f32<IDT, VF>(kp, kt);
   }
-  load_f32<0, VF>(A.a + unit * DK + uo, av);
   const float beta = A.beta[unit];
-  float gv[VF];
-  float gs = 0.f;
-  if constexpr (DIAG) {
-    load_f32<0, VF>(A.g + unit * DK + uo, gv);
-  } else {
-    gs = A.g[unit];
-#pragma unroll
-    for (int e = 0; e < VF; ++e) gv[e] = gs;
-  }
-  float vv[VF], vb[VF];
-  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.v) + unit * DV + vo, vv);
-  load_f32<0, VF>(A.vbar + static_cast<int64_t>(head) * DV + vo, vb);
+  const float gs = DIAG ? 0.f : A.g[unit];
 
-  // lazy decay state
   float* __restrict__ sc = A.scale + unit * A.scale_len;
-  float kt[VF], qt[VF], Gn[VF];
+  float Gn[VF];
   float own_scale = 0.f;
   if constexpr (DIAG) {
-    float Gm[VF];
+    float Gm[VF], gv[VF];
+    load_f32<0, VF>(A.g + unit * DK + uo, gv);
     load_f32<0, VF>(sc + uo, Gm);
     bool tiny = false;
 #pragma unroll
@@ -182,14 +198,32 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
         ur[i] = pack16<FDT, VF>(u);
       }
     }
+    // the new U column kappa / Gamma and Gamma itself do not depend on the passes: written now
+    // (the U pass reads only the columns before m), their registers are free for the U pass
+    if (ug == 0) {
+      float nu[VF];
+#pragma unroll
+      for (int e = 0; e < VF; ++e) nu[e] = kt[e] / Gn[e];
+      store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
+      store_f32<0, VF>(sc + uo, Gn);
+    }
 #pragma unroll
     for (int e = 0; e < VF; ++e) {
-      kt[e] = Gn[e] * kv[e];
-      qt[e] = Gn[e] * qv[e];
+      kt[e] *= Gn[e];
+      qt[e] *= Gn[e];
     }
   } else {
+    // the new U column is the key itself
+    if (ug == 0) {
+      float nu[VF];
+      if constexpr (DOT2) {
+        unpack16<1, VF>(kraw, nu);
+      } else {
 #pragma unroll
-    for (int e = 0; e < VF; ++e) { kt[e] = kv[e]; qt[e] = qv[e]; }
+        for (int e = 0; e < VF; ++e) nu[e] = kt[e];
+      }
+      store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
+    }
     // one load per lane: lane l holds slot min(l, m - r); column l's scale comes from its slot
     // (columns past the live ones get a finite stand-in: their loads read zeros)
     own_scale = sc[min(lane, m - r)];
@@ -198,39 +232,7 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
     wave_lds_sync();
   }
 
-  // ---- 3. value split along vbar (omega, eps) --------------------------------------------------
-  float pvv = 0.f, pnn = 0.f;
-#pragma unroll
-  for (int e = 0; e < VF; ++e) { pvv += vv[e] * vb[e]; pnn += vb[e] * vb[e]; }
-  pvv = group_sum<LPV>(pvv);
-  pnn = group_sum<LPV>(pnn);
-  const float omega = pnn > 0.f ? pvv / pnn : 0.f;
-  float eps[VF];
-#pragma unroll
-  for (int e = 0; e < VF; ++e) eps[e] = vv[e] - omega * vb[e];
-
-  // ---- 4. sink: a_d = G a, a+ = a_d + beta (omega - kappa . a_d) kappa (Mamba-2: no kappa . a_d)
-  float ad[VF];
-  float pka = 0.f, pkq = 0.f;
-#pragma unroll
-  for (int e = 0; e < VF; ++e) {
-    ad[e] = gv[e] * av[e];
-    pka += kv[e] * ad[e];
-    pkq += kv[e] * qv[e];
-  }
-  const float ka = group_sum<LPU>(pka);
-  const float s = group_sum<LPU>(pkq);  // kappa . q: the new column's share of the read-out
-  const float coef = beta * (DELTA ? (omega - ka) : omega);
-  float an[VF];
-  float paq = 0.f;
-#pragma unroll
-  for (int e = 0; e < VF; ++e) {
-    an[e] = ad[e] + coef * kv[e];
-    paq += an[e] * qv[e];
-  }
-  const float aq = group_sum<LPU>(paq);
-
-  // ---- 5. U pass: x = (G U)^T kappa, y = (G U)^T q ----------------------------------------------
+  // ---- 3. U pass: x = (G U)^T kappa, y = (G U)^T q ----------------------------------------------
 #pragma unroll
   for (int i = 0; i < NIU; ++i) {
     float pk = 0.f, pq = 0.f;
@@ -263,9 +265,69 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
       ys[wv][j] = c * pq;
     }
   }
+
+  // ---- 4. the per-unit vectors of the update, then V when it was not loaded up front ----------
+  // q, kappa and the gate are read again (cache hits) rather than held through the U pass. The
+  // small loads go first: loads complete in order, so the sink below waits only for them.
+  if constexpr (SPLIT) __builtin_amdgcn_sched_barrier(0);
+  float qv[VF], kv[VF], gv[VF], av[VF], vv[VF], vb[VF];
+  load_f32<IDT, VF>(qp, qv);
+  load_f32<IDT, VF>(kp, kv);
+  if constexpr (DIAG) {
+    load_f32<0, VF>(A.g + unit * DK + uo, gv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VF; ++e) gv[e] = gs;
+  }
+  load_f32<0, VF>(A.a + unit * DK + uo, av);
+  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.v) + unit * DV + vo, vv);
+  load_f32<0, VF>(A.vbar + static_cast<int64_t>(head) * DV + vo, vb);
+  if constexpr (SPLIT) {
+    load_v();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   wave_lds_sync();
 
-  // ---- 6. V pass: V x and V y -------------------------------------------------------------------
+  // value split along vbar (omega, eps)
+  float pvv = 0.f, pnn = 0.f;
+#pragma unroll
+  for (int e = 0; e < VF; ++e) { pvv += vv[e] * vb[e]; pnn += vb[e] * vb[e]; }
+  pvv = group_sum<LPV>(pvv);
+  pnn = group_sum<LPV>(pnn);
+  const float omega = pnn > 0.f ? pvv / pnn : 0.f;
+  float eps[VF];
+#pragma unroll
+  for (int e = 0; e < VF; ++e) eps[e] = vv[e] - omega * vb[e];
+
+  // sink: a_d = G a, a+ = a_d + beta (omega - kappa . a_d) kappa (Mamba-2: no kappa . a_d)
+  float pka = 0.f, pkq = 0.f;
+#pragma unroll
+  for (int e = 0; e < VF; ++e) {
+    av[e] *= gv[e];
+    pka += kv[e] * av[e];
+    pkq += kv[e] * qv[e];
+  }
+  const float ka = group_sum<LPU>(pka);
+  const float s = group_sum<LPU>(pkq);  // kappa . q: the new column's share of the read-out
+  const float coef = beta * (DELTA ? (omega - ka) : omega);
+  float an[VF];
+  float paq = 0.f;
+#pragma unroll
+  for (int e = 0; e < VF; ++e) {
+    an[e] = av[e] + coef * kv[e];
+    paq += an[e] * qv[e];
+  }
+  const float aq = group_sum<LPU>(paq);
+
+  // a+ and the decay state are final: write them now, so their registers are free for the V pass
+  if (ug == 0) store_f32<0, VF>(A.a + unit * DK + uo, an);
+  if constexpr (!DIAG) {
+    // slot 0: the r columns kept by the last compression; slot 1 + i: column r + i
+    if (lane <= m - r) sc[lane] = gs * own_scale;
+    else if (lane == m - r + 1) sc[lane] = 1.f;
+  }
+
+  // ---- 5. V pass: V x and V y -------------------------------------------------------------------
   float accx[VF], accy[VF];
 #pragma unroll
   for (int e = 0; e < VF; ++e) { accx[e] = 0.f; accy[e] = 0.f; }
@@ -288,7 +350,7 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
     accy[e] = across_groups_sum<LPV>(accy[e]);
   }
 
-  // ---- 7. epilogue: append the column pair, write a+, o and the decay state --------------------
+  // ---- 6. epilogue: append the V column and write o ---------------------------------------------
   if (vg == 0) {
     float w[VF], o[VF];
 #pragma unroll
@@ -298,19 +360,6 @@ __global__ __launch_bounds__(256) void k_decode(const StepArgs A) {
     }
     store_f32<FDT, VF>(Vb + static_cast<int64_t>(m) * DV + vo, w);
     store_f32<IDT, VF>(reinterpret_cast<IT*>(A.o) + unit * DV + vo, o);
-  }
-  if (ug == 0) {
-    float nu[VF];
-#pragma unroll
-    for (int e = 0; e < VF; ++e) nu[e] = DIAG ? kv[e] / Gn[e] : kv[e];
-    store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
-    store_f32<0, VF>(A.a + unit * DK + uo, an);
-    if constexpr (DIAG) store_f32<0, VF>(sc + uo, Gn);
-  }
-  if constexpr (!DIAG) {
-    // slot 0: the r columns kept by the last compression; slot 1 + i: column r + i
-    if (lane <= m - r) sc[lane] = gs * own_scale;
-    else if (lane == m - r + 1) sc[lane] = 1.f;
   }
 }
 
