@@ -49,6 +49,8 @@ __device__ __forceinline__ void load_f32(const stor_t<DT>* __restrict__ p, float
 #pragma unroll
       for (int e = 0; e < N; ++e) out[e] = p[e];
     }
+  } else if constexpr (N == 1) {
+    out[0] = bf16_to_f32(p[0]);
   } else {
     static_assert(N % 2 == 0, "bf16 vector width");
     if constexpr (N % 8 == 0) {
@@ -95,6 +97,8 @@ __device__ __forceinline__ void store_f32(stor_t<DT>* __restrict__ p, const floa
 #pragma unroll
       for (int e = 0; e < N; ++e) p[e] = in[e];
     }
+  } else if constexpr (N == 1) {
+    p[0] = f32_to_bf16(in[0]);
   } else {
     static_assert(N % 2 == 0, "bf16 vector width");
     uint32_t w[N / 2];
@@ -148,6 +152,32 @@ __device__ __forceinline__ float across_groups_sum(float v) {
   if constexpr (W <= 16) v += __shfl_xor(v, 16, 64);
   if constexpr (W <= 32) v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+// v_permlane32_swap: lanes 32..63 of x trade places with lanes 0..31 of y.
+__device__ __forceinline__ void lane_swap32(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// v_permlane16_swap: the odd 16-lane rows of x trade places with the even rows of y.
+__device__ __forceinline__ void lane_swap16(float& x, float& y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(r[0]);
+  y = __uint_as_float(r[1]);
+}
+
+// Sum over all 64 lanes; every lane gets it.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  float x = v, y = v;
+  lane_swap16(x, y);
+  v = x + y;
+  x = v;
+  y = v;
+  lane_swap32(x, y);
+  return x + y;
 }
 
 // Orders LDS traffic between lanes of one wavefront (LDS operations of a wave execute in

@@ -6,15 +6,19 @@
 // diagonal gate in place of g and Mamba-2 without the delta terms.
 //
 // Design (gfx950): one 64-lane wavefront per (request, head) unit, four units per 256-thread
-// workgroup. The step is HBM-bound: its bytes are the m columns of U and of V, read once.
-// Each lane owns a 16-byte slice of a column; a wave-wide load covers 64 / (lanes per column)
-// whole columns, so every load instruction streams a contiguous 1 KiB. All U and V loads of
-// the unit are issued before any arithmetic, which keeps up to 32 KiB per wave in flight. With
+// workgroup. The step is HBM-bound: its bytes are the m columns of U and of V, read once, with
+// non-temporal loads (no reuse within a step). Each lane owns a 16-byte slice of a column; a
+// wave-wide load covers 64 / (lanes per column) whole columns, so every load instruction
+// streams a contiguous 1 KiB. The small per-unit vectors are loaded first, then U, and V
+// either with U or, where both would not fit in 96 registers per lane, as soon as the U pass
+// has consumed U (half the registers per wave: a 4096-unit launch is resident at once). With
 // bf16 factors and inputs the U pass uses packed bf16 dot products (v_dot2_f32_bf16).
-//   U pass: per column, x_j = (G U)_j . kappa and y_j = (G U)_j . q, reduced over the lanes of
-//           the column with DPP row operations. The decay is lazy: U is never rewritten, the
-//           per-column scales (GDN, Mamba-2) or per-channel Gamma (KDA) absorb it.
-//   V pass: V x and V y accumulated per lane, then summed across column groups.
+//   U pass: per column, x_j = (G U)_j . kappa and y_j = (G U)_j . q, summed over the lanes of
+//           the column with transposed DPP exchanges (every lane ends with one column). The
+//           decay is lazy: U is never rewritten, the per-column scales (GDN, Mamba-2) or
+//           per-channel Gamma (KDA) absorb it.
+//   V pass: V x and V y accumulated per lane, then summed across column groups with
+//           transposed permlane swaps (every lane ends with a few elements of d_v).
 //   Epilogue: w = beta (eps - V x) (delta kinds) or beta eps (Mamba-2) becomes column m of V,
 //           the key becomes column m of U, and o = vbar (a+ . q) + V y + (kappa . q) w.
 #include "common.hpp"
@@ -26,6 +30,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Third word of a raw buffer resource on gfx9-family chips (32-bit data, no swizzle).
 constexpr int kRawBufferWord3 = 0x00020000;
+// Cache-policy bits of a buffer load: non-temporal (gfx950's nt bit). A step reads each factor
+// column once, and the next read of the same state comes only after the other layers' traffic.
+constexpr int kNonTemporal = 2;
 
 // NI wave-wide loads of 16 bytes per lane over consecutive KiB of a unit's factor columns, with
 // the bytes past `bytes` (the columns at and after m) reading as zeros. Each resource covers
@@ -40,7 +47,7 @@ __device__ __forceinline__ void load_columns(const void* base, int bytes, int la
         const_cast<char*>(static_cast<const char*>(base)) + g * 4096, 0, rest > 0 ? rest : 0, kRawBufferWord3);
 #pragma unroll
     for (int k = 0; k < 4 && 4 * g + k < NI; ++k) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + k * 1024, 0, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off + k * 1024, 0, kNonTemporal);
       out[4 * g + k] = make_uint4(x[0], x[1], x[2], x[3]);
     }
   }
@@ -77,6 +84,90 @@ __device__ __forceinline__ uint4 pack16(const float (&in)[VF]) {
 // KDA: a channel's cumulative gate below this is folded into the stored factors (2^-40).
 constexpr float kFoldFloor = 9.094947e-13f;
 
+// ---- transposed sums ---------------------------------------------------------------------------
+// A lane holds N partial sums, each to be summed over a group of lanes. Rather than reducing
+// every value over the whole group (N log2 W exchanges), pairs of values trade halves at each
+// bit of the lane index: the lane whose bit is clear keeps the first of the pair plus its
+// partner's copy, the other keeps the second, so the N sums take N - 1 exchanges and end up
+// spread over the lanes.
+
+// The partner at bit B of lane % 16 inside a 16-lane row: row_mirror (B = 8),
+// row_half_mirror (4), lane ^ 2, lane ^ 1. Each partner differs in bit B and agrees on the bits
+// above it, which is all the pairing needs.
+template <int B>
+__device__ __forceinline__ float row_partner(float v) {
+  if constexpr (B == 8) return dpp<0x140>(v);
+  else if constexpr (B == 4) return dpp<0x141>(v);
+  else if constexpr (B == 2) return dpp<0x4E>(v);
+  else return dpp<0xB1>(v);
+}
+
+// Sums over aligned groups of 2B lanes (B = W / 2 at the call; W <= 32): afterwards lane t of a
+// group holds in v[0] the group's total of v[t * N / W] as it was on entry (N <= W; for N < W,
+// W / N neighbouring lanes hold the same total).
+template <int NMAX, int N, int B>
+__device__ __forceinline__ void tsum_in_group(float (&v)[NMAX], int lane) {
+  if constexpr (B >= 1) {
+    constexpr int H = N / 2;
+    if constexpr (N >= 2) {
+      if constexpr (B == 16) {
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+          lane_swap16(v[k], v[k + H]);
+          v[k] += v[k + H];
+        }
+      } else {
+        const bool hi = (lane & B) != 0;
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+          const float keep = hi ? v[k + H] : v[k];
+          const float send = hi ? v[k] : v[k + H];
+          v[k] = keep + row_partner<B>(send);
+        }
+      }
+      tsum_in_group<NMAX, H, B / 2>(v, lane);
+    } else {
+      if constexpr (B == 16) {
+        float x = v[0], y = v[0];
+        lane_swap16(x, y);
+        v[0] = x + y;
+      } else {
+        v[0] += row_partner<B>(v[0]);
+      }
+      tsum_in_group<NMAX, 1, B / 2>(v, lane);
+    }
+  }
+}
+
+// Sums over the 64 / W lanes that share lane % W (bits B = 32 down to W of the lane index):
+// afterwards the lanes of group g = lane / W hold the totals of v[g * N * W / 64 ...] in
+// v[0 .. N * W / 64 - 1].
+template <int NMAX, int N, int B, int W>
+__device__ __forceinline__ void tsum_across_groups(float (&v)[NMAX], int lane) {
+  if constexpr (B >= W) {
+    static_assert(N >= 2, "fewer values than groups");
+    constexpr int H = N / 2;
+    if constexpr (B == 32 || B == 16) {
+#pragma unroll
+      for (int k = 0; k < H; ++k) {
+        if constexpr (B == 32) lane_swap32(v[k], v[k + H]);
+        else lane_swap16(v[k], v[k + H]);
+        v[k] += v[k + H];
+      }
+    } else {
+      static_assert(B == 8, "partner lane ^ 8 inside a row (row_ror 8)");
+      const bool hi = (lane & B) != 0;
+#pragma unroll
+      for (int k = 0; k < H; ++k) {
+        const float keep = hi ? v[k + H] : v[k];
+        const float send = hi ? v[k] : v[k + H];
+        v[k] = keep + dpp<0x128>(send);
+      }
+    }
+    tsum_across_groups<NMAX, H, B / 2, W>(v, lane);
+  }
+}
+
 // Lane geometry of one unit, and how its factors are staged. A lane owns a 16-byte slice of a
 // column; NIU (NIV) wave-wide loads cover MAXC columns of U (V). When both sets together would
 // hold more than 96 registers per lane, V is loaded only after the U pass has consumed U, so a
@@ -106,14 +197,15 @@ void k_decode(const StepArgs A) {
   constexpr int NIU = Geo::NIU;
   constexpr int NIV = Geo::NIV;
   constexpr bool SPLIT = Geo::SPLIT;
+  constexpr int NB = VF * LPV / kWave;  // value elements per lane once the V pass is summed
   constexpr bool DELTA = (KIND != SEED_MAMBA2);
   constexpr bool DIAG = (KIND == SEED_KDA);
   static_assert(VF * sizeof(FT) == 16, "16-byte lane slices");
-  static_assert(LPU <= kWave && LPV <= kWave, "column wider than a wave");
+  static_assert(LPU <= 32 && LPV <= 32 && NIU <= LPU && NB >= 1, "lane geometry");
+  static_assert(CPU_ * DK * sizeof(FT) == 1024 && CPV * DV * sizeof(FT) == 1024, "1 KiB per load");
 
   __shared__ float xs[4][MAXC];
   __shared__ float ys[4][MAXC];
-  __shared__ float cscl[4][MAXC];  // per-column decay scale (GDN, Mamba-2)
 
   const int lane = threadIdx.x & (kWave - 1);
   // the wave index is uniform: keep it (and every per-unit address) in scalar registers
@@ -125,27 +217,17 @@ void k_decode(const StepArgs A) {
 
   const int ug = lane / LPU, uo = (lane % LPU) * VF;  // U column group and d_k offset
   const int vg = lane / LPV, vo = (lane % LPV) * VF;  // V column group and d_v offset
+  // the column whose x and y this lane holds after the U pass's transposed sums
+  const int jt = ((lane % LPU) * NIU / LPU) * CPU_ + ug;
+  // the value elements this lane finishes: NB of them from d_v index ve
+  const int ve = vo + vg * NB;
 
   FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(C) * DK;
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
 
-  // ---- 1. stream the factors ------------------------------------------------------------------
-  // Buffer loads whose range ends at column m: a lane whose column is past the live ones reads
-  // zeros (the range check covers the lane offset and the immediate, so the column offset is
-  // kept there), and no load waits on another. Columns m..slots-1 may hold anything, even NaN.
-  static_assert(CPU_ * DK * sizeof(FT) == 1024 && CPV * DV * sizeof(FT) == 1024, "1 KiB per load");
-  const int uoff = (ug * DK + uo) * static_cast<int>(sizeof(FT));
-  const int voff = (vg * DV + vo) * static_cast<int>(sizeof(FT));
-  uint4 ur[NIU];
-  uint4 vr[NIV];
-  auto load_v = [&]() { load_columns<NIV>(Vb, m * DV * static_cast<int>(sizeof(FT)), voff, vr); };
-  load_columns<NIU>(Ub, m * DK * static_cast<int>(sizeof(FT)), uoff, ur);
-  if constexpr (!SPLIT) load_v();
-  // keep the factor loads ahead of the first wait (the scheduler would otherwise sink them
-  // below the U pass to save registers, serialising the latencies)
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 2. key-side vectors (U layout) and the lazy decay state ----------------------------------
+  // ---- 1. key-side vectors (U layout) and the lazy decay state -------------------------------
+  // These small loads go ahead of the factors: loads complete in order, so the values that need
+  // only them (the new U column, the column scales) do not wait for the factors.
   // bf16 factors with bf16 inputs (no channel gate): the U pass takes packed bf16 dot products
   constexpr bool DOT2 = (FDT == 1) && (IDT == 1) && !DIAG;
   const IT* __restrict__ qp = reinterpret_cast<const IT*>(A.q) + unit * DK + uo;
@@ -161,18 +243,38 @@ void k_decode(const StepArgs A) {
   }
   const float beta = A.beta[unit];
   const float gs = DIAG ? 0.f : A.g[unit];
-
   float* __restrict__ sc = A.scale + unit * A.scale_len;
-  float Gn[VF];
-  float own_scale = 0.f;
+  float own_scale = 0.f, col_scale = 1.f, Gm[VF], alpha[VF];
   if constexpr (DIAG) {
-    float Gm[VF], gv[VF];
-    load_f32<0, VF>(A.g + unit * DK + uo, gv);
+    load_f32<0, VF>(A.g + unit * DK + uo, alpha);
     load_f32<0, VF>(sc + uo, Gm);
+  } else {
+    // slot 0 scales the r columns kept by the last compression, slot 1 + i column r + i; a
+    // column past the live ones gets a finite stand-in (its loads read zeros)
+    own_scale = sc[min(lane, m - r)];
+    col_scale = sc[jt < r ? 0 : min(1 + jt - r, m - r)];
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. stream the factors --------------------------------------------------------------------
+  const int uoff = (ug * DK + uo) * static_cast<int>(sizeof(FT));
+  const int voff = (vg * DV + vo) * static_cast<int>(sizeof(FT));
+  uint4 ur[NIU];
+  uint4 vr[NIV];
+  auto load_v = [&]() { load_columns<NIV>(Vb, m * DV * static_cast<int>(sizeof(FT)), voff, vr); };
+  load_columns<NIU>(Ub, m * DK * static_cast<int>(sizeof(FT)), uoff, ur);
+  if constexpr (!SPLIT) load_v();
+  // keep the factor loads ahead of the first wait (the scheduler would otherwise sink them
+  // below the U pass to save registers, serialising the latencies)
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (DIAG) {
+    float Gn[VF];
     bool tiny = false;
 #pragma unroll
     for (int e = 0; e < VF; ++e) {
-      Gn[e] = gv[e] * Gm[e];  // Gamma <- alpha . Gamma
+      Gn[e] = alpha[e] * Gm[e];  // Gamma <- alpha . Gamma
       tiny |= !(Gn[e] >= kFoldFloor);
     }
     if (__ballot(tiny) != 0) {
@@ -224,15 +326,11 @@ void k_decode(const StepArgs A) {
       }
       store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
     }
-    // one load per lane: lane l holds slot min(l, m - r); column l's scale comes from its slot
-    // (columns past the live ones get a finite stand-in: their loads read zeros)
-    own_scale = sc[min(lane, m - r)];
-    const float cl = gs * __shfl(own_scale, lane < r ? 0 : min(1 + lane - r, m - r));
-    if (lane < MAXC) cscl[wv][lane] = cl;
-    wave_lds_sync();
+    col_scale *= gs;
   }
 
   // ---- 3. U pass: x = (G U)^T kappa, y = (G U)^T q ----------------------------------------------
+  float px[NIU], py[NIU];
 #pragma unroll
   for (int i = 0; i < NIU; ++i) {
     float pk = 0.f, pq = 0.f;
@@ -255,22 +353,22 @@ void k_decode(const StepArgs A) {
         pq += u[e] * qt[e];
       }
     }
-    if constexpr (DELTA) pk = group_sum<LPU>(pk);
-    pq = group_sum<LPU>(pq);
-    const int j = i * CPU_ + ug;
-    // every column slot is written (zero past the live columns), so the V pass needs no mask
-    if ((lane % LPU) == 0) {
-      const float c = DIAG ? 1.f : cscl[wv][j];
-      xs[wv][j] = c * pk;
-      ys[wv][j] = c * pq;
-    }
+    px[i] = pk;
+    py[i] = pq;
   }
+  // column sums over the LPU lanes of each column, transposed: this lane ends with column jt
+  if constexpr (DELTA) tsum_in_group<NIU, NIU, LPU / 2>(px, lane);
+  tsum_in_group<NIU, NIU, LPU / 2>(py, lane);
+  // every column slot is written (zero past the live columns), so the V pass needs no mask;
+  // lanes that share a column write the same value
+  if constexpr (DELTA) xs[wv][jt] = col_scale * px[0];
+  ys[wv][jt] = col_scale * py[0];
 
   // ---- 4. the per-unit vectors of the update, then V when it was not loaded up front ----------
   // q, kappa and the gate are read again (cache hits) rather than held through the U pass. The
   // small loads go first: loads complete in order, so the sink below waits only for them.
   if constexpr (SPLIT) __builtin_amdgcn_sched_barrier(0);
-  float qv[VF], kv[VF], gv[VF], av[VF], vv[VF], vb[VF];
+  float qv[VF], kv[VF], gv[VF], av[VF], vv[NB], vb[NB];
   load_f32<IDT, VF>(qp, qv);
   load_f32<IDT, VF>(kp, kv);
   if constexpr (DIAG) {
@@ -280,24 +378,21 @@ void k_decode(const StepArgs A) {
     for (int e = 0; e < VF; ++e) gv[e] = gs;
   }
   load_f32<0, VF>(A.a + unit * DK + uo, av);
-  load_f32<IDT, VF>(reinterpret_cast<const IT*>(A.v) + unit * DV + vo, vv);
-  load_f32<0, VF>(A.vbar + static_cast<int64_t>(head) * DV + vo, vb);
+  load_f32<IDT, NB>(reinterpret_cast<const IT*>(A.v) + unit * DV + ve, vv);
+  load_f32<0, NB>(A.vbar + static_cast<int64_t>(head) * DV + ve, vb);
   if constexpr (SPLIT) {
     load_v();
     __builtin_amdgcn_sched_barrier(0);
   }
   wave_lds_sync();
 
-  // value split along vbar (omega, eps)
+  // value split along vbar (omega, eps): every lane holds NB distinct elements of v
   float pvv = 0.f, pnn = 0.f;
 #pragma unroll
-  for (int e = 0; e < VF; ++e) { pvv += vv[e] * vb[e]; pnn += vb[e] * vb[e]; }
-  pvv = group_sum<LPV>(pvv);
-  pnn = group_sum<LPV>(pnn);
+  for (int e = 0; e < NB; ++e) { pvv += vv[e] * vb[e]; pnn += vb[e] * vb[e]; }
+  pvv = wave_sum(pvv);
+  pnn = wave_sum(pnn);
   const float omega = pnn > 0.f ? pvv / pnn : 0.f;
-  float eps[VF];
-#pragma unroll
-  for (int e = 0; e < VF; ++e) eps[e] = vv[e] - omega * vb[e];
 
   // sink: a_d = G a, a+ = a_d + beta (omega - kappa . a_d) kappa (Mamba-2: no kappa . a_d)
   float pka = 0.f, pkq = 0.f;
@@ -322,7 +417,6 @@ void k_decode(const StepArgs A) {
   // a+ and the decay state are final: write them now, so their registers are free for the V pass
   if (ug == 0) store_f32<0, VF>(A.a + unit * DK + uo, an);
   if constexpr (!DIAG) {
-    // slot 0: the r columns kept by the last compression; slot 1 + i: column r + i
     if (lane <= m - r) sc[lane] = gs * own_scale;
     else if (lane == m - r + 1) sc[lane] = 1.f;
   }
@@ -344,23 +438,20 @@ void k_decode(const StepArgs A) {
       accy[e] += yj * vc[e];
     }
   }
-#pragma unroll
-  for (int e = 0; e < VF; ++e) {
-    if constexpr (DELTA) accx[e] = across_groups_sum<LPV>(accx[e]);
-    accy[e] = across_groups_sum<LPV>(accy[e]);
-  }
+  // sums over the column groups, transposed: this lane ends with elements ve .. ve + NB - 1
+  if constexpr (DELTA) tsum_across_groups<VF, VF, 32, LPV>(accx, lane);
+  tsum_across_groups<VF, VF, 32, LPV>(accy, lane);
 
-  // ---- 6. epilogue: append the V column and write o ---------------------------------------------
-  if (vg == 0) {
-    float w[VF], o[VF];
+  // ---- 6. epilogue: append the V column and write o (every lane: NB elements) -----------------
+  float w[NB], o[NB];
 #pragma unroll
-    for (int e = 0; e < VF; ++e) {
-      w[e] = beta * (DELTA ? (eps[e] - accx[e]) : eps[e]);
-      o[e] = vb[e] * aq + accy[e] + s * w[e];
-    }
-    store_f32<FDT, VF>(Vb + static_cast<int64_t>(m) * DV + vo, w);
-    store_f32<IDT, VF>(reinterpret_cast<IT*>(A.o) + unit * DV + vo, o);
+  for (int e = 0; e < NB; ++e) {
+    const float eps = vv[e] - omega * vb[e];
+    w[e] = beta * (DELTA ? (eps - accx[e]) : eps);
+    o[e] = vb[e] * aq + accy[e] + s * w[e];
   }
+  store_f32<FDT, NB>(Vb + static_cast<int64_t>(m) * DV + ve, w);
+  store_f32<IDT, NB>(reinterpret_cast<IT*>(A.o) + unit * DV + ve, o);
 }
 
 // ---- host-side dispatch ----------------------------------------------------------------------
