@@ -41,9 +41,11 @@ namespace seed {
 
 namespace cw {
 
-constexpr int N = 64;           // padded column count
+// N is the padded column count of the core, 64 or 32 (r + T <= 32). With N = 32, lanes c and
+// c + 32 hold the same row c, so that the MFMA tiles and the lane-pair phases keep their
+// 64-lane form; sums over rows then stop at 32 lanes.
 constexpr int RX = 32;          // maximum rank on this path
-constexpr int LDL = N + 1;      // LDS row stride of L (odd: row and column reads both conflict-free)
+constexpr int kGrid = 128;      // points of the shared Sturm grid (two per lane)
 constexpr int NSEC = 7;         // 5-section steps after the 128-point grid (129 * 5^7 ~ 1e7)
 constexpr float kPivTol = 1e-7f;
 constexpr float kReduceFloor = 1e-30f;  // squared column norm below which no reflector is built
@@ -96,6 +98,22 @@ __device__ __forceinline__ float wsum(float v) {
   float x = v, y = v;
   swap32(x, y);
   return x + y;
+}
+
+// Sum over each 32-lane half (both halves get their own).
+__device__ __forceinline__ float hsum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return swap16_sum(v);
+}
+
+// Sum over the rows of an N-wide core: all 64 lanes, or one copy of the 32 rows.
+template <int N>
+__device__ __forceinline__ float rsum(float v) {
+  if constexpr (N == 64) return wsum(v);
+  else return hsum(v);
 }
 
 __device__ __forceinline__ float wmax(float v) {
@@ -155,9 +173,22 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Accumulator tiles t[I][J] of a 64 x 64 product P -> lane L, register rho = P[rho][L].
+// Accumulator tiles t[I][J] of an N x N product P -> lane L, register rho = P[rho][L] (N = 32:
+// P[rho][L % 32] on both lanes of a pair).
+template <int N>
 __device__ __forceinline__ M64 tiles_to_rows(const f32x16 (&t)[2][2]) {
   f32x32 R_lo, R_hi;
+  if constexpr (N == 32) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float x = t[0][0][j], y = t[0][0][j];
+      swap32(x, y);
+      const int rho = 8 * (j >> 2) + (j & 3);
+      R_lo[rho] = x;
+      R_lo[rho + 4] = y;
+    }
+    return M64{R_lo, R_lo};
+  }
 #pragma unroll
   for (int I = 0; I < 2; ++I) {
 #pragma unroll
@@ -173,8 +204,13 @@ __device__ __forceinline__ M64 tiles_to_rows(const f32x16 (&t)[2][2]) {
 }
 
 // MFMA 32x32x2 operands of K-step s (k = 2s + lane / 32) from a row-per-lane matrix X: .x
-// serves row (or column) block 0, .y block 1; as A they give X, as B they give X^T.
+// serves row (or column) block 0, .y block 1; as A they give X, as B they give X^T. With
+// N = 32 each lane already holds its row: .x is element k of it.
+template <int N>
 __device__ __forceinline__ float2 rows_operand(const f32x32 X_lo, const f32x32 X_hi, int s) {
+  if constexpr (N == 32) {
+    return make_float2((threadIdx.x & 32) ? X_lo[(2 * s + 1) & 31] : X_lo[(2 * s) & 31], 0.f);
+  }
   float x = MGET(X, 2 * s), y = MGET(X, 2 * s + 1);
   swap32(x, y);
   return make_float2(x, y);
@@ -182,7 +218,8 @@ __device__ __forceinline__ float2 rows_operand(const f32x32 X_lo, const f32x32 X
 
 // One 32-row accumulator tile (rows 32 I + 8 q + 4 h + t, column lane % 32) -> MFMA 32x32x2 B
 // operands: out[16 I + 4 q + {0, 2, 1, 3}] hold rows 2 s + h of that column.
-__device__ __forceinline__ void tile_to_kops(const f32x16& acc, int I, float (&out)[32]) {
+template <int NO>
+__device__ __forceinline__ void tile_to_kops(const f32x16& acc, int I, float (&out)[NO]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float x0 = acc[4 * q + 0], y0 = acc[4 * q + 1];
@@ -200,8 +237,9 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+template <int N>
 struct Smem {
-  alignas(16) float Lp[N * LDL];
+  alignas(16) float Lp[N * (N + 1)];  // row stride N + 1 (odd: row and column reads both conflict-free)
   alignas(16) float bvw[2 * N];    // broadcast vectors (v, w); the second vector of a pair
   alignas(16) float y2[2 * N];     // Gram-Schmidt / back-transformation: one vector, even then odd entries
   alignas(16) float dg[N];
@@ -216,18 +254,19 @@ struct Smem {
 
 // Gram of the stored columns 0..m-1 (rows of length D, bf16), as row-per-lane registers. With
 // ROWSCALE the A operand carries gam^2 along d (KDA's per-channel lazy decay).
-template <int D, bool ROWSCALE>
+template <int D, bool ROWSCALE, int N>
 __device__ __forceinline__ M64 gram(const uint16_t* __restrict__ base, const int m, const float* __restrict__ gam) {
   const int lane = threadIdx.x;
   const int c0 = lane & 31, kh = lane >> 5;
-  const bool ok0 = c0 < m, ok1 = c0 + 32 < m;
+  const bool ok0 = c0 < m, ok1 = N == 64 && c0 + 32 < m;
   const uint16_t* p0 = base + (ok0 ? c0 : 0) * D + 8 * kh;
   const uint16_t* p1 = base + (ok1 ? c0 + 32 : 0) * D + 8 * kh;
   f32x16 t[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
 #pragma unroll
   for (int k0 = 0; k0 < D; k0 += 16) {
     uint4 u0 = *reinterpret_cast<const uint4*>(p0 + k0);
-    uint4 u1 = *reinterpret_cast<const uint4*>(p1 + k0);
+    uint4 u1 = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (N == 64) u1 = *reinterpret_cast<const uint4*>(p1 + k0);
     if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
     if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
     const bf16x8 b0 = __builtin_bit_cast(bf16x8, u0);
@@ -242,30 +281,36 @@ __device__ __forceinline__ M64 gram(const uint16_t* __restrict__ base, const int
       }
     }
     t[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, t[0][0], 0, 0, 0);
-    t[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, t[0][1], 0, 0, 0);
-    t[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, t[1][0], 0, 0, 0);
-    t[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, t[1][1], 0, 0, 0);
+    if constexpr (N == 64) {
+      t[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, t[0][1], 0, 0, 0);
+      t[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, t[1][0], 0, 0, 0);
+      t[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, t[1][1], 0, 0, 0);
+    }
   }
-  return tiles_to_rows(t);
+  return tiles_to_rows<N>(t);
 }
 
 // P = X * Lp (X row-per-lane in registers, Lp in LDS) -> P^T row-per-lane.
+template <int N>
 __device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, const float* __restrict__ Lp) {
+  constexpr int LDL = N + 1;
   const int lane = threadIdx.x;
   const int c = lane & 31, kh = lane >> 5;
   f32x16 t[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
 #pragma unroll
   for (int s = 0; s < N / 2; ++s) {
-    const float2 a = rows_operand(X_lo, X_hi, s);
+    const float2 a = rows_operand<N>(X_lo, X_hi, s);
     const float a0 = a.x, a1 = a.y;
     const float b0 = Lp[(2 * s + kh) * LDL + c];
-    const float b1 = Lp[(2 * s + kh) * LDL + 32 + c];
     t[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, t[0][0], 0, 0, 0);
-    t[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, t[0][1], 0, 0, 0);
-    t[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, t[1][0], 0, 0, 0);
-    t[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, t[1][1], 0, 0, 0);
+    if constexpr (N == 64) {
+      const float b1 = Lp[(2 * s + kh) * LDL + 32 + c];
+      t[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, t[0][1], 0, 0, 0);
+      t[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, t[1][0], 0, 0, 0);
+      t[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, t[1][1], 0, 0, 0);
+    }
   }
-  return tiles_to_rows(t);
+  return tiles_to_rows<N>(t);
 }
 
 // Y = F X for F (D x 64: the stored bf16 columns 0..m-1 of a factor) and X given as MFMA
@@ -273,8 +318,8 @@ __device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, con
 // of tile I is d = NT i + I, so that one lane's A operands of a column are NT consecutive
 // elements (one load per K-step). Output: y[I][j] is Y[d][lane % 32] with
 // d = NT (8 (j / 4) + 4 (lane / 32) + j % 4) + I.
-template <int D>
-__device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, const int m, const float (&xop)[32],
+template <int D, int N>
+__device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, const int m, const float (&xop)[N / 2],
                                              f32x16 (&y)[D / 32]) {
   constexpr int NT = D / 32;
   static_assert(NT == 2 || NT == 4, "d of 64 or 128");
@@ -310,6 +355,7 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
 // (two independent recurrences interleaved). e2 is floored at FLT_MIN, so a zero pivot gives an
 // infinite next pivot of the opposite sign (IEEE arithmetic) instead of NaN; pivots are counted
 // by their sign bit, so that +0 followed by -inf and -0 followed by +inf count once each.
+template <int N>
 __device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float* __restrict__ e2, const float x1,
                                        const float x2, int& c1, int& c2) {
   float q1 = dg[0] - x1, q2 = dg[0] - x2;
@@ -328,12 +374,15 @@ __device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float
 
 }  // namespace cw
 
-template <int DK, int DV, bool DIAG>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_compress_wave(const CompressArgs A) {
+template <int DK, int DV, bool DIAG, int N>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 : 3))) void k_compress_wave(const CompressArgs A) {
   using namespace cw;
-  __shared__ Smem S;
+  static_assert(N == 64 || N == 32, "core width");
+  constexpr int LDL = N + 1;  // LDS row stride of L
+  __shared__ Smem<N> S;
   const int lane = threadIdx.x;
   const int h = lane >> 5, c32 = lane & 31;
+  const int row = N == 64 ? lane : c32;  // the core row this lane holds
   const int64_t unit = blockIdx.x;
   const int m = A.m, r = A.rank, C = A.slots;
   uint16_t* __restrict__ Ub = reinterpret_cast<uint16_t*>(A.U) + unit * static_cast<int64_t>(C) * DK;
@@ -344,18 +393,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   float csc;
   if constexpr (DIAG) {
     for (int i = lane; i < DK; i += 64) S.gam[i] = sc[i];
-    csc = lane < m ? 1.f : 0.f;
+    csc = row < m ? 1.f : 0.f;
   } else {
-    csc = lane < m ? sc[lane < r ? 0 : 1 + lane - r] : 0.f;
+    csc = row < m ? sc[row < r ? 0 : 1 + row - r] : 0.f;
   }
-  S.colsc[lane] = csc;
+  S.colsc[row] = csc;
   wave_lds_sync();
 
   // ---- Grams of the stored columns -------------------------------------------------------------
   f32x32 GU_lo, GU_hi, GV_lo, GV_hi;
   {
-    const M64 gu = gram<DK, DIAG>(Ub, m, S.gam);
-    const M64 gv = gram<DV, false>(Vb, m, nullptr);
+    const M64 gu = gram<DK, DIAG, N>(Ub, m, S.gam);
+    const M64 gv = gram<DV, false, N>(Vb, m, nullptr);
     GU_lo = gu.lo; GU_hi = gu.hi; GV_lo = gv.lo; GV_hi = gv.hi;
   }
 
@@ -363,7 +412,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   float du = 0.f, dv = 0.f;
 #pragma unroll
   for (int c = 0; c < N; ++c) {
-    if (lane == c) { du = MGET(GU, c); dv = MGET(GV, c); }
+    if (row == c) { du = MGET(GU, c); dv = MGET(GV, c); }
   }
   float bal = 0.f, ibal = 0.f;
   if (du > 0.f && dv > 0.f && csc > 0.f) {
@@ -371,8 +420,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     bal = sq * qv / qu;
     ibal = sq * qu / qv;
   }
-  S.bal[lane] = bal;
-  S.ibal[lane] = ibal;
+  S.bal[row] = bal;
+  S.ibal[row] = ibal;
   wave_lds_sync();
 #pragma unroll
   for (int c4 = 0; c4 < N / 4; ++c4) {
@@ -397,8 +446,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const float tol = uni(kPivTol * wmax(d));
     float lprev = 0.f;
     for (int s = 0; s < N; ++s) {
-      const bool was = (chosen >> lane) & 1ull;
-      const int key = (!was && d > 0.f) ? __float_as_int(d) : -1;   // d is finite
+      const bool was = (chosen >> row) & 1ull;
+      // d is finite; with N = 32 the pivot is taken among lanes 0..31 (lanes 32.. hold copies)
+      const int key = (!was && d > 0.f && (N == 64 || lane < 32)) ? __float_as_int(d) : -1;
       const int kmax = __builtin_amdgcn_readfirstlane(wmax_key(key));
       const float vmax = __int_as_float(kmax);
       if (kmax < 0 || !(vmax > tol) || !(tol > 0.f)) break;  // uniform
@@ -408,9 +458,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const float piv = vmax * rp;
       const float col = MGET(GU, p) - lprev * bcast(lprev, p);
       float l = was ? 0.f : col * rp;
-      if (lane == p) l = piv;
-      S.bvw[N * (s & 1) + lane] = l;
-      S.Lp[lane * LDL + p] = l;
+      if (row == p) l = piv;
+      S.bvw[N * (s & 1) + row] = l;
+      S.Lp[row * LDL + p] = l;
       if (s > 0) {  // uniform: the deferred update of step s - 1
         const float* prv = S.bvw + N * ((s - 1) & 1);
 #pragma unroll
@@ -434,15 +484,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   // columns never chosen (Schur residue below the tolerance) are zero in L
 #pragma unroll
   for (int c = 0; c < N; ++c) {
-    if (!((chosen >> c) & 1ull)) S.Lp[lane * LDL + c] = 0.f;
+    if (!((chosen >> c) & 1ull)) S.Lp[row * LDL + c] = 0.f;
   }
   wave_lds_sync();
 
   // ---- core B = L^T G_V L (in pivot-column order) ------------------------------------------------
   f32x32 Bm_lo, Bm_hi;
   {
-    const M64 rt = times_L(GV_lo, GV_hi, S.Lp);   // (G_V L)^T = L^T G_V, row per lane
-    const M64 bt = times_L(rt.lo, rt.hi, S.Lp);   // (L^T G_V L)^T, symmetric up to rounding
+    const M64 rt = times_L<N>(GV_lo, GV_hi, S.Lp);   // (G_V L)^T = L^T G_V, row per lane
+    const M64 bt = times_L<N>(rt.lo, rt.hi, S.Lp);   // (L^T G_V L)^T, symmetric up to rounding
     Bm_lo = bt.lo; Bm_hi = bt.hi;
   }
   // The eigen phase works on B / bs (bs = largest |entry|): entries of order one keep every
@@ -460,16 +510,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   }
 
   // ---- Householder tridiagonalisation, the reflectors kept in the registers they zero ---------
-  // From step 16 qt on, v and w vanish on lanes (and registers) below 16 qt, so quarter qt of
+  // From step 16 qt on, v and w vanish on rows (and registers) below 16 qt, so block qt of
   // the steps works on registers 16 qt.. only.
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < N / 16; ++qt) {
     const int c0 = 4 * qt;                       // first float4 block of registers touched
-    for (int j = 16 * qt; j < (qt == 3 ? N - 2 : 16 * qt + 16); ++j) {
+    for (int j = 16 * qt; j < (qt == N / 16 - 1 ? N - 2 : 16 * qt + 16); ++j) {
       const float colj = MGET(Bm, j);
-      const bool tr = lane > j;
+      const bool tr = row > j;
       const float x = tr ? colj : 0.f;
-      const float sig = uni(wsum(x * x));
+      const float sig = uni(rsum<N>(x * x));
       const float x0 = bcast(x, j + 1);
       const float djj = bcast(colj, j);
       float t = 0.f, ej = x0, v = x;
@@ -479,12 +529,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         const float v0 = x0 - al;
         t = 2.f * __builtin_amdgcn_rcpf(sig - x0 * x0 + v0 * v0);
         ej = al;
-        v = (lane == j + 1) ? v0 : x;
+        v = (row == j + 1) ? v0 : x;
       }
       MSET(Bm, j, v);
       if (lane == 0) { S.dg[j] = djj; S.e[j] = ej; S.tau[j] = t; }
       if (t == 0.f) continue;  // uniform
-      S.bvw[lane] = v;
+      S.bvw[row] = v;
       wave_lds_sync();
       float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -497,9 +547,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       }
       float p = (p4[0] + p4[1]) + (p4[2] + p4[3]);
       p = tr ? p * t : 0.f;
-      const float K = 0.5f * t * uni(wsum(p * v));
+      const float K = 0.5f * t * uni(rsum<N>(p * v));
       const float w = tr ? p - K * v : 0.f;
-      (S.bvw + N)[lane] = w;
+      (S.bvw + N)[row] = w;
       wave_lds_sync();
 #pragma unroll
       for (int c4 = c0; c4 < N / 4; ++c4) {
@@ -534,8 +584,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const int rr = r < k ? r : k;
   float lam;
   {
-    const float di = S.dg[lane], ei = S.e[lane], em = lane > 0 ? S.e[lane - 1] : 0.f;
-    S.e2[lane] = fmaxf(ei * ei, FLT_MIN);
+    const float di = S.dg[row], ei = S.e[row], em = row > 0 ? S.e[row - 1] : 0.f;
+    S.e2[row] = fmaxf(ei * ei, FLT_MIN);
     float lo = wmin(di - fabsf(em) - fabsf(ei));
     float hi = wmax(di + fabsf(em) + fabsf(ei));
     const float pad = 1e-6f * fmaxf(fabsf(lo), fabsf(hi)) + FLT_MIN;
@@ -550,13 +600,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const float x1 = lo + static_cast<float>(2 * lane + 1) * step;
       const float x2 = lo + static_cast<float>(2 * lane + 2) * step;
       int n1, n2;
-      sturm2(S.dg, S.e2, x1, x2, n1, n2);
+      sturm2<N>(S.dg, S.e2, x1, x2, n1, n2);
       float nlo = lo, nhi = hi;
       for (int g = 0; g < rr; ++g) {
         const int t = N - 1 - g;
         const int cnt = __builtin_popcountll(__ballot(n1 <= t)) + __builtin_popcountll(__ballot(n2 <= t));
         const float glo = cnt > 0 ? lo + static_cast<float>(cnt) * step : lo;
-        const float ghi = cnt < 2 * N ? lo + static_cast<float>(cnt + 1) * step : hi;
+        const float ghi = cnt < kGrid ? lo + static_cast<float>(cnt + 1) * step : hi;
         if (c32 == g) { nlo = glo; nhi = ghi; }
       }
       lo = nlo;
@@ -568,7 +618,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const float x1 = lo + static_cast<float>(2 * h + 1) * step;
       const float x2 = lo + static_cast<float>(2 * h + 2) * step;
       int n1, n2;
-      sturm2(S.dg, S.e2, x1, x2, n1, n2);
+      sturm2<N>(S.dg, S.e2, x1, x2, n1, n2);
       const float clo = fmaxf(n1 <= target ? x1 : -FLT_MAX, n2 <= target ? x2 : -FLT_MAX);
       const float chi = fminf(n1 > target ? x1 : FLT_MAX, n2 > target ? x2 : FLT_MAX);
       lo = fmaxf(lo, fmaxf(clo, partner(clo)));
@@ -582,7 +632,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   // register array serves both sweeps: slot i holds e_i / D-_{i+1} (bottom-up pivots) for
   // i >= kb and e_i / D+_i (top-down pivots, recomputed once the twist kb is known) for i < kb;
   // each z then overwrites the slot its own step consumed.
-  float Y[32];
+  float Y[N / 2];
   {
     float rt[N];
     float dm = S.dg[N - 1] - lam;
@@ -627,7 +677,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     // z_j = rt[j] (j < kb), 1 (j = kb), rt[j - 1] (j > kb)
     float nn0 = 0.f, nn1 = 0.f;
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
+    for (int s = 0; s < N / 2; ++s) {
       const int je = 2 * s, jo = 2 * s + 1;
       const float ze = je < kb ? rt[je] : (je == kb ? 1.f : rt[je > 0 ? je - 1 : 0]);
       const float zo = jo < kb ? rt[jo] : (jo == kb ? 1.f : rt[jo - 1]);
@@ -639,7 +689,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const bool ok = nn > 0.f && nn < FLT_MAX;
     const float inv = ok ? 1.f / sqrtf(nn) : 0.f;
 #pragma unroll
-    for (int s = 0; s < 32; ++s) Y[s] = ok ? Y[s] * inv : ((2 * s + h) == kb ? 1.f : 0.f);
+    for (int s = 0; s < N / 2; ++s) Y[s] = ok ? Y[s] * inv : ((2 * s + h) == kb ? 1.f : 0.f);
   }
 
   // ---- modified Gram-Schmidt across the rr vectors, two at a time (norms applied at the end) ---
@@ -652,19 +702,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     const bool pair = c + 1 < rr;  // uniform
     float n4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) n4[s & 3] += Y[s] * Y[s];
+    for (int s = 0; s < N / 2; ++s) n4[s & 3] += Y[s] * Y[s];
     float nn = (n4[0] + n4[1]) + (n4[2] + n4[3]);
     nn += partner(nn);
     if (c32 == c || c32 == c + 1) {
       float* buf = (c32 == c ? S.y2 : S.bvw) + N * h;
 #pragma unroll
-      for (int s4 = 0; s4 < 8; ++s4)
+      for (int s4 = 0; s4 < N / 8; ++s4)
         reinterpret_cast<float4*>(buf)[s4] = make_float4(Y[4 * s4], Y[4 * s4 + 1], Y[4 * s4 + 2], Y[4 * s4 + 3]);
     }
     wave_lds_sync();
-    float ya[32], yb[32];
+    float ya[N / 2], yb[N / 2];
 #pragma unroll
-    for (int s4 = 0; s4 < 8; ++s4) {
+    for (int s4 = 0; s4 < N / 8; ++s4) {
       const float4 a4 = reinterpret_cast<const float4*>(S.y2 + N * h)[s4];
       const float4 b4 = reinterpret_cast<const float4*>(S.bvw + N * h)[s4];
       ya[4 * s4] = a4.x; ya[4 * s4 + 1] = a4.y; ya[4 * s4 + 2] = a4.z; ya[4 * s4 + 3] = a4.w;
@@ -672,7 +722,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
     float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
+    for (int s = 0; s < N / 2; ++s) {
       p4[s & 3] += Y[s] * ya[s];
       q4[s & 3] += Y[s] * yb[s];
     }
@@ -695,20 +745,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       f1 = mu;
     }
 #pragma unroll
-    for (int s = 0; s < 32; ++s) Y[s] = fmaf(-f2, yb[s], fmaf(-f1, ya[s], Y[s]));
+    for (int s = 0; s < N / 2; ++s) Y[s] = fmaf(-f2, yb[s], fmaf(-f1, ya[s], Y[s]));
     if (c32 == c) ys = a > 0.f ? 1.f / sqrtf(a) : 0.f;
     if (pair && c32 == c + 1) ys = nu2 > 0.f ? 1.f / sqrtf(nu2) : 0.f;
     wave_lds_sync();
   }
 #pragma unroll
-  for (int s = 0; s < 32; ++s) Y[s] = c32 < rr ? Y[s] * ys : 0.f;
+  for (int s = 0; s < N / 2; ++s) Y[s] = c32 < rr ? Y[s] * ys : 0.f;
 
   // ---- back-transformation Y <- H_0 H_1 ... H_{N-3} Y, two reflectors at a time --------------
   // H_{j-1} H_j Y = Y - t_j v_j g1 - t_{j-1} v_{j-1} (g0 - t_j kappa g1) with g1 = v_j^T Y,
   // g0 = v_{j-1}^T Y and kappa = v_{j-1}^T v_j. Vectors go through LDS with entry i at
   // (i % 2) 32 + i / 2, so that each lane half reads its parity as 8 float4.
   {
-    const int pos = (lane & 1) * 32 + (lane >> 1);
+    const int pos = (row & 1) * (N / 2) + (row >> 1);
     for (int j = N - 3; j >= 0; j -= 2) {
       const bool two = j >= 1;  // uniform
       const float t1 = S.tau[j];
@@ -716,21 +766,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       if (t1 == 0.f && t0 == 0.f) continue;  // uniform
       const float v1 = MGET(Bm, j);
       const float v0 = two ? MGET(Bm, j - 1) : 0.f;
-      const float kap = uni(wsum(v0 * v1));
+      const float kap = uni(rsum<N>(v0 * v1));
       S.y2[pos] = v1;
       S.bvw[pos] = v0;
       wave_lds_sync();
-      float a1[32], a0[32];
+      float a1[N / 2], a0[N / 2];
 #pragma unroll
-      for (int s4 = 0; s4 < 8; ++s4) {
-        const float4 x4 = reinterpret_cast<const float4*>(S.y2 + 32 * h)[s4];
-        const float4 z4 = reinterpret_cast<const float4*>(S.bvw + 32 * h)[s4];
+      for (int s4 = 0; s4 < N / 8; ++s4) {
+        const float4 x4 = reinterpret_cast<const float4*>(S.y2 + (N / 2) * h)[s4];
+        const float4 z4 = reinterpret_cast<const float4*>(S.bvw + (N / 2) * h)[s4];
         a1[4 * s4] = x4.x; a1[4 * s4 + 1] = x4.y; a1[4 * s4 + 2] = x4.z; a1[4 * s4 + 3] = x4.w;
         a0[4 * s4] = z4.x; a0[4 * s4 + 1] = z4.y; a0[4 * s4 + 2] = z4.z; a0[4 * s4 + 3] = z4.w;
       }
       float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 32; ++s) {
+      for (int s = 0; s < N / 2; ++s) {
         p4[s & 3] += a1[s] * Y[s];
         q4[s & 3] += a0[s] * Y[s];
       }
@@ -741,7 +791,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const float f1 = t1 * g1;
       const float f0 = t0 * (g0 - kap * f1);
 #pragma unroll
-      for (int s = 0; s < 32; ++s) Y[s] = fmaf(-f0, a0[s], fmaf(-f1, a1[s], Y[s]));
+      for (int s = 0; s < N / 2; ++s) Y[s] = fmaf(-f0, a0[s], fmaf(-f1, a1[s], Y[s]));
       wave_lds_sync();
     }
   }
@@ -754,18 +804,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const float qu = live ? 1.f / (q4 * q4) : 0.f;   // lambda^(-1/2)
 
   // ---- X_V = diag(ibal) L Y lambda^(-1/4) (m x r) ----------------------------------------------
-  float xop[32];
+  constexpr int NTI = N / 32;  // 32-row tiles of an m x r operand
+  float xop[N / 2];
   {
-    f32x16 xv[2] = {zero16(), zero16()};
+    f32x16 xv[NTI];
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      const float a0 = S.Lp[c32 * LDL + 2 * s + h];
-      const float a1 = S.Lp[(32 + c32) * LDL + 2 * s + h];
-      xv[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, Y[s], xv[0], 0, 0, 0);
-      xv[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, Y[s], xv[1], 0, 0, 0);
+    for (int I = 0; I < NTI; ++I) xv[I] = zero16();
+#pragma unroll
+    for (int s = 0; s < N / 2; ++s) {
+#pragma unroll
+      for (int I = 0; I < NTI; ++I)
+        xv[I] = __builtin_amdgcn_mfma_f32_32x32x2f32(S.Lp[(32 * I + c32) * LDL + 2 * s + h], Y[s], xv[I], 0, 0, 0);
     }
 #pragma unroll
-    for (int I = 0; I < 2; ++I) {
+    for (int I = 0; I < NTI; ++I) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 i4 = reinterpret_cast<const float4*>(S.ibal)[8 * I + 2 * q + h];
@@ -786,7 +838,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   uint32_t vw[16 * NV / 2];
   {
     f32x16 vt[NV];
-    factor_times<DV>(Vb, m, xop, vt);
+    factor_times<DV, N>(Vb, m, xop, vt);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
 #pragma unroll
@@ -795,7 +847,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   }
   {
     f32x16 w[2] = {zero16(), zero16()};
-    const bool ok0 = c32 < m, ok1 = c32 + 32 < m;
+    const bool ok0 = c32 < m, ok1 = N == 64 && c32 + 32 < m;
     const uint16_t* p0 = Vb + (ok0 ? c32 : 0) * DV + 4 * NV * h;
     const uint16_t* p1 = Vb + (ok1 ? c32 + 32 : 0) * DV + 4 * NV * h;
 #pragma unroll
@@ -809,11 +861,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       const uint4 bw4 = make_uint4(vw[4 * s], vw[4 * s + 1], vw[4 * s + 2], vw[4 * s + 3]);
       const bf16x8 bop = __builtin_bit_cast(bf16x8, bw4);
       w[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u0), bop, w[0], 0, 0, 0);
-      w[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u1), bop, w[1], 0, 0, 0);
+      if constexpr (N == 64)
+        w[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u1), bop, w[1], 0, 0, 0);
     }
     // X_U = diag(colsc) W lambda^(-1/2) (U' = U_s D_c V_s^T V' / sigma), as B operands
 #pragma unroll
-    for (int I = 0; I < 2; ++I) {
+    for (int I = 0; I < NTI; ++I) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 c4 = reinterpret_cast<const float4*>(S.colsc)[8 * I + 2 * q + h];
@@ -830,7 +883,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   uint32_t uw[16 * NU / 2];
   {
     f32x16 ut[NU];
-    factor_times<DK>(Ub, m, xop, ut);
+    factor_times<DK, N>(Ub, m, xop, ut);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int i = 8 * (j >> 2) + 4 * h + (j & 3);
@@ -867,14 +920,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 namespace {
 using WaveFn = void (*)(const CompressArgs);
 
-WaveFn pick_compress_wave(const seed_shape& sh) {
-  if (sh.factor_dtype != SEED_BF16 || sh.rank > cw::RX || sh.rank + sh.period > cw::N) return nullptr;
+template <int N>
+WaveFn pick_width(const seed_shape& sh) {
   const bool diag = sh.kind == SEED_KDA;
-  if (sh.d_k == 128 && sh.d_v == 128) return diag ? k_compress_wave<128, 128, true> : k_compress_wave<128, 128, false>;
-  if (sh.d_k == 128 && sh.d_v == 64) return diag ? k_compress_wave<128, 64, true> : k_compress_wave<128, 64, false>;
-  if (sh.d_k == 64 && sh.d_v == 128) return diag ? k_compress_wave<64, 128, true> : k_compress_wave<64, 128, false>;
-  if (sh.d_k == 64 && sh.d_v == 64) return diag ? k_compress_wave<64, 64, true> : k_compress_wave<64, 64, false>;
+  if (sh.d_k == 128 && sh.d_v == 128) return diag ? k_compress_wave<128, 128, true, N> : k_compress_wave<128, 128, false, N>;
+  if (sh.d_k == 128 && sh.d_v == 64) return diag ? k_compress_wave<128, 64, true, N> : k_compress_wave<128, 64, false, N>;
+  if (sh.d_k == 64 && sh.d_v == 128) return diag ? k_compress_wave<64, 128, true, N> : k_compress_wave<64, 128, false, N>;
+  if (sh.d_k == 64 && sh.d_v == 64) return diag ? k_compress_wave<64, 64, true, N> : k_compress_wave<64, 64, false, N>;
   return nullptr;
+}
+
+WaveFn pick_compress_wave(const seed_shape& sh) {
+  if (sh.factor_dtype != SEED_BF16 || sh.rank > cw::RX || sh.rank + sh.period > 64) return nullptr;
+  return sh.rank + sh.period <= 32 ? pick_width<32>(sh) : pick_width<64>(sh);
 }
 }  // namespace
 
