@@ -151,6 +151,11 @@ __device__ __forceinline__ int wmax_key(int v) {
   return max(static_cast<int>(r[0]), static_cast<int>(r[1]));
 }
 
+// The same value through an identity DPP move, which the compiler cannot see through: loops
+// that compare constant indices with a lane-varying index each get their own copy, so that
+// their comparison masks are not kept alive from one loop to the next.
+__device__ __forceinline__ int opaque(int v) { return __builtin_amdgcn_mov_dpp(v, 0xE4, 0xF, 0xF, false); }
+
 // A value every lane holds (a wave reduction's result), moved to a scalar register so that the
 // compiler treats branches on it as uniform.
 __device__ __forceinline__ float uni(float v) {
@@ -205,12 +210,10 @@ __device__ __forceinline__ M64 tiles_to_rows(const f32x16 (&t)[2][2]) {
 
 // MFMA 32x32x2 operands of K-step s (k = 2s + lane / 32) from a row-per-lane matrix X: .x
 // serves row (or column) block 0, .y block 1; as A they give X, as B they give X^T. With
-// N = 32 each lane already holds its row: .x is element k of it.
+// N = 32 both lanes of a pair hold the same row, so the same swap leaves element k of it in .x
+// (selecting it by lane half instead would become a lane-varying register index).
 template <int N>
 __device__ __forceinline__ float2 rows_operand(const f32x32 X_lo, const f32x32 X_hi, int s) {
-  if constexpr (N == 32) {
-    return make_float2((threadIdx.x & 32) ? X_lo[(2 * s + 1) & 31] : X_lo[(2 * s) & 31], 0.f);
-  }
   float x = MGET(X, 2 * s), y = MGET(X, 2 * s + 1);
   swap32(x, y);
   return make_float2(x, y);
@@ -654,33 +657,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       if (i < N - 1) dp = (S.dg[i + 1] - lam) - ei * (ei * __builtin_amdgcn_rcpf(nz(dp)));
     }
     dp = S.dg[0] - lam;
+    const int kb0 = opaque(kb);
 #pragma unroll
     for (int i = 0; i < N - 1; ++i) {    // e_i / D+_i into the slots above the twist
       const float ei = S.e[i];
       const float q = ei * __builtin_amdgcn_rcpf(nz(dp));
-      if (i < kb) rt[i] = q;
+      if (i < kb0) rt[i] = q;
       dp = (S.dg[i + 1] - lam) - ei * q;
     }
     // below the twist z_{i+1} = -rt[i] z_i (into rt[i]); above it z_i = -rt[i] z_{i+1} (into rt[i])
+    // (zc is 1 until the sweep passes the twist, so one comparison per slot selects)
     float zc = 1.f;
+    const int kb1 = opaque(kb);
 #pragma unroll
     for (int i = 0; i < N - 1; ++i) {
-      zc = (i == kb) ? -rt[i] : (i > kb ? -rt[i] * zc : 0.f);
-      if (i >= kb) rt[i] = zc;
+      const bool on = i >= kb1;
+      const float z = -rt[i] * zc;
+      if (on) rt[i] = z;
+      zc = on ? z : 1.f;
     }
     zc = 1.f;
+    const int kb2 = opaque(kb);
 #pragma unroll
     for (int i = N - 2; i >= 0; --i) {
-      zc = (i == kb - 1) ? -rt[i] : (i < kb - 1 ? -rt[i] * zc : 0.f);
-      if (i < kb) rt[i] = zc;
+      const bool on = i < kb2;
+      const float z = -rt[i] * zc;
+      if (on) rt[i] = z;
+      zc = on ? z : 1.f;
     }
     // z_j = rt[j] (j < kb), 1 (j = kb), rt[j - 1] (j > kb)
     float nn0 = 0.f, nn1 = 0.f;
+    const int kb3 = opaque(kb);
 #pragma unroll
     for (int s = 0; s < N / 2; ++s) {
       const int je = 2 * s, jo = 2 * s + 1;
-      const float ze = je < kb ? rt[je] : (je == kb ? 1.f : rt[je > 0 ? je - 1 : 0]);
-      const float zo = jo < kb ? rt[jo] : (jo == kb ? 1.f : rt[jo - 1]);
+      const float ze = je < kb3 ? rt[je] : (je == kb3 ? 1.f : rt[je > 0 ? je - 1 : 0]);
+      const float zo = jo < kb3 ? rt[jo] : (jo == kb3 ? 1.f : rt[jo - 1]);
       Y[s] = h ? zo : ze;
       if (s & 1) nn1 += Y[s] * Y[s]; else nn0 += Y[s] * Y[s];
     }
