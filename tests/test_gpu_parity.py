@@ -165,6 +165,12 @@ SMALL = [
     (synth.MAMBA2, 128, 64, 16, 16, synth.BF16, 3, 3),
     (synth.GDN, 64, 128, 4, 12, synth.F32, 1, 7),
     (synth.GDN, 64, 64, 24, 40, synth.BF16, 2, 3),
+    # the 32-wide compression kernel (r + T <= 32) with d_k = 64, at its largest rank, and the
+    # 64-wide one at r + T = 33
+    (synth.KDA, 64, 64, 8, 24, synth.BF16, 2, 3),
+    (synth.GDN, 64, 128, 12, 20, synth.BF16, 3, 2),
+    (synth.GDN, 128, 128, 31, 1, synth.BF16, 2, 2),
+    (synth.MAMBA2, 128, 64, 17, 16, synth.BF16, 2, 3),
 ]
 
 
