@@ -528,7 +528,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       float t = 0.f, ej = x0, v = x;
       // below the floor the column is already reduced (B is scaled to entries <= 1)
       if (sig - x0 * x0 > 1e-30f * sig && sig > kReduceFloor) {  // uniform
-        const float al = x0 >= 0.f ? -sqrtf(sig) : sqrtf(sig);
+        const float sr = __builtin_amdgcn_sqrtf(sig);   // v_sqrt_f32 (1 ulp; sig > 1e-30)
+        const float al = x0 >= 0.f ? -sr : sr;
         const float v0 = x0 - al;
         t = 2.f * __builtin_amdgcn_rcpf(sig - x0 * x0 + v0 * v0);
         ej = al;
