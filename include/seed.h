@@ -136,7 +136,10 @@ int32_t seed_from_dense_iterations(void);
  *   o      written, [units][d_v] (io_dtype): o = vbar (a+^T q) + V+ (U+^T q).
  *   state  a is decayed and projected, the scales take the decay, column m of U receives the
  *          key and column m of V receives beta (eps - V (G U)^T kappa) (GDN, KDA) or beta eps
- *          (Mamba-2), with omega = v^T vbar / |vbar|^2 and eps = v - omega vbar.
+ *          (Mamba-2), with omega = v^T vbar / |vbar|^2 and eps = v - omega vbar. KDA: a key
+ *          channel whose cumulative gate (its scale) would fall below 2^-40 is folded into
+ *          the stored columns first (that row of U is multiplied by it, the scale restarts at
+ *          1), so that the new column k / scale stays finite; the true state is unchanged.
  * Afterwards the caller holds m + 1 columns. Source: picx.dev summary, "Exact Update
  * (Lemma 2)" and "SEED Architecture".
  */
@@ -149,8 +152,10 @@ int seed_decode_step(const seed_shape *shape, const seed_state *state, int32_t m
  * The content U V^T (m columns) is replaced by its best rank-r approximation, with
  * sqrt(sigma_i) on both factors; a is not touched; scales reset to 1. Method: lazy decay
  * folded into U; column pairs balanced; Grams G_U = U^T U and G_V = V^T V; pivoted Cholesky
- * G_U ~ L L^T; the (k x k, k <= m) core B = L^T G_V L, whose eigenvalues are sigma_i^2,
- * diagonalised by cyclic Jacobi; the top r eigenpairs give U' = U X_U and V' = V X_V.
+ * G_U ~ L L^T; the (k x k, k <= m) core B = L^T G_V L, whose eigenvalues are sigma_i^2; the
+ * top r eigenpairs give U' = U X_U and V' = V X_V. The core's eigenpairs come from cyclic
+ * Jacobi in fp64 for fp32 factors, and for bf16 factors (r <= 32) from a Householder
+ * tridiagonalisation, Sturm-count multisection and twisted factorisations in fp32.
  * ws as for seed_state_from_dense with SEED_OP_COMPRESS.
  * Source: picx.dev summary, "Open-Loop Error Bound (Corollary 4)" (periodic compressions)
  * and thelatestinai.com figures & tables, overview table (compression back to rank r).
