@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--pool", type=int, default=64, help="steps of resident inputs, cycled")
     ap.add_argument("--dense-steps", type=int, default=32, help="timed dense-baseline steps")
     ap.add_argument("--prefill", type=int, default=None, help="override the prefill length")
-    ap.add_argument("--cpu-units", type=int, default=512, help="units in the oracle CPU sample")
+    ap.add_argument("--cpu-units", type=int, default=8192, help="units in the oracle CPU sample (layer-major)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--seed", type=int, default=1005)
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of graph replay")
@@ -222,16 +222,17 @@ def main():
     # host copies for the CPU baseline (taken before the decode touches the states)
     cpu_job = None
     if not args.no_cpu:
-        ns = min(args.cpu_units, U1)
-        idx = torch.arange(ns, device=dev)
+        # the first ns units of the stack: whole layers 0, 1, ... (units are layer-major)
+        ns = min(args.cpu_units, N)
+        nl = -(-ns // U1)
         ah = a[:ns].double().cpu().numpy()
         Uh = Uf[:ns, :w.rank].double().cpu().numpy()
         Vh = Vf[:ns, :w.rank].double().cpu().numpy()
         xs_h = []
         for p in range(T):
-            x = pool[p % P][0]
-            xs_h.append({k: v.index_select(0, idx).double().cpu().numpy() for k, v in x.items()})
-        vb_h = vbars[0].double().cpu().numpy()
+            xs_h.append({k: torch.cat([pool[p % P][l][k] for l in range(nl)])[:ns].double().cpu().numpy()
+                         for k in pool[p % P][0]})
+        vb_h = [vbars[l].double().cpu().numpy() for l in range(nl)]
         cpu_job = (ah, Uh, Vh, xs_h, vb_h, ns)
 
     def enqueue_window(wi):
@@ -338,7 +339,7 @@ def main():
         cores = min(16, os.cpu_count() or 1)
         states_h = [(ah[u], Uh[u].T.copy(), Vh[u].T.copy()) for u in range(ns)]
         inputs_h = [[{k: x[k][u] for k in x} for x in xs_h] for u in range(ns)]
-        heads = [vb_h[u % w.heads] for u in range(ns)]
+        heads = [vb_h[u // U1][u % w.heads] for u in range(ns)]
         shards = [(w.kind, w.rank, w.period, states_h[i::cores], inputs_h[i::cores], heads[i::cores])
                   for i in range(cores)]
         c0 = time.perf_counter()
@@ -347,7 +348,7 @@ def main():
         c_wall = time.perf_counter() - c0
         cpu = {"value": ns * w.period / c_wall, "unit": "head-steps/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"{ns} units of layer 0 x one compression window ({w.period} decode "
+               "sample": f"{ns} units (layers 0..{-(-ns // U1) - 1}) x one compression window ({w.period} decode "
                          f"steps + 1 compression), fp64 NumPy oracle, {sum(cpu_secs):.1f} s of "
                          f"CPU work on {cores} processes"}
         log(f"[bench] oracle CPU baseline: {cpu['value']:.0f} head-steps/s on {cores} cores")
