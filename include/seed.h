@@ -153,9 +153,10 @@ int seed_decode_step(const seed_shape *shape, const seed_state *state, int32_t m
  * sqrt(sigma_i) on both factors; a is not touched; scales reset to 1. Method: lazy decay
  * folded into U; column pairs balanced; Grams G_U = U^T U and G_V = V^T V; pivoted Cholesky
  * G_U ~ L L^T; the (k x k, k <= m) core B = L^T G_V L, whose eigenvalues are sigma_i^2; the
- * top r eigenpairs give U' = U X_U and V' = V X_V. The core's eigenpairs come from cyclic
- * Jacobi in fp64 for fp32 factors, and for bf16 factors (r <= 32) from a Householder
- * tridiagonalisation, Sturm-count multisection and twisted factorisations in fp32.
+ * top r eigenpairs give U' = U X_U and V' = V X_V. The core's eigenpairs come from a
+ * Householder tridiagonalisation, Sturm-count multisection and twisted factorisations in
+ * fp32 for bf16 factors with r <= 32, and otherwise from cyclic Jacobi (fp64 for fp32
+ * factors, fp32 for bf16 factors).
  * ws as for seed_state_from_dense with SEED_OP_COMPRESS.
  * Source: picx.dev summary, "Open-Loop Error Bound (Corollary 4)" (periodic compressions)
  * and thelatestinai.com figures & tables, overview table (compression back to rank r).

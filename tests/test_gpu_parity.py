@@ -171,6 +171,8 @@ SMALL = [
     (synth.GDN, 64, 128, 12, 20, synth.BF16, 3, 2),
     (synth.GDN, 128, 128, 31, 1, synth.BF16, 2, 2),
     (synth.MAMBA2, 128, 64, 17, 16, synth.BF16, 2, 3),
+    # bf16 factors with r > 32: the workgroup compression kernel with an fp32 Jacobi core
+    (synth.GDN, 128, 64, 40, 8, synth.BF16, 2, 2),
 ]
 
 
