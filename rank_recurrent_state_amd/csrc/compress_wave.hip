@@ -9,12 +9,13 @@
 //   eigenvectors Y and eigenvalues lambda, V' = V~ L Y lambda^(-1/4) and U' = M V' lambda^(-1/2)
 //   (M = U~ V~^T, so U' V'^T = M times the projector on the kept right singular directions).
 //
-// Layout on gfx950: one 64-lane wavefront per unit, lane i owning row i of every 64 x 64 core
-// matrix (64 registers, two 32-wide vectors so that a wave-uniform index reaches a register
-// through the indirect-register mode). MFMA tiles move in and out of that layout with
-// v_permlane32_swap: a 32 x 32 accumulator tile keeps one column per lane pair (l, l + 32), and
-// swapping the upper half of tile (I, 0) with the lower half of tile (I, 1) leaves every lane
-// with its own column; for a symmetric matrix that is its row.
+// Layout on gfx950: one 64-lane wavefront per unit, lane i owning row i of every N x N core
+// matrix (N = 64: 64 registers, two 32-wide vectors so that a wave-uniform index reaches a
+// register through the indirect-register mode; N = 32 when r + T <= 32: lanes i and i + 32
+// both hold row i). MFMA tiles move in and out of that layout with v_permlane32_swap: a
+// 32 x 32 accumulator tile keeps one column per lane pair (l, l + 32), and swapping the upper
+// half of tile (I, 0) with the lower half of tile (I, 1) leaves every lane with its own column;
+// for a symmetric matrix that is its row.
 //
 //   Grams                 MFMA 32x32x16 bf16 straight from the stored columns (fp32 sums);
 //   pivoted Cholesky      no row swaps: the L column of step s lands in column p_s of its LDS
@@ -31,7 +32,8 @@
 //                         I, so that each lane loads NT consecutive elements of a column);
 //                         W = V_s^T V' by MFMA 32x32x16 bf16 on the rounded V' that is stored,
 //                         so that U' = M V' / sigma holds for the stored pair.
-// LDS holds L (64 x 65 fp32) and a few vectors, about 19.5 KB, so eight units share a CU.
+// LDS holds L (N x (N + 1) fp32) and a few vectors: about 19.5 KB for N = 64, so eight units
+// share a CU (two waves per SIMD), and 6 KB for N = 32 (three waves per SIMD).
 #include <float.h>
 
 #include "common.hpp"
