@@ -15,9 +15,12 @@ steps after --warmup untimed ones, bracketed by torch.cuda.synchronize(); inputs
 in HBM (a pool of --pool steps of seeded inputs, cycled).
 
 Algorithmic bytes per unit-step of the decode at m columns (what the method must move):
-  read a (4 d_k), U and V (f (d_k + d_v) m), q, k, v (e (2 d_k + d_v)), beta and g (4 + 4 or
-  4 d_k); write a (4 d_k), the new column pair (f (d_k + d_v)) and o (e d_v). f = factor bytes,
-  e = activation bytes. The lazy decay scales and vbar are not credited.
+  read the sink a_0 (4 d_k) and its m - r window coefficients (4 (m - r)), U and V
+  (f (d_k + d_v) m), q, k, v (e (2 d_k + d_v)), beta and g (4 + 4 or 4 d_k); write the new
+  coefficient (4), the new column pair (f (d_k + d_v)) and o (e d_v). f = factor bytes,
+  e = activation bytes. The lazy decay scales and vbar are not credited. The sink is lazy: a
+  step adds a multiple of its key to a, and the key is the column it appends to U, so a step
+  stores that multiple and a is rebuilt only at compression.
 Dense step per unit: 8 d_k d_v (fp32 state read and written) + inputs + o.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -98,8 +101,8 @@ def decode_bytes(w, m: int) -> int:
     f = 2 if w.factor_dtype else 4
     e = 2 if w.io_dtype else 4
     gb = 4 * w.d_k if w.kind == 1 else 4
-    return (4 * w.d_k + f * (w.d_k + w.d_v) * m + e * (2 * w.d_k + w.d_v) + 4 + gb
-            + 4 * w.d_k + f * (w.d_k + w.d_v) + e * w.d_v)
+    return (4 * w.d_k + 4 * (m - w.rank) + f * (w.d_k + w.d_v) * m + e * (2 * w.d_k + w.d_v)
+            + 4 + gb + 4 + f * (w.d_k + w.d_v) + e * w.d_v)
 
 
 def compress_bytes(w, m: int) -> int:

@@ -76,17 +76,22 @@ typedef struct seed_shape {
 } seed_shape;
 
 /*
- * Factored state. With C = r + T column slots per unit and s = seed_scale_len(shape):
- *   a      float [units][d_k]      sink coefficient.
+ * Factored state. With C = r + T column slots per unit, s = seed_scale_len(shape) and
+ * s0 = 1 + T (GDN, Mamba-2) or d_k (KDA):
+ *   a      float [units][d_k]      sink at the last compression (a_0).
  *   U      [units][C][d_k]         slot j holds column j of U, contiguous over d_k (factor_dtype).
  *   V      [units][C][d_v]         slot j holds column j of V, contiguous over d_v (factor_dtype).
- *   scale  float [units][s]        lazy decay of U, so that U is never rewritten by a decay:
- *            GDN, Mamba-2 (s = 1 + T): the true column j of U is scale[0] * U[j] for j < r and
- *              scale[1 + j - r] * U[j] for j >= r.
- *            KDA (s = d_k): the true column j of U is scale (elementwise, per key channel) times
- *              U[j], for every j.
- *          seed_state_from_dense and seed_compress reset the scales to 1.
- * The true state is a vbar^T + sum_{j<m} U_true[:, j] V[:, j]^T.
+ *   scale  float [units][s]        s = s0 + T: the lazy decay of U (scale[0 .. s0)), so that U is
+ *          never rewritten by a decay, then the sink coefficients c (scale[s0 .. s0 + T)):
+ *            GDN, Mamba-2: the true column j of U is scale[0] * U[j] for j < r and
+ *              scale[1 + j - r] * U[j] for j >= r; the true sink is
+ *              a_true = scale[0] * a + sum_{r <= j < m} c[j - r] * U_true[:, j].
+ *            KDA: the true column j of U is scale[0 .. d_k) (elementwise, per key channel) times
+ *              U[j], for every j; a_true = scale[0 .. d_k) . (a + sum_{r <= j < m} c[j - r] U[j]).
+ *          The sink is thus kept lazily like the decay: a decode step appends the new column's
+ *          coefficient instead of rewriting a. seed_state_from_dense and seed_compress leave
+ *          a = a_true, the decay scales at 1 and the coefficients at 0.
+ * The true state is a_true vbar^T + sum_{j<m} U_true[:, j] V[:, j]^T.
  */
 typedef struct seed_state {
   float *a;
@@ -99,7 +104,8 @@ typedef struct seed_state {
  * the shape is invalid. Host-only, pure. */
 size_t seed_state_bytes(const seed_shape *shape);
 
-/* Length s of one unit's scale vector (1 + T, or d_k for KDA), or 0 if the shape is invalid. */
+/* Length s of one unit's scale vector (decay scales 1 + T, or d_k for KDA, then T sink
+ * coefficients), or 0 if the shape is invalid. */
 int32_t seed_scale_len(const seed_shape *shape);
 
 /* Workspace bytes that an operation needs (op = SEED_OP_COMPRESS or SEED_OP_FROM_DENSE);
@@ -134,12 +140,15 @@ int32_t seed_from_dense_iterations(void);
  *   beta   float [units]. g: float [units] (GDN, Mamba-2) or float [units][d_k] (KDA).
  *   vbar   float [heads][d_v].
  *   o      written, [units][d_v] (io_dtype): o = vbar (a+^T q) + V+ (U+^T q).
- *   state  a is decayed and projected, the scales take the decay, column m of U receives the
- *          key and column m of V receives beta (eps - V (G U)^T kappa) (GDN, KDA) or beta eps
- *          (Mamba-2), with omega = v^T vbar / |vbar|^2 and eps = v - omega vbar. KDA: a key
+ *   state  the scales take the decay, column m of U receives the key, column m of V receives
+ *          beta (eps - V (G U)^T kappa) (GDN, KDA) or beta eps (Mamba-2), and the sink
+ *          coefficient of column m is beta (omega - kappa^T G a_true) (GDN, KDA) or beta omega
+ *          (Mamba-2), with omega = v^T vbar / |vbar|^2 and eps = v - omega vbar; a itself is not
+ *          written (Lemma 2's sink update a+ = G a + coef kappa, kept lazily). KDA: a key
  *          channel whose cumulative gate (its scale) would fall below 2^-40 is folded into
  *          the stored columns first (that row of U is multiplied by it, the scale restarts at
- *          1), so that the new column k / scale stays finite; the true state is unchanged.
+ *          1, and a carries the same factor), so that the new column k / scale stays finite;
+ *          the true state is unchanged.
  * Afterwards the caller holds m + 1 columns. Source: picx.dev summary, "Exact Update
  * (Lemma 2)" and "SEED Architecture".
  */
@@ -150,7 +159,8 @@ int seed_decode_step(const seed_shape *shape, const seed_state *state, int32_t m
 /*
  * Compression of the content back to rank r (leaves m = r; nothing is done when m <= r).
  * The content U V^T (m columns) is replaced by its best rank-r approximation, with
- * sqrt(sigma_i) on both factors; a is not touched; scales reset to 1. Method: lazy decay
+ * sqrt(sigma_i) on both factors; a becomes a_true, the decay scales 1 and the sink
+ * coefficients 0. Method: lazy decay
  * folded into U; column pairs balanced; Grams G_U = U^T U and G_V = V^T V; pivoted Cholesky
  * G_U ~ L L^T; the (k x k, k <= m) core B = L^T G_V L, whose eigenvalues are sigma_i^2; the
  * top r eigenpairs give U' = U X_U and V' = V X_V. The core's eigenpairs come from a

@@ -144,6 +144,7 @@ class State:
         U = torch.zeros((n, shape.slots, shape.d_k), dtype=fdt, device=device)
         V = torch.zeros((n, shape.slots, shape.d_v), dtype=fdt, device=device)
         scale = torch.ones((n, seed_scale_len(shape)), dtype=torch.float32, device=device)
+        scale[:, seed_scale_len(shape) - shape.period:] = 0.0  # sink coefficients
         return cls(a, U, V, scale)
 
     def tensors(self):

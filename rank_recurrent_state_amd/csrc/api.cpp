@@ -31,9 +31,13 @@ int check_shape(const seed_shape* sh) {
 
 int64_t units_of(const seed_shape* sh) { return static_cast<int64_t>(sh->batch) * sh->heads; }
 
-int32_t scale_len(const seed_shape* sh) {
+// Per-unit scale buffer: the lazy decay scales (1 + T slot scales, or KDA's d_k channel scales),
+// then the T sink coefficients of the window's columns.
+int32_t coef_off(const seed_shape* sh) {
   return sh->kind == SEED_KDA ? sh->d_k : 1 + sh->period;
 }
+
+int32_t scale_len(const seed_shape* sh) { return coef_off(sh) + sh->period; }
 
 bool state_ok(const seed_state* st) {
   return st && st->a && st->U && st->V && st->scale;
@@ -49,6 +53,7 @@ seed::CompressArgs compress_args(const seed_shape* sh, const seed_state* st, int
   a.rank = sh->rank;
   a.slots = sh->rank + sh->period;
   a.scale_len = scale_len(sh);
+  a.coef_off = coef_off(sh);
   a.a = st->a;
   a.U = st->U;
   a.V = st->V;
@@ -112,6 +117,7 @@ int seed_decode_step(const seed_shape* sh, const seed_state* st, int32_t m, cons
   a.rank = sh->rank;
   a.slots = sh->rank + sh->period;
   a.scale_len = scale_len(sh);
+  a.coef_off = coef_off(sh);
   a.a = st->a;
   a.U = st->U;
   a.V = st->V;

@@ -399,6 +399,25 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
   }
   __syncthreads();
 
+  // the lazy sink folded into a: a = (slot-0 decay) a_0 + sum_{j >= r} c_j (true column j)
+  // (KDA: Gamma . (a_0 + sum_j c_j U_j)); the window columns are not rewritten below. The
+  // column reads go out 8 at a time, independent of one another.
+  for (int d = t; d < DK; d += 256) {
+    float acc = 0.f;
+    for (int j0 = r; j0 < m; j0 += 8) {
+      float u[8], cj[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int j = j0 + i < m ? j0 + i : m - 1;
+        cj[i] = j0 + i < m ? sc[A.coef_off + j - r] * (DIAG ? 1.f : sc[1 + j - r]) : 0.f;
+        u[i] = to_f32<FDT>(Ub[static_cast<int64_t>(j) * DK + d]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = fmaf(cj[i], u[i], acc);
+    }
+    A.a[unit * DK + d] = DIAG ? gam[d] * (A.a[unit * DK + d] + acc) : sc[0] * A.a[unit * DK + d] + acc;
+  }
+
   // 1. Grams of the stored columns
   gram_rows<CT, CT, DK, FDT, DIAG ? 1 : 0>(S, Ub, m, gam, S.GA);
   gram_rows<CT, CT, DV, FDT, 0>(S, Vb, m, gam, S.GB);
@@ -421,8 +440,8 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
   }
   __syncthreads();
   reconstruct_rows<CT, DV, FDT, false>(S, S.GA, m, r, nullptr, Vb);
-  // scales back to 1
-  for (int i = t; i < A.scale_len; i += 256) sc[i] = 1.f;
+  // decay scales back to 1, sink coefficients to 0
+  for (int i = t; i < A.scale_len; i += 256) sc[i] = i < A.coef_off ? 1.f : 0.f;
 }
 
 template <int DK, int FDT>
@@ -737,7 +756,7 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
     }
   }
   float* __restrict__ sc = A.scale + unit * A.scale_len;
-  for (int i = t; i < A.scale_len; i += 256) sc[i] = 1.f;
+  for (int i = t; i < A.scale_len; i += 256) sc[i] = i < A.coef_off ? 1.f : 0.f;
 }
 
 // ---- host dispatch ---------------------------------------------------------------------------

@@ -405,6 +405,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   S.colsc[row] = csc;
   wave_lds_sync();
 
+  // ---- the lazy sink folded into a: a = (slot-0 decay) a_0 + sum_{j >= r} c_j (true column j)
+  // (KDA: Gamma . (a_0 + sum_j c_j U_j)); the window columns are not rewritten below. A lane
+  // holds DK / 64 consecutive channels; the column reads go out 16 at a time, independent of
+  // one another, so a unit waits on memory about twice rather than once per column.
+  {
+    constexpr int EPL = DK / 64;
+    static_assert(EPL == 1 || EPL == 2, "d_k of 64 or 128");
+    const int d0 = EPL * lane;
+    float acc[EPL] = {};
+    for (int j0 = r; j0 < m; j0 += 16) {
+      uint32_t w[16];
+      float cj[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = j0 + i < m ? j0 + i : m - 1;
+        cj[i] = j0 + i < m ? sc[A.coef_off + j - r] * (DIAG ? 1.f : sc[1 + j - r]) : 0.f;
+        const uint16_t* p = Ub + static_cast<int64_t>(j) * DK + d0;
+        if constexpr (EPL == 2) w[i] = *reinterpret_cast<const uint32_t*>(p);
+        else w[i] = p[0];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[0] = fmaf(cj[i], __uint_as_float(w[i] << 16), acc[0]);
+        if constexpr (EPL == 2) acc[1] = fmaf(cj[i], __uint_as_float(w[i] & 0xffff0000u), acc[1]);
+      }
+    }
+    float* __restrict__ ap = A.a + unit * DK + d0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      ap[e] = DIAG ? S.gam[d0 + e] * (ap[e] + acc[e]) : sc[0] * ap[e] + acc[e];
+  }
+
   // ---- Grams of the stored columns -------------------------------------------------------------
   f32x32 GU_lo, GU_hi, GV_lo, GV_hi;
   {
@@ -929,7 +961,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
         *reinterpret_cast<uint32_t*>(Ub + c32 * DK + NU * i) = uw[j];
     }
   }
-  for (int i = lane; i < A.scale_len; i += 64) sc[i] = 1.f;
+  // decay scales restart at 1, sink coefficients at 0
+  for (int i = lane; i < A.scale_len; i += 64) sc[i] = i < A.coef_off ? 1.f : 0.f;
 }
 
 namespace {

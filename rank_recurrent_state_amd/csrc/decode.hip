@@ -21,6 +21,13 @@
 //           transposed permlane swaps (every lane ends with a few elements of d_v).
 //   Epilogue: w = beta (eps - V x) (delta kinds) or beta eps (Mamba-2) becomes column m of V,
 //           the key becomes column m of U, and o = vbar (a+ . q) + V y + (kappa . q) w.
+// The sink is lazy as well. Lemma 2 adds a multiple of kappa to a at every step, and kappa is
+// the column the step appends to U, so the state keeps a_0 (the sink when the factors were last
+// compressed) and one coefficient c_j per window column: a = (decay of slot 0) a_0 + sum_j c_j
+// (decayed U)_j. The step reads a_0 and the coefficients and writes only its own c_m = beta
+// (omega - kappa . a) (beta omega for Mamba-2). It never rewrites the d_k-vector a, whose
+// read-modify-write made a third stream next to the factor reads and column writes. Compression
+// folds a back to one vector and clears the coefficients.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -244,7 +251,7 @@ void k_decode(const StepArgs A) {
   const float beta = A.beta[unit];
   const float gs = DIAG ? 0.f : A.g[unit];
   float* __restrict__ sc = A.scale + unit * A.scale_len;
-  float own_scale = 0.f, col_scale = 1.f, Gm[VF], alpha[VF];
+  float own_scale = 0.f, col_scale = 1.f, slot0 = 1.f, Gm[VF], alpha[VF], av[VF];
   if constexpr (DIAG) {
     load_f32<0, VF>(A.g + unit * DK + uo, alpha);
     load_f32<0, VF>(sc + uo, Gm);
@@ -253,7 +260,11 @@ void k_decode(const StepArgs A) {
     // column past the live ones gets a finite stand-in (its loads read zeros)
     own_scale = sc[min(lane, m - r)];
     col_scale = sc[jt < r ? 0 : min(1 + jt - r, m - r)];
+    slot0 = sc[0];
   }
+  // the lazy sink: a_0 (decayed like slot 0; KDA: by Gamma) plus c_j times each window column
+  load_f32<0, VF>(A.a + unit * DK + uo, av);
+  const float cw = (jt >= r && jt < m) ? sc[A.coef_off + jt - r] : 0.f;
 
   __builtin_amdgcn_sched_barrier(0);
 
@@ -269,6 +280,9 @@ void k_decode(const StepArgs A) {
   // below the U pass to save registers, serialising the latencies)
   __builtin_amdgcn_sched_barrier(0);
 
+  // kappa . q (the new column's share of the read-out) and the sink's a_0 part of kappa . a_d and
+  // a_d . q, before the U pass
+  float s, ka0, aq0;
   if constexpr (DIAG) {
     float Gn[VF];
     bool tiny = false;
@@ -299,6 +313,10 @@ void k_decode(const StepArgs A) {
         if (j < m) store_f32<FDT, VF>(Ub + static_cast<int64_t>(j) * DK + uo, u);
         ur[i] = pack16<FDT, VF>(u);
       }
+      // a_0 carries the same per-channel factor as the stored columns
+#pragma unroll
+      for (int e = 0; e < VF; ++e) av[e] *= f[e];
+      if (ug == 0) store_f32<0, VF>(A.a + unit * DK + uo, av);
     }
     // the new U column kappa / Gamma and Gamma itself do not depend on the passes: written now
     // (the U pass reads only the columns before m), their registers are free for the U pass
@@ -309,11 +327,18 @@ void k_decode(const StepArgs A) {
       store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
       store_f32<0, VF>(sc + uo, Gn);
     }
+    float pkq = 0.f, pka = 0.f, paq = 0.f;
 #pragma unroll
     for (int e = 0; e < VF; ++e) {
+      pkq += kt[e] * qt[e];
       kt[e] *= Gn[e];
       qt[e] *= Gn[e];
+      pka += kt[e] * av[e];
+      paq += qt[e] * av[e];
     }
+    s = group_sum<LPU>(pkq);
+    ka0 = group_sum<LPU>(pka);
+    aq0 = group_sum<LPU>(paq);
   } else {
     // the new U column is the key itself
     if (ug == 0) {
@@ -327,6 +352,25 @@ void k_decode(const StepArgs A) {
       store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
     }
     col_scale *= gs;
+    float kv[VF], qv[VF];
+    if constexpr (DOT2) {
+      unpack16<1, VF>(kraw, kv);
+      unpack16<1, VF>(qraw, qv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VF; ++e) { kv[e] = kt[e]; qv[e] = qt[e]; }
+    }
+    float pkq = 0.f, pka = 0.f, paq = 0.f;
+#pragma unroll
+    for (int e = 0; e < VF; ++e) {
+      pkq += kv[e] * qv[e];
+      pka += kv[e] * av[e];
+      paq += qv[e] * av[e];
+    }
+    const float p0 = gs * slot0;  // a_0's decay to this step
+    s = group_sum<LPU>(pkq);
+    ka0 = p0 * group_sum<LPU>(pka);
+    aq0 = p0 * group_sum<LPU>(paq);
   }
 
   // ---- 3. U pass: x = (G U)^T kappa, y = (G U)^T q ----------------------------------------------
@@ -361,23 +405,14 @@ void k_decode(const StepArgs A) {
   tsum_in_group<NIU, NIU, LPU / 2>(py, lane);
   // every column slot is written (zero past the live columns), so the V pass needs no mask;
   // lanes that share a column write the same value
-  if constexpr (DELTA) xs[wv][jt] = col_scale * px[0];
-  ys[wv][jt] = col_scale * py[0];
+  const float xj = col_scale * px[0], yj = col_scale * py[0];
+  if constexpr (DELTA) xs[wv][jt] = xj;
+  ys[wv][jt] = yj;
 
-  // ---- 4. the per-unit vectors of the update, then V when it was not loaded up front ----------
-  // q, kappa and the gate are read again (cache hits) rather than held through the U pass. The
-  // small loads go first: loads complete in order, so the sink below waits only for them.
+  // ---- 4. the value-side vectors, then V when it was not loaded up front -----------------------
+  // The small loads go first: loads complete in order, so the value split waits only for them.
   if constexpr (SPLIT) __builtin_amdgcn_sched_barrier(0);
-  float qv[VF], kv[VF], gv[VF], av[VF], vv[NB], vb[NB];
-  load_f32<IDT, VF>(qp, qv);
-  load_f32<IDT, VF>(kp, kv);
-  if constexpr (DIAG) {
-    load_f32<0, VF>(A.g + unit * DK + uo, gv);
-  } else {
-#pragma unroll
-    for (int e = 0; e < VF; ++e) gv[e] = gs;
-  }
-  load_f32<0, VF>(A.a + unit * DK + uo, av);
+  float vv[NB], vb[NB];
   load_f32<IDT, NB>(reinterpret_cast<const IT*>(A.v) + unit * DV + ve, vv);
   load_f32<0, NB>(A.vbar + static_cast<int64_t>(head) * DV + ve, vb);
   if constexpr (SPLIT) {
@@ -385,6 +420,12 @@ void k_decode(const StepArgs A) {
     __builtin_amdgcn_sched_barrier(0);
   }
   wave_lds_sync();
+
+  // the window's share of the sink: sum_j c_j x_j and sum_j c_j y_j (one copy of each column;
+  // summed once the V loads are out)
+  const bool first = ((lane % LPU) % (LPU / NIU)) == 0;
+  const float cx = DELTA ? wave_sum(first ? cw * xj : 0.f) : 0.f;
+  const float cy = wave_sum(first ? cw * yj : 0.f);
 
   // value split along vbar (omega, eps): every lane holds NB distinct elements of v
   float pvv = 0.f, pnn = 0.f;
@@ -394,28 +435,15 @@ void k_decode(const StepArgs A) {
   pnn = wave_sum(pnn);
   const float omega = pnn > 0.f ? pvv / pnn : 0.f;
 
-  // sink: a_d = G a, a+ = a_d + beta (omega - kappa . a_d) kappa (Mamba-2: no kappa . a_d)
-  float pka = 0.f, pkq = 0.f;
-#pragma unroll
-  for (int e = 0; e < VF; ++e) {
-    av[e] *= gv[e];
-    pka += kv[e] * av[e];
-    pkq += kv[e] * qv[e];
-  }
-  const float ka = group_sum<LPU>(pka);
-  const float s = group_sum<LPU>(pkq);  // kappa . q: the new column's share of the read-out
+  // sink: a_d = G a, a+ = a_d + beta (omega - kappa . a_d) kappa (Mamba-2: no kappa . a_d). The
+  // new column's coefficient is beta (omega - kappa . a_d) (Mamba-2: beta omega), and
+  // a+ . q = a_d . q + coef (kappa . q).
+  const float ka = ka0 + cx;
   const float coef = beta * (DELTA ? (omega - ka) : omega);
-  float an[VF];
-  float paq = 0.f;
-#pragma unroll
-  for (int e = 0; e < VF; ++e) {
-    an[e] = av[e] + coef * kv[e];
-    paq += an[e] * qv[e];
-  }
-  const float aq = group_sum<LPU>(paq);
+  const float aq = aq0 + cy + coef * s;
 
-  // a+ and the decay state are final: write them now, so their registers are free for the V pass
-  if (ug == 0) store_f32<0, VF>(A.a + unit * DK + uo, an);
+  // the coefficient and the decay state are final: write them now
+  if (lane == 0) sc[A.coef_off + m - r] = coef;
   if constexpr (!DIAG) {
     if (lane <= m - r) sc[lane] = gs * own_scale;
     else if (lane == m - r + 1) sc[lane] = 1.f;

@@ -14,7 +14,8 @@ struct StepArgs {
   int32_t m;          // columns held before the step
   int32_t rank;       // r
   int32_t slots;      // r + T: column slots per unit
-  int32_t scale_len;  // 1 + T (GDN, Mamba-2) or d_k (KDA)
+  int32_t scale_len;  // per-unit floats of the scale buffer: decay scales, then sink coefficients
+  int32_t coef_off;   // where the T sink coefficients start: 1 + T (GDN, Mamba-2) or d_k (KDA)
   float* a;
   void* U;
   void* V;
@@ -46,6 +47,7 @@ struct CompressArgs {
   int32_t rank;
   int32_t slots;
   int32_t scale_len;
+  int32_t coef_off;
   float* a;
   void* U;
   void* V;

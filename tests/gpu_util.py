@@ -44,10 +44,11 @@ def host_inputs(dx: dict, units) -> list:
 
 
 def host_state(shape, st, units, m: int):
-    """Read back (a, U, V) in true (decay-folded) form, float64, for the given units.
+    """Read back (a, U, V) in true (decay- and sink-folded) form, float64, for the given units.
 
-    U columns: GDN / Mamba-2 fold the per-column scale (slot 0 for j < r, slot 1 + j - r
-    after); KDA folds the per-channel Gamma.
+    The scale buffer holds the lazy decay (GDN / Mamba-2: slot 0 for the columns j < r, slot
+    1 + j - r after; KDA: the per-channel Gamma), then the sink coefficients c of the window's
+    columns: the true sink is the decayed stored a plus sum_{j >= r} c[j - r] times true column j.
     """
     import torch
     idx = torch.as_tensor(list(units), device=st.a.device)
@@ -55,14 +56,20 @@ def host_state(shape, st, units, m: int):
     Us = st.U.index_select(0, idx)[:, :m].double().cpu().numpy()
     Vs = st.V.index_select(0, idx)[:, :m].double().cpu().numpy()
     sc = st.scale.index_select(0, idx).double().cpu().numpy()
+    s0 = shape.d_k if shape.kind == synth.KDA else 1 + shape.period
+    r = shape.rank
     out = []
     for n in range(len(units)):
         if shape.kind == synth.KDA:
-            U = (Us[n] * sc[n][None, :]).T
+            U = (Us[n] * sc[n][None, :s0]).T
+            a_true = sc[n][:s0] * a[n]
         else:
-            c = np.array([sc[n][0] if j < shape.rank else sc[n][1 + j - shape.rank] for j in range(m)])
+            c = np.array([sc[n][0] if j < r else sc[n][1 + j - r] for j in range(m)])
             U = (Us[n] * c[:, None]).T
-        out.append((a[n], U, Vs[n].T))
+            a_true = sc[n][0] * a[n]
+        for j in range(r, m):
+            a_true = a_true + sc[n][s0 + j - r] * U[:, j]
+        out.append((a_true, U, Vs[n].T))
     return out
 
 

@@ -35,12 +35,13 @@ def test_every_declared_symbol_is_exported():
 def test_size_queries():
     rrs = _lib()
     sh = rrs.make_shape(rrs.SEED_GDN, 64, 16, 128, 128, 16, 16, rrs.SEED_BF16)
-    # a (4 d_k) + U, V (2 bytes x 32 slots x (128 + 128)) + scale (4 (1 + T))
-    assert rrs.seed_state_bytes(sh) == 4 * 128 + 2 * 32 * 256 + 4 * 17
-    assert rrs.seed_scale_len(sh) == 17
+    # a (4 d_k) + U, V (2 bytes x 32 slots x (128 + 128)) + scale (4 ((1 + T) + T): decay scales,
+    # then the sink coefficients)
+    assert rrs.seed_state_bytes(sh) == 4 * 128 + 2 * 32 * 256 + 4 * 33
+    assert rrs.seed_scale_len(sh) == 33
     kda = rrs.make_shape(rrs.SEED_KDA, 2, 2, 128, 128, 32, 32, rrs.SEED_F32)
-    assert rrs.seed_scale_len(kda) == 128
-    assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 128
+    assert rrs.seed_scale_len(kda) == 128 + 32
+    assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 160
     assert rrs.seed_workspace_bytes(sh, rrs.SEED_OP_COMPRESS) == 0
     assert rrs.seed_workspace_bytes(sh, rrs.SEED_OP_FROM_DENSE) == 0
     assert rrs.seed_from_dense_iterations() >= 1
