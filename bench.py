@@ -28,6 +28,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=1024, help="timed decode steps")
     ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps first")
     ap.add_argument("--workload", default="gdn-stack36")
+    ap.add_argument("--factor-dtype", choices=["fp32", "bf16", "fp16"], default=None,
+                    help="factor storage other than the workload's own (fp16: with bf16 inputs)")
     ap.add_argument("--pool", type=int, default=64, help="steps of resident inputs, cycled")
     ap.add_argument("--dense-steps", type=int, default=32, help="timed dense-baseline steps")
     ap.add_argument("--prefill", type=int, default=None, help="override the prefill length")
@@ -155,13 +158,18 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[args.workload]
+    if args.factor_dtype is not None:
+        fd = {"fp32": synth.F32, "bf16": synth.BF16, "fp16": synth.F16}[args.factor_dtype]
+        w = dataclasses.replace(w, factor_dtype=fd,
+                                io_dtype=synth.BF16 if fd == synth.F16 else (w.io_dtype if fd else synth.F32))
     prefill = w.prefill if args.prefill is None else args.prefill
     L = w.layers
     U1 = w.batch * w.heads           # units per launch (one layer)
     N = L * U1
     C = w.rank + w.period
-    io = torch.bfloat16 if w.io_dtype else torch.float32
-    fdt = torch.bfloat16 if w.factor_dtype else torch.float32
+    torch_dt = {synth.F32: torch.float32, synth.BF16: torch.bfloat16, synth.F16: torch.float16}
+    io = torch_dt[w.io_dtype]
+    fdt = torch_dt[w.factor_dtype]
     sh = rrs.make_shape(w.kind, w.batch, w.heads, w.d_k, w.d_v, w.rank, w.period,
                         w.factor_dtype, w.io_dtype)
     sh_all = rrs.make_shape(w.kind, w.batch * L, w.heads, w.d_k, w.d_v, w.rank, w.period,
@@ -387,10 +395,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.describe()}", "units": N, "launch_units": U1,
-                   "layers": L, "factor_storage": "bf16" if w.factor_dtype else "fp32",
+                   "layers": L, "factor_storage": {synth.F32: "fp32", synth.BF16: "bf16", synth.F16: "fp16"}[w.factor_dtype],
                    "prefill_tokens": prefill},
         "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
+                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name) if args.factor_dtype is None else None,
                      "kernel": "k_decode (factored read-out + update)",
                      "bytes_per_launch": dec_bytes / n_dec_launch,
                      "avg_launch_us": avg_launch_us},

@@ -38,9 +38,14 @@
  *   - Column count m. The caller keeps m (uniform over the batch): seed_state_from_dense
  *     leaves m = r; seed_decode_step takes m (r <= m < r + T) and leaves m + 1;
  *     seed_compress takes m and leaves r (nothing is done when m <= r).
- *   - Data types. factor_dtype selects the storage of U and V (fp32, or bf16 rounded to
- *     nearest-even); io_dtype the storage of q, k, v and o. a, scale, beta, g, vbar and dense
- *     states are always fp32. Arithmetic is fp32 throughout.
+ *   - Data types. factor_dtype selects the storage of U and V: fp32, or bf16 or IEEE fp16, both
+ *     rounded to nearest-even (the reduced-precision factor formats of the pages' appendix
+ *     table on number formats and rounding); io_dtype the storage of q, k, v and o. The factor /
+ *     io pairs are fp32 / fp32, bf16 / bf16 and fp16 / bf16. a, scale, beta, g, vbar and dense
+ *     states are always fp32. Arithmetic is fp32 throughout. With fp16 factors, KDA folds a key
+ *     channel's cumulative gate into the stored columns once it falls below 2^-12 (2^-40 for
+ *     the other formats), so that the stored key kappa / Gamma stays within fp16's range;
+ *     values beyond that range (65504) are not checked and become infinities.
  *   - Supported shapes: d_k, d_v in {64, 128}; rank >= 1, period >= 1, rank + period <= 64.
  *     Other shapes return SEED_ERR_UNSUPPORTED.
  */
@@ -63,7 +68,7 @@ enum {
 };
 
 enum { SEED_GDN = 0, SEED_KDA = 1, SEED_MAMBA2 = 2 };
-enum { SEED_F32 = 0, SEED_BF16 = 1 };
+enum { SEED_F32 = 0, SEED_BF16 = 1, SEED_F16 = 2 };
 enum { SEED_OP_COMPRESS = 0, SEED_OP_FROM_DENSE = 1 };
 
 typedef struct seed_shape {
@@ -71,7 +76,7 @@ typedef struct seed_shape {
   int32_t batch, heads;  /* units = batch * heads                                            */
   int32_t d_k, d_v;      /* d_k: key side (Mamba-2 d_state), the side of a; d_v: value side   */
   int32_t rank, period;  /* r and T: compression back to r columns every T steps             */
-  int32_t factor_dtype;  /* SEED_F32 or SEED_BF16: storage of U and V                        */
+  int32_t factor_dtype;  /* SEED_F32, SEED_BF16 or SEED_F16: storage of U and V              */
   int32_t io_dtype;      /* SEED_F32 or SEED_BF16: storage of q, k, v and o                  */
 } seed_shape;
 

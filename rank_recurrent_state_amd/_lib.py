@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libseed.so")
 
 SEED_OK, SEED_ERR_ARG, SEED_ERR_UNSUPPORTED, SEED_ERR_WORKSPACE, SEED_ERR_HIP = 0, -1, -2, -3, -4
 SEED_GDN, SEED_KDA, SEED_MAMBA2 = 0, 1, 2
-SEED_F32, SEED_BF16 = 0, 1
+SEED_F32, SEED_BF16, SEED_F16 = 0, 1, 2
 SEED_OP_COMPRESS, SEED_OP_FROM_DENSE = 0, 1
 
 EXPORTS = [
@@ -82,8 +82,11 @@ LIB = _load()
 
 def make_shape(kind: int, batch: int, heads: int, d_k: int, d_v: int, rank: int, period: int,
                factor_dtype: int = SEED_F32, io_dtype: int | None = None) -> seed_shape:
-    return seed_shape(kind, batch, heads, d_k, d_v, rank, period, factor_dtype,
-                      factor_dtype if io_dtype is None else io_dtype)
+    """A seed_shape; io_dtype defaults to the factor dtype (bf16 for fp16 factors, the one
+    input format compiled with them)."""
+    if io_dtype is None:
+        io_dtype = SEED_BF16 if factor_dtype == SEED_F16 else factor_dtype
+    return seed_shape(kind, batch, heads, d_k, d_v, rank, period, factor_dtype, io_dtype)
 
 
 def _stream_ptr(stream):
@@ -138,7 +141,7 @@ class State:
     @classmethod
     def empty(cls, shape: seed_shape, device="cuda"):
         import torch
-        fdt = torch.bfloat16 if shape.factor_dtype == SEED_BF16 else torch.float32
+        fdt = _torch_dt(shape.factor_dtype)
         n = shape.units
         a = torch.zeros((n, shape.d_k), dtype=torch.float32, device=device)
         U = torch.zeros((n, shape.slots, shape.d_k), dtype=fdt, device=device)
@@ -157,7 +160,7 @@ def _state_c(state):
 
 def _torch_dt(code):
     import torch
-    return torch.bfloat16 if code == SEED_BF16 else torch.float32
+    return {SEED_F32: torch.float32, SEED_BF16: torch.bfloat16, SEED_F16: torch.float16}[code]
 
 
 def _expect(name, t, numel, code=None):

@@ -12,9 +12,9 @@ int32_t from_dense_iterations();
 
 namespace {
 
-bool dtype_ok(int32_t d) { return d == SEED_F32 || d == SEED_BF16; }
+bool dtype_ok(int32_t d) { return d == SEED_F32 || d == SEED_BF16 || d == SEED_F16; }
 bool dim_ok(int32_t d) { return d == 64 || d == 128; }
-size_t dt_bytes(int32_t d) { return d == SEED_BF16 ? 2 : 4; }
+size_t dt_bytes(int32_t d) { return d == SEED_F32 ? 4 : 2; }
 
 // 0: valid; SEED_ERR_ARG: malformed; SEED_ERR_UNSUPPORTED: well formed but not compiled.
 int check_shape(const seed_shape* sh) {
@@ -23,6 +23,7 @@ int check_shape(const seed_shape* sh) {
   if (sh->batch <= 0 || sh->heads <= 0 || sh->d_k <= 0 || sh->d_v <= 0) return SEED_ERR_ARG;
   if (sh->rank <= 0 || sh->period <= 0) return SEED_ERR_ARG;
   if (!dtype_ok(sh->factor_dtype) || !dtype_ok(sh->io_dtype)) return SEED_ERR_ARG;
+  if (sh->io_dtype == SEED_F16) return SEED_ERR_UNSUPPORTED;  // fp16 is a factor format only
   if (!dim_ok(sh->d_k) || !dim_ok(sh->d_v)) return SEED_ERR_UNSUPPORTED;
   if (sh->rank + sh->period > 64) return SEED_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(sh->batch) * sh->heads > (int64_t{1} << 31) - 1) return SEED_ERR_UNSUPPORTED;

@@ -9,10 +9,12 @@ namespace seed {
 
 constexpr int kWave = 64;
 
-// Storage type for a dtype code (0 = fp32, 1 = bf16 held as raw 16-bit words).
+// Storage type for a dtype code (0 = fp32, 1 = bf16 and 2 = IEEE fp16, both held as raw
+// 16-bit words).
 template <int DT> struct Stor;
 template <> struct Stor<0> { using T = float; };
 template <> struct Stor<1> { using T = uint16_t; };
+template <> struct Stor<2> { using T = uint16_t; };
 template <int DT> using stor_t = typename Stor<DT>::T;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -25,13 +27,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Round to nearest even (v_cvt_f16_f32 in the default rounding mode); beyond the fp16 range the
+// result is an infinity.
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
 template <int DT> __device__ __forceinline__ float to_f32(stor_t<DT> x);
 template <> __device__ __forceinline__ float to_f32<0>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<1>(uint16_t x) { return bf16_to_f32(x); }
+template <> __device__ __forceinline__ float to_f32<2>(uint16_t x) { return f16_to_f32(x); }
 
 template <int DT> __device__ __forceinline__ stor_t<DT> from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<0>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t from_f32<1>(float x) { return f32_to_bf16(x); }
+template <> __device__ __forceinline__ uint16_t from_f32<2>(float x) { return f32_to_f16(x); }
+
+// The two 16-bit elements of a 32-bit word (element 0 in the low half) of dtype DT (1 or 2),
+// and the word two values round to.
+template <int DT> __device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (DT == 1) return __uint_as_float(w << 16);
+  else return f16_to_f32(static_cast<uint16_t>(w & 0xffffu));
+}
+template <int DT> __device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (DT == 1) return __uint_as_float(w & 0xffff0000u);
+  else return f16_to_f32(static_cast<uint16_t>(w >> 16));
+}
+template <int DT> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return static_cast<uint32_t>(from_f32<DT>(a)) | (static_cast<uint32_t>(from_f32<DT>(b)) << 16);
+}
 
 // Load N consecutive elements of storage dtype DT into fp32 registers. N * sizeof(T) must be
 // a multiple of 4 and the address aligned to it; wide accesses are used where possible.
@@ -50,9 +78,9 @@ __device__ __forceinline__ void load_f32(const stor_t<DT>* __restrict__ p, float
       for (int e = 0; e < N; ++e) out[e] = p[e];
     }
   } else if constexpr (N == 1) {
-    out[0] = bf16_to_f32(p[0]);
+    out[0] = to_f32<DT>(p[0]);
   } else {
-    static_assert(N % 2 == 0, "bf16 vector width");
+    static_assert(N % 2 == 0, "16-bit vector width");
     if constexpr (N % 8 == 0) {
 #pragma unroll
       for (int c = 0; c < N / 8; ++c) {
@@ -60,31 +88,31 @@ __device__ __forceinline__ void load_f32(const stor_t<DT>* __restrict__ p, float
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          out[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
-          out[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+          out[8 * c + 2 * e] = lo16<DT>(w[e]);
+          out[8 * c + 2 * e + 1] = hi16<DT>(w[e]);
         }
       }
     } else if constexpr (N % 4 == 0) {
 #pragma unroll
       for (int c = 0; c < N / 4; ++c) {
         uint2 v = reinterpret_cast<const uint2*>(p)[c];
-        out[4 * c + 0] = __uint_as_float(v.x << 16);
-        out[4 * c + 1] = __uint_as_float(v.x & 0xffff0000u);
-        out[4 * c + 2] = __uint_as_float(v.y << 16);
-        out[4 * c + 3] = __uint_as_float(v.y & 0xffff0000u);
+        out[4 * c + 0] = lo16<DT>(v.x);
+        out[4 * c + 1] = hi16<DT>(v.x);
+        out[4 * c + 2] = lo16<DT>(v.y);
+        out[4 * c + 3] = hi16<DT>(v.y);
       }
     } else {
 #pragma unroll
       for (int c = 0; c < N / 2; ++c) {
         uint32_t v = reinterpret_cast<const uint32_t*>(p)[c];
-        out[2 * c] = __uint_as_float(v << 16);
-        out[2 * c + 1] = __uint_as_float(v & 0xffff0000u);
+        out[2 * c] = lo16<DT>(v);
+        out[2 * c + 1] = hi16<DT>(v);
       }
     }
   }
 }
 
-// Store N fp32 values as storage dtype DT (bf16: round to nearest even).
+// Store N fp32 values as storage dtype DT (bf16, fp16: round to nearest even).
 template <int DT, int N>
 __device__ __forceinline__ void store_f32(stor_t<DT>* __restrict__ p, const float (&in)[N]) {
   if constexpr (DT == 0) {
@@ -98,14 +126,12 @@ __device__ __forceinline__ void store_f32(stor_t<DT>* __restrict__ p, const floa
       for (int e = 0; e < N; ++e) p[e] = in[e];
     }
   } else if constexpr (N == 1) {
-    p[0] = f32_to_bf16(in[0]);
+    p[0] = from_f32<DT>(in[0]);
   } else {
-    static_assert(N % 2 == 0, "bf16 vector width");
+    static_assert(N % 2 == 0, "16-bit vector width");
     uint32_t w[N / 2];
 #pragma unroll
-    for (int e = 0; e < N / 2; ++e)
-      w[e] = static_cast<uint32_t>(f32_to_bf16(in[2 * e])) |
-             (static_cast<uint32_t>(f32_to_bf16(in[2 * e + 1])) << 16);
+    for (int e = 0; e < N / 2; ++e) w[e] = pack2<DT>(in[2 * e], in[2 * e + 1]);
     if constexpr (N % 8 == 0) {
 #pragma unroll
       for (int c = 0; c < N / 8; ++c)

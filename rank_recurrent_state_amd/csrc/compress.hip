@@ -769,6 +769,10 @@ KFn pick_c(int dt, bool diag, size_t* lds) {
     *lds = compress_lds_bytes<DK, 1>();
     return diag ? k_compress<DK, DV, 1, true> : k_compress<DK, DV, 1, false>;
   }
+  if (dt == SEED_F16) {
+    *lds = compress_lds_bytes<DK, 2>();
+    return diag ? k_compress<DK, DV, 2, true> : k_compress<DK, DV, 2, false>;
+  }
   *lds = compress_lds_bytes<DK, 0>();
   return diag ? k_compress<DK, DV, 0, true> : k_compress<DK, DV, 0, false>;
 }
@@ -785,6 +789,7 @@ KFn pick_compress(const seed_shape& sh, size_t* lds) {
 template <int DK, int DV>
 KFn pick_f(int dt, size_t* lds) {
   if (dt == SEED_BF16) { *lds = FD<DK, DV, 1>::LDS; return k_from_dense<DK, DV, 1>; }
+  if (dt == SEED_F16) { *lds = FD<DK, DV, 2>::LDS; return k_from_dense<DK, DV, 2>; }
   *lds = FD<DK, DV, 0>::LDS;
   return k_from_dense<DK, DV, 0>;
 }

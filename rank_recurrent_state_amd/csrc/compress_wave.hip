@@ -1,5 +1,5 @@
 // Compression back to rank r, one wavefront per unit, with the core matrices in registers
-// (bf16 factors, r <= 32, r + T <= 64).
+// (16-bit factors, bf16 or fp16, r <= 32, r + T <= 64).
 //
 // Method: pages titled "Shallow Encoding Emits Deep Memories" (SEED architecture: every T
 // steps the rank r + T factors are truncated back to rank r by a Gram / QR step and a truncated
@@ -17,7 +17,8 @@
 // half of tile (I, 0) with the lower half of tile (I, 1) leaves every lane with its own column;
 // for a symmetric matrix that is its row.
 //
-//   Grams                 MFMA 32x32x16 bf16 straight from the stored columns (fp32 sums);
+//   Grams                 MFMA 32x32x16 bf16 (fp16) straight from the stored columns (fp32
+//                         sums);
 //   pivoted Cholesky      no row swaps: the L column of step s lands in column p_s of its LDS
 //                         copy, so L is held as L P^T (the core below is permuted alike,
 //                         which changes neither its eigenvalues nor X_V);
@@ -30,7 +31,8 @@
 //                         modified Gram-Schmidt, back-transformation by the reflectors;
 //   X_V, V', U'           MFMA 32x32x2 fp32 (the rows of a factor tile interleaved, d = NT i +
 //                         I, so that each lane loads NT consecutive elements of a column);
-//                         W = V_s^T V' by MFMA 32x32x16 bf16 on the rounded V' that is stored,
+//                         W = V_s^T V' by MFMA 32x32x16 bf16 (fp16) on the rounded V' that is
+//                         stored,
 //                         so that U' = M V' / sigma holds for the stored pair.
 // LDS holds L (N x (N + 1) fp32) and a few vectors: about 19.5 KB for N = 64, so eight units
 // share a CU (two waves per SIMD), and 6 KB for N = 32 (three waves per SIMD).
@@ -55,6 +57,24 @@ constexpr float kReduceFloor = 1e-30f;  // squared column norm below which no re
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// MFMA 32x32x16 over the 16-bit factor format (1 = bf16, 2 = fp16), fp32 accumulation.
+template <int FDT> struct Mf16;
+template <> struct Mf16<1> {
+  using V8 = bf16x8;
+  using E = __bf16;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mf16<2> {
+  using V8 = f16x8;
+  using E = _Float16;
+  static __device__ __forceinline__ f32x16 mfma(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
 
 // A 64 x 64 matrix held one row per lane: register c of lane i is element (i, c), kept in two
 // local 32-wide vectors NAME_lo, NAME_hi. The index is a compile-time constant after unrolling
@@ -238,10 +258,6 @@ __device__ __forceinline__ void tile_to_kops(const f32x16& acc, int I, float (&o
   }
 }
 
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
-
 template <int N>
 struct Smem {
   alignas(16) float Lp[N * (N + 1)];  // row stride N + 1 (odd: row and column reads both conflict-free)
@@ -259,8 +275,10 @@ struct Smem {
 
 // Gram of the stored columns 0..m-1 (rows of length D, bf16), as row-per-lane registers. With
 // ROWSCALE the A operand carries gam^2 along d (KDA's per-channel lazy decay).
-template <int D, bool ROWSCALE, int N>
+template <int D, bool ROWSCALE, int N, int FDT>
 __device__ __forceinline__ M64 gram(const uint16_t* __restrict__ base, const int m, const float* __restrict__ gam) {
+  using MF = Mf16<FDT>;
+  using V8 = typename MF::V8;
   const int lane = threadIdx.x;
   const int c0 = lane & 31, kh = lane >> 5;
   const bool ok0 = c0 < m, ok1 = N == 64 && c0 + 32 < m;
@@ -274,22 +292,22 @@ __device__ __forceinline__ M64 gram(const uint16_t* __restrict__ base, const int
     if constexpr (N == 64) u1 = *reinterpret_cast<const uint4*>(p1 + k0);
     if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
     if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
-    const bf16x8 b0 = __builtin_bit_cast(bf16x8, u0);
-    const bf16x8 b1 = __builtin_bit_cast(bf16x8, u1);
-    bf16x8 a0 = b0, a1 = b1;
+    const V8 b0 = __builtin_bit_cast(V8, u0);
+    const V8 b1 = __builtin_bit_cast(V8, u1);
+    V8 a0 = b0, a1 = b1;
     if constexpr (ROWSCALE) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float gj = gam[k0 + 8 * kh + j];
-        a0[j] = static_cast<__bf16>(static_cast<float>(b0[j]) * gj * gj);
-        a1[j] = static_cast<__bf16>(static_cast<float>(b1[j]) * gj * gj);
+        a0[j] = static_cast<typename MF::E>(static_cast<float>(b0[j]) * gj * gj);
+        a1[j] = static_cast<typename MF::E>(static_cast<float>(b1[j]) * gj * gj);
       }
     }
-    t[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, t[0][0], 0, 0, 0);
+    t[0][0] = MF::mfma(a0, b0, t[0][0]);
     if constexpr (N == 64) {
-      t[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, t[0][1], 0, 0, 0);
-      t[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, t[1][0], 0, 0, 0);
-      t[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, t[1][1], 0, 0, 0);
+      t[0][1] = MF::mfma(a0, b1, t[0][1]);
+      t[1][0] = MF::mfma(a1, b0, t[1][0]);
+      t[1][1] = MF::mfma(a1, b1, t[1][1]);
     }
   }
   return tiles_to_rows<N>(t);
@@ -323,7 +341,7 @@ __device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, con
 // of tile I is d = NT i + I, so that one lane's A operands of a column are NT consecutive
 // elements (one load per K-step). Output: y[I][j] is Y[d][lane % 32] with
 // d = NT (8 (j / 4) + 4 (lane / 32) + j % 4) + I.
-template <int D, int N>
+template <int D, int N, int FDT>
 __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, const int m, const float (&xop)[N / 2],
                                              f32x16 (&y)[D / 32]) {
   constexpr int NT = D / 32;
@@ -350,7 +368,7 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
 #pragma unroll
     for (int I = 0; I < NT; ++I) {
       const uint32_t wi = w[I >> 1];
-      const float a = __uint_as_float((I & 1) ? (wi & 0xffff0000u) : (wi << 16));
+      const float a = (I & 1) ? hi16<FDT>(wi) : lo16<FDT>(wi);
       y[I] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xop[s], y[I], 0, 0, 0);
     }
   }
@@ -379,7 +397,7 @@ __device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float
 
 }  // namespace cw
 
-template <int DK, int DV, bool DIAG, int N>
+template <int DK, int DV, bool DIAG, int N, int FDT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 : 3))) void k_compress_wave(const CompressArgs A) {
   using namespace cw;
   static_assert(N == 64 || N == 32, "core width");
@@ -427,8 +445,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        acc[0] = fmaf(cj[i], __uint_as_float(w[i] << 16), acc[0]);
-        if constexpr (EPL == 2) acc[1] = fmaf(cj[i], __uint_as_float(w[i] & 0xffff0000u), acc[1]);
+        acc[0] = fmaf(cj[i], lo16<FDT>(w[i]), acc[0]);
+        if constexpr (EPL == 2) acc[1] = fmaf(cj[i], hi16<FDT>(w[i]), acc[1]);
       }
     }
     float* __restrict__ ap = A.a + unit * DK + d0;
@@ -440,8 +458,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   // ---- Grams of the stored columns -------------------------------------------------------------
   f32x32 GU_lo, GU_hi, GV_lo, GV_hi;
   {
-    const M64 gu = gram<DK, DIAG, N>(Ub, m, S.gam);
-    const M64 gv = gram<DV, false, N>(Vb, m, nullptr);
+    const M64 gu = gram<DK, DIAG, N, FDT>(Ub, m, S.gam);
+    const M64 gv = gram<DV, false, N, FDT>(Vb, m, nullptr);
     GU_lo = gu.lo; GU_hi = gu.hi; GV_lo = gv.lo; GV_hi = gv.hi;
   }
 
@@ -885,11 +903,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   uint32_t vw[16 * NV / 2];
   {
     f32x16 vt[NV];
-    factor_times<DV, N>(Vb, m, xop, vt);
+    factor_times<DV, N, FDT>(Vb, m, xop, vt);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
 #pragma unroll
-      for (int e = 0; e < NV / 2; ++e) vw[j * NV / 2 + e] = pack2(vt[2 * e][j], vt[2 * e + 1][j]);
+      for (int e = 0; e < NV / 2; ++e) vw[j * NV / 2 + e] = pack2<FDT>(vt[2 * e][j], vt[2 * e + 1][j]);
     }
   }
   {
@@ -906,10 +924,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
       if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
       const uint4 bw4 = make_uint4(vw[4 * s], vw[4 * s + 1], vw[4 * s + 2], vw[4 * s + 3]);
-      const bf16x8 bop = __builtin_bit_cast(bf16x8, bw4);
-      w[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u0), bop, w[0], 0, 0, 0);
-      if constexpr (N == 64)
-        w[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u1), bop, w[1], 0, 0, 0);
+      using MF = Mf16<FDT>;
+      using V8 = typename MF::V8;
+      const V8 bop = __builtin_bit_cast(V8, bw4);
+      w[0] = MF::mfma(__builtin_bit_cast(V8, u0), bop, w[0]);
+      if constexpr (N == 64) w[1] = MF::mfma(__builtin_bit_cast(V8, u1), bop, w[1]);
     }
     // X_U = diag(colsc) W lambda^(-1/2) (U' = U_s D_c V_s^T V' / sigma), as B operands
 #pragma unroll
@@ -930,7 +949,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   uint32_t uw[16 * NU / 2];
   {
     f32x16 ut[NU];
-    factor_times<DK, N>(Ub, m, xop, ut);
+    factor_times<DK, N, FDT>(Ub, m, xop, ut);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int i = 8 * (j >> 2) + 4 * h + (j & 3);
@@ -942,7 +961,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
         for (int I = 0; I < NU; ++I) g[I] = S.gam[NU * i + I];
       }
 #pragma unroll
-      for (int e = 0; e < NU / 2; ++e) uw[j * NU / 2 + e] = pack2(ut[2 * e][j] * g[2 * e], ut[2 * e + 1][j] * g[2 * e + 1]);
+      for (int e = 0; e < NU / 2; ++e) uw[j * NU / 2 + e] = pack2<FDT>(ut[2 * e][j] * g[2 * e], ut[2 * e + 1][j] * g[2 * e + 1]);
     }
   }
 
@@ -968,19 +987,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
 namespace {
 using WaveFn = void (*)(const CompressArgs);
 
-template <int N>
+template <int N, int FDT>
 WaveFn pick_width(const seed_shape& sh) {
   const bool diag = sh.kind == SEED_KDA;
-  if (sh.d_k == 128 && sh.d_v == 128) return diag ? k_compress_wave<128, 128, true, N> : k_compress_wave<128, 128, false, N>;
-  if (sh.d_k == 128 && sh.d_v == 64) return diag ? k_compress_wave<128, 64, true, N> : k_compress_wave<128, 64, false, N>;
-  if (sh.d_k == 64 && sh.d_v == 128) return diag ? k_compress_wave<64, 128, true, N> : k_compress_wave<64, 128, false, N>;
-  if (sh.d_k == 64 && sh.d_v == 64) return diag ? k_compress_wave<64, 64, true, N> : k_compress_wave<64, 64, false, N>;
+  if (sh.d_k == 128 && sh.d_v == 128)
+    return diag ? k_compress_wave<128, 128, true, N, FDT> : k_compress_wave<128, 128, false, N, FDT>;
+  if (sh.d_k == 128 && sh.d_v == 64)
+    return diag ? k_compress_wave<128, 64, true, N, FDT> : k_compress_wave<128, 64, false, N, FDT>;
+  if (sh.d_k == 64 && sh.d_v == 128)
+    return diag ? k_compress_wave<64, 128, true, N, FDT> : k_compress_wave<64, 128, false, N, FDT>;
+  if (sh.d_k == 64 && sh.d_v == 64)
+    return diag ? k_compress_wave<64, 64, true, N, FDT> : k_compress_wave<64, 64, false, N, FDT>;
   return nullptr;
 }
 
+template <int FDT>
+WaveFn pick_format(const seed_shape& sh) {
+  return sh.rank + sh.period <= 32 ? pick_width<32, FDT>(sh) : pick_width<64, FDT>(sh);
+}
+
+// 16-bit factors (bf16, fp16) with r <= 32
 WaveFn pick_compress_wave(const seed_shape& sh) {
-  if (sh.factor_dtype != SEED_BF16 || sh.rank > cw::RX || sh.rank + sh.period > 64) return nullptr;
-  return sh.rank + sh.period <= 32 ? pick_width<32>(sh) : pick_width<64>(sh);
+  if (sh.rank > cw::RX || sh.rank + sh.period > 64) return nullptr;
+  if (sh.factor_dtype == SEED_BF16) return pick_format<1>(sh);
+  if (sh.factor_dtype == SEED_F16) return pick_format<2>(sh);
+  return nullptr;
 }
 }  // namespace
 

@@ -69,8 +69,8 @@ __device__ __forceinline__ void unpack16(const uint4& r, float (&out)[VF]) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      out[2 * e] = __uint_as_float(w[e] << 16);
-      out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      out[2 * e] = lo16<FDT>(w[e]);
+      out[2 * e + 1] = hi16<FDT>(w[e]);
     }
   }
 }
@@ -83,13 +83,15 @@ __device__ __forceinline__ uint4 pack16(const float (&in)[VF]) {
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = static_cast<uint32_t>(f32_to_bf16(in[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(in[2 * e + 1])) << 16);
+      w[e] = pack2<FDT>(in[2 * e], in[2 * e + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
-// KDA: a channel's cumulative gate below this is folded into the stored factors (2^-40).
-constexpr float kFoldFloor = 9.094947e-13f;
+// KDA: a channel's cumulative gate below this is folded into the stored factors: 2^-40 for
+// fp32 and bf16 storage, 2^-12 for fp16, whose range (65504) must hold kappa / Gamma.
+template <int FDT>
+constexpr float kFoldFloor = FDT == 2 ? 2.44140625e-4f : 9.094947e-13f;
 
 // ---- transposed sums ---------------------------------------------------------------------------
 // A lane holds N partial sums, each to be summed over a group of lanes. Rather than reducing
@@ -289,7 +291,7 @@ void k_decode(const StepArgs A) {
 #pragma unroll
     for (int e = 0; e < VF; ++e) {
       Gn[e] = alpha[e] * Gm[e];  // Gamma <- alpha . Gamma
-      tiny |= !(Gn[e] >= kFoldFloor);
+      tiny |= !(Gn[e] >= kFoldFloor<FDT>);
     }
     if (__ballot(tiny) != 0) {
       // A channel whose Gamma fell below the floor (a zero gate included) is folded into the
@@ -299,7 +301,7 @@ void k_decode(const StepArgs A) {
       float f[VF];
 #pragma unroll
       for (int e = 0; e < VF; ++e) {
-        const bool fold = !(Gn[e] >= kFoldFloor);
+        const bool fold = !(Gn[e] >= kFoldFloor<FDT>);
         f[e] = fold ? Gn[e] : 1.f;
         Gn[e] = fold ? 1.f : Gn[e];
       }
@@ -487,34 +489,38 @@ namespace {
 
 using DecodeFn = void (*)(const StepArgs);
 
-template <int KIND, int DK, int DV, int DT>
+template <int KIND, int DK, int DV, int FDT, int IDT>
 DecodeFn pick_cols(int slots) {
-  if (slots <= 32) return k_decode<KIND, DK, DV, DT, DT, 32>;
-  return k_decode<KIND, DK, DV, DT, DT, 64>;
+  if (slots <= 32) return k_decode<KIND, DK, DV, FDT, IDT, 32>;
+  return k_decode<KIND, DK, DV, FDT, IDT, 64>;
 }
 
+// factor / input dtypes: fp32 / fp32, bf16 / bf16, fp16 / bf16
 template <int KIND, int DK, int DV>
-DecodeFn pick_dt(int dt, int slots) {
-  return dt == SEED_BF16 ? pick_cols<KIND, DK, DV, 1>(slots) : pick_cols<KIND, DK, DV, 0>(slots);
+DecodeFn pick_dt(int fdt, int idt, int slots) {
+  if (fdt == SEED_F32 && idt == SEED_F32) return pick_cols<KIND, DK, DV, 0, 0>(slots);
+  if (fdt == SEED_BF16 && idt == SEED_BF16) return pick_cols<KIND, DK, DV, 1, 1>(slots);
+  if (fdt == SEED_F16 && idt == SEED_BF16) return pick_cols<KIND, DK, DV, 2, 1>(slots);
+  return nullptr;
 }
 
 template <int KIND>
-DecodeFn pick_dims(int dk, int dv, int dt, int slots) {
-  if (dk == 128 && dv == 128) return pick_dt<KIND, 128, 128>(dt, slots);
-  if (dk == 128 && dv == 64) return pick_dt<KIND, 128, 64>(dt, slots);
-  if (dk == 64 && dv == 128) return pick_dt<KIND, 64, 128>(dt, slots);
-  if (dk == 64 && dv == 64) return pick_dt<KIND, 64, 64>(dt, slots);
+DecodeFn pick_dims(int dk, int dv, int fdt, int idt, int slots) {
+  if (dk == 128 && dv == 128) return pick_dt<KIND, 128, 128>(fdt, idt, slots);
+  if (dk == 128 && dv == 64) return pick_dt<KIND, 128, 64>(fdt, idt, slots);
+  if (dk == 64 && dv == 128) return pick_dt<KIND, 64, 128>(fdt, idt, slots);
+  if (dk == 64 && dv == 64) return pick_dt<KIND, 64, 64>(fdt, idt, slots);
   return nullptr;
 }
 
 DecodeFn pick_decode(const seed_shape& sh) {
-  if (sh.factor_dtype != sh.io_dtype) return nullptr;
   const int slots = sh.rank + sh.period;
   if (slots > 64) return nullptr;
+  const int f = sh.factor_dtype, i = sh.io_dtype;
   switch (sh.kind) {
-    case SEED_GDN: return pick_dims<SEED_GDN>(sh.d_k, sh.d_v, sh.factor_dtype, slots);
-    case SEED_KDA: return pick_dims<SEED_KDA>(sh.d_k, sh.d_v, sh.factor_dtype, slots);
-    case SEED_MAMBA2: return pick_dims<SEED_MAMBA2>(sh.d_k, sh.d_v, sh.factor_dtype, slots);
+    case SEED_GDN: return pick_dims<SEED_GDN>(sh.d_k, sh.d_v, f, i, slots);
+    case SEED_KDA: return pick_dims<SEED_KDA>(sh.d_k, sh.d_v, f, i, slots);
+    case SEED_MAMBA2: return pick_dims<SEED_MAMBA2>(sh.d_k, sh.d_v, f, i, slots);
     default: return nullptr;
   }
 }

@@ -29,7 +29,7 @@ import numpy as np
 
 GDN, KDA, MAMBA2 = 0, 1, 2
 KIND_NAMES = {GDN: "gdn", KDA: "kda", MAMBA2: "mamba2"}
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -61,7 +61,7 @@ class Workload:
     def describe(self) -> str:
         kind = KIND_NAMES[self.kind]
         lay = f"{self.layers} layers x " if self.layers > 1 else ""
-        dt = "bf16" if self.factor_dtype == BF16 else "fp32"
+        dt = {F32: "fp32", BF16: "bf16", F16: "fp16"}[self.factor_dtype]
         return (f"{kind} {lay}{self.heads} heads x batch {self.batch}, d_k={self.d_k} d_v={self.d_v}, "
                 f"r={self.rank} T={self.period}, {self.steps} steps, {dt} factors, "
                 f"prefill {self.prefill} tokens")
@@ -218,7 +218,7 @@ class DeviceStream:
 
 
 def bytes_of(dtype_code: int) -> int:
-    return 2 if dtype_code == BF16 else 4
+    return 4 if dtype_code == F32 else 2
 
 
 def ceil_div(a: int, b: int) -> int:
@@ -226,7 +226,7 @@ def ceil_div(a: int, b: int) -> int:
 
 
 __all__ = [
-    "GDN", "KDA", "MAMBA2", "F32", "BF16", "Workload", "WORKLOADS", "HeadConsts", "head_consts",
+    "GDN", "KDA", "MAMBA2", "F32", "BF16", "F16", "Workload", "WORKLOADS", "HeadConsts", "head_consts",
     "step_inputs", "sequence", "round_bf16", "DeviceStream", "rng", "bytes_of", "ceil_div",
     "unit_heads",
     "KIND_NAMES",

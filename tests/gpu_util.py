@@ -15,7 +15,7 @@ import synth
 
 def torch_dtype(code):
     import torch
-    return torch.bfloat16 if code == synth.BF16 else torch.float32
+    return {synth.F32: torch.float32, synth.BF16: torch.bfloat16, synth.F16: torch.float16}[code]
 
 
 def shape_of(w: synth.Workload, batch=None, heads=None, units_layers=1):
@@ -87,12 +87,20 @@ def rel_out(o_gpu, o_ref, S_ref, q) -> float:
 
 
 def tolerance(w_or_dtype) -> float:
+    """Relative tolerance by factor storage: about five units of the format's rounding (bf16
+    2^-8, fp16 2^-11), and 1e-5 for fp32 factors."""
     code = w_or_dtype.factor_dtype if hasattr(w_or_dtype, "factor_dtype") else w_or_dtype
-    return 2e-2 if code == synth.BF16 else 1e-5
+    return {synth.F32: 1e-5, synth.BF16: 2e-2, synth.F16: 2.5e-3}[code]
+
+
+def out_tolerance(w) -> float:
+    """Tolerance of a read-out o: o is stored in the io dtype, so it is held to the looser of the
+    factor and io formats' tolerances (fp16 factors come with bf16 inputs and outputs)."""
+    return max(tolerance(w.factor_dtype), tolerance(w.io_dtype))
 
 
 def near_tie_threshold(code) -> float:
-    return 5e-2 if code == synth.BF16 else 1e-3
+    return {synth.F32: 1e-3, synth.BF16: 5e-2, synth.F16: 1e-2}[code]
 
 
 def compare_compression(C_before, a, vbar, U_gpu, V_gpu, r, code, a_ref=None):

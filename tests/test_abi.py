@@ -42,6 +42,10 @@ def test_size_queries():
     kda = rrs.make_shape(rrs.SEED_KDA, 2, 2, 128, 128, 32, 32, rrs.SEED_F32)
     assert rrs.seed_scale_len(kda) == 128 + 32
     assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 160
+    # fp16 factors take the bytes of bf16 ones; their default inputs are bf16
+    f16 = rrs.make_shape(rrs.SEED_GDN, 64, 16, 128, 128, 16, 16, rrs.SEED_F16)
+    assert f16.io_dtype == rrs.SEED_BF16
+    assert rrs.seed_state_bytes(f16) == rrs.seed_state_bytes(sh)
     assert rrs.seed_workspace_bytes(sh, rrs.SEED_OP_COMPRESS) == 0
     assert rrs.seed_workspace_bytes(sh, rrs.SEED_OP_FROM_DENSE) == 0
     assert rrs.seed_from_dense_iterations() >= 1
@@ -103,6 +107,12 @@ def test_invalid_arguments_are_rejected_on_the_host():
     # mixed factor / io dtypes are not compiled for the decode step
     mixed = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16, rrs.SEED_F32)
     assert decode(mixed, 16) == rrs.SEED_ERR_UNSUPPORTED
+    # fp16 is a factor format: fp16 inputs, and fp16 factors with fp32 inputs, are not compiled
+    f16_io = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16, rrs.SEED_F16)
+    assert decode(f16_io, 16) == rrs.SEED_ERR_UNSUPPORTED
+    f16_f32 = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_F16, rrs.SEED_F32)
+    assert decode(f16_f32, 16) == rrs.SEED_ERR_UNSUPPORTED
+    assert decode(rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, 3, 3), 16) == rrs.SEED_ERR_ARG
     st = _FakeState(rrs)
     with pytest.raises(rrs.SeedError) as e:
         rrs.seed_compress(sh, st, 33, stream=0)

@@ -5,20 +5,23 @@ the prefill-end compression, a full compression window of decode steps, the comp
 two more decode steps. The fp64 oracle checks a seeded sample of units call by call
 (teacher-forced: it starts each call from the GPU's own state), with the first and last unit
 always in the sample. Inputs are drawn on the device by the same seeded generators as the
-benchmark's. gdn-stack36 is checked on one layer (4,096 units): a benchmark launch.
+benchmark's. gdn-stack36 is checked on one layer (4,096 units): a benchmark launch, with its
+bf16 factors and again with fp16 factors (bf16 inputs).
 """
 from __future__ import annotations
+
+import dataclasses
 
 import numpy as np
 import pytest
 
 import synth
-from gpu_util import (check_compress_call, check_decode_call, check_from_dense_call, tolerance,
-                      torch_dtype)
+from gpu_util import (check_compress_call, check_decode_call, check_from_dense_call, out_tolerance,
+                      tolerance, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["gdn-layer", "kda-layer", "mamba2-layer", "gdn-stack36"]
+FULL = ["gdn-layer", "kda-layer", "mamba2-layer", "gdn-stack36", "gdn-stack36:fp16"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -28,7 +31,10 @@ def test_full_size_sampled(name):
         pytest.skip("no GPU")
     import rank_recurrent_state_amd as rrs
 
+    name, _, fmt = name.partition(":")
     w = synth.WORKLOADS[name]
+    if fmt == "fp16":
+        w = dataclasses.replace(w, factor_dtype=synth.F16)
     units = w.batch * w.heads
     seed = 3000 + sorted(synth.WORKLOADS).index(name)
     sh = rrs.make_shape(w.kind, w.batch, w.heads, w.d_k, w.d_v, w.rank, w.period, w.factor_dtype,
@@ -38,6 +44,7 @@ def test_full_size_sampled(name):
     vbar = ds.vbar(0)
     vbar_np = vbar.double().cpu().numpy()
     tol = tolerance(w)
+    tol_o = out_tolerance(w)
     rng = np.random.default_rng(seed)
     sample = sorted({0, units - 1, *rng.choice(units, size=10, replace=False).tolist()})
     print(f"\n[{name}] {units} units, prefill {w.prefill}, sample {sample}", flush=True)
@@ -60,7 +67,7 @@ def test_full_size_sampled(name):
         x = ds.step(io)
         eS, eo = check_decode_call(rrs, sh, st, m, x, vbar, vbar_np, w.heads, sample, o)
         worst_S, worst_o = max(worst_S, eS), max(worst_o, eo)
-        assert eS <= tol and eo <= tol, f"{name} decode step {t}: S {eS} o {eo}"
+        assert eS <= tol and eo <= tol_o, f"{name} decode step {t}: S {eS} o {eo}"
         m += 1
         if m == w.rank + w.period:
             ec, ties = check_compress_call(rrs, sh, st, m, vbar_np, w.heads, sample, w.factor_dtype)
