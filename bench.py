@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--workload", default="gdn-stack36")
     ap.add_argument("--factor-dtype", choices=["fp32", "bf16", "fp16"], default=None,
                     help="factor storage other than the workload's own (fp16: with bf16 inputs)")
+    ap.add_argument("--rounding", choices=["nearest", "stochastic"], default="nearest",
+                    help="rounding of the 16-bit factor stores")
     ap.add_argument("--pool", type=int, default=64, help="steps of resident inputs, cycled")
     ap.add_argument("--dense-steps", type=int, default=32, help="timed dense-baseline steps")
     ap.add_argument("--prefill", type=int, default=None, help="override the prefill length")
@@ -170,10 +172,15 @@ def main():
     torch_dt = {synth.F32: torch.float32, synth.BF16: torch.bfloat16, synth.F16: torch.float16}
     io = torch_dt[w.io_dtype]
     fdt = torch_dt[w.factor_dtype]
-    sh = rrs.make_shape(w.kind, w.batch, w.heads, w.d_k, w.d_v, w.rank, w.period,
-                        w.factor_dtype, w.io_dtype)
+    rnd = rrs.SEED_ROUND_STOCHASTIC if args.rounding == "stochastic" else rrs.SEED_ROUND_NEAREST
+    # stochastic rounding's keys: the per-layer launches index units from 0 in every layer, so
+    # each layer takes its own key; the stack-wide compression indexes all units at once
+    sh_l = [rrs.make_shape(w.kind, w.batch, w.heads, w.d_k, w.d_v, w.rank, w.period,
+                           w.factor_dtype, w.io_dtype, rounding=rnd, rng_key=args.seed * 1000 + l)
+            for l in range(L)]
+    sh = sh_l[0]
     sh_all = rrs.make_shape(w.kind, w.batch * L, w.heads, w.d_k, w.d_v, w.rank, w.period,
-                            w.factor_dtype, w.io_dtype)
+                            w.factor_dtype, w.io_dtype, rounding=rnd, rng_key=args.seed * 1000 + L)
     log(f"[bench] {w.describe()}; {N} units ({L} launches of {U1} per step); {rrs.seed_version()}")
 
     if args.copy_calibration:
@@ -209,7 +216,7 @@ def main():
     vbars = [ds.vbar(l) for l in range(L)]
     t0 = time.time()
     for l in range(L):
-        rrs.seed_state_from_dense(sh, S[l * U1:(l + 1) * U1], vbars[l], states[l])
+        rrs.seed_state_from_dense(sh_l[l], S[l * U1:(l + 1) * U1], vbars[l], states[l])
         if L > 1 and (l + 1) % 6 == 0:
             torch.cuda.synchronize()
             log(f"[bench] prefill-end compression {l + 1}/{L} layers ({time.time() - t0:.1f} s)")
@@ -254,7 +261,7 @@ def main():
             xl = pool[wi * T + j]
             for l in range(L):
                 x = xl[l]
-                rrs.seed_decode_step(sh, states[l], w.rank + j, x["q"], x["k"], x["v"], x["beta"],
+                rrs.seed_decode_step(sh_l[l], states[l], w.rank + j, x["q"], x["k"], x["v"], x["beta"],
                                      x["g"], vbars[l], o[l])
 
     # Every layer reaches r + T columns on the same step, and the layers' states are contiguous,
@@ -265,7 +272,7 @@ def main():
     def enqueue_compress():
         if args.compress_per_layer:
             for l in range(L):
-                rrs.seed_compress(sh, states[l], w.rank + T)
+                rrs.seed_compress(sh_l[l], states[l], w.rank + T)
         else:
             rrs.seed_compress(sh_all, state_all, w.rank + T)
 
@@ -396,9 +403,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.describe()}", "units": N, "launch_units": U1,
                    "layers": L, "factor_storage": {synth.F32: "fp32", synth.BF16: "bf16", synth.F16: "fp16"}[w.factor_dtype],
-                   "prefill_tokens": prefill},
+                   "prefill_tokens": prefill, "rounding": args.rounding},
         "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name) if args.factor_dtype is None else None,
+                     "frac": dec_gbs / HBM_PEAK_GBS, "traffic": (recorded_traffic(w.name)
+                                 if args.factor_dtype is None and args.rounding == "nearest" else None),
                      "kernel": "k_decode (factored read-out + update)",
                      "bytes_per_launch": dec_bytes / n_dec_launch,
                      "avg_launch_us": avg_launch_us},

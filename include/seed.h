@@ -46,6 +46,19 @@
  *     channel's cumulative gate into the stored columns once it falls below 2^-12 (2^-40 for
  *     the other formats), so that the stored key kappa / Gamma stays within fp16's range;
  *     values beyond that range (65504) are not checked and become infinities.
+ *   - Rounding. rounding selects how the 16-bit factor stores round (the appendix table on number
+ *     formats and rounding measures both): SEED_ROUND_NEAREST (nearest, ties to even) or
+ *     SEED_ROUND_STOCHASTIC, which rounds x away from zero with probability equal to its
+ *     fractional distance f between the format's two neighbouring values: exactly when the
+ *     element's 16-bit draw r satisfies r < 65536 f. The draws come from Philox4x32-10 (Salmon et
+ *     al., SC'11) with key (rng_key, 0) and counter (element / 8, site << 16 | aux << 8 | slot,
+ *     unit, window); element e of the group of 8 takes half e % 2 of output word (e % 8) / 2.
+ *     site: 0 the decode step's U column, 1 its V column, 2 / 3 a compression's U' / V',
+ *     4 / 5 the prefill-end U / V, 6 a KDA gate fold rewriting a U column during the decode step
+ *     with m columns (aux = m; 0 elsewhere). unit is the index within the call's own batch, and
+ *     window the unit's compression-window count (below), so that every store of a trajectory
+ *     draws fresh bits; states that share unit indices and windows (layers, say) should take
+ *     different keys. Stochastic rounding with fp32 factors is SEED_ERR_ARG.
  *   - Supported shapes: d_k, d_v in {64, 128}; rank >= 1, period >= 1, rank + period <= 64.
  *     Other shapes return SEED_ERR_UNSUPPORTED.
  */
@@ -69,6 +82,7 @@ enum {
 
 enum { SEED_GDN = 0, SEED_KDA = 1, SEED_MAMBA2 = 2 };
 enum { SEED_F32 = 0, SEED_BF16 = 1, SEED_F16 = 2 };
+enum { SEED_ROUND_NEAREST = 0, SEED_ROUND_STOCHASTIC = 1 };
 enum { SEED_OP_COMPRESS = 0, SEED_OP_FROM_DENSE = 1 };
 
 typedef struct seed_shape {
@@ -78,6 +92,8 @@ typedef struct seed_shape {
   int32_t rank, period;  /* r and T: compression back to r columns every T steps             */
   int32_t factor_dtype;  /* SEED_F32, SEED_BF16 or SEED_F16: storage of U and V              */
   int32_t io_dtype;      /* SEED_F32 or SEED_BF16: storage of q, k, v and o                  */
+  int32_t rounding;      /* SEED_ROUND_NEAREST or SEED_ROUND_STOCHASTIC: factor stores        */
+  uint32_t rng_key;      /* key of the stochastic-rounding draws (ignored when nearest)       */
 } seed_shape;
 
 /*
@@ -86,8 +102,9 @@ typedef struct seed_shape {
  *   a      float [units][d_k]      sink at the last compression (a_0).
  *   U      [units][C][d_k]         slot j holds column j of U, contiguous over d_k (factor_dtype).
  *   V      [units][C][d_v]         slot j holds column j of V, contiguous over d_v (factor_dtype).
- *   scale  float [units][s]        s = s0 + T: the lazy decay of U (scale[0 .. s0)), so that U is
- *          never rewritten by a decay, then the sink coefficients c (scale[s0 .. s0 + T)):
+ *   scale  float [units][s]        s = s0 + T + 1: the lazy decay of U (scale[0 .. s0)), so that U
+ *          is never rewritten by a decay, then the sink coefficients c (scale[s0 .. s0 + T)), then
+ *          the compression-window count (scale[s0 + T], the bits of a uint32):
  *            GDN, Mamba-2: the true column j of U is scale[0] * U[j] for j < r and
  *              scale[1 + j - r] * U[j] for j >= r; the true sink is
  *              a_true = scale[0] * a + sum_{r <= j < m} c[j - r] * U_true[:, j].
@@ -95,7 +112,8 @@ typedef struct seed_shape {
  *              U[j], for every j; a_true = scale[0 .. d_k) . (a + sum_{r <= j < m} c[j - r] U[j]).
  *          The sink is thus kept lazily like the decay: a decode step appends the new column's
  *          coefficient instead of rewriting a. seed_state_from_dense and seed_compress leave
- *          a = a_true, the decay scales at 1 and the coefficients at 0.
+ *          a = a_true, the decay scales at 1 and the coefficients at 0; seed_state_from_dense
+ *          sets the window count to 0 and every compression that runs adds one.
  * The true state is a_true vbar^T + sum_{j<m} U_true[:, j] V[:, j]^T.
  */
 typedef struct seed_state {

@@ -14,7 +14,8 @@ import importlib
 _NAMES = {
     "EXPORTS", "LIB_PATH", "SEED_BF16", "SEED_ERR_ARG", "SEED_ERR_HIP", "SEED_ERR_UNSUPPORTED",
     "SEED_ERR_WORKSPACE", "SEED_F16", "SEED_F32", "SEED_GDN", "SEED_KDA", "SEED_MAMBA2", "SEED_OK",
-    "SEED_OP_COMPRESS", "SEED_OP_FROM_DENSE", "SeedError", "State", "make_shape",
+    "SEED_OP_COMPRESS", "SEED_OP_FROM_DENSE", "SEED_ROUND_NEAREST", "SEED_ROUND_STOCHASTIC",
+    "SeedError", "State", "make_shape",
     "seed_compress", "seed_decode_step", "seed_dense_decode_step", "seed_from_dense_iterations",
     "seed_scale_len", "seed_shape", "seed_state", "seed_state_bytes", "seed_state_from_dense",
     "seed_status_string", "seed_version", "seed_workspace_bytes",

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libseed.so")
 SEED_OK, SEED_ERR_ARG, SEED_ERR_UNSUPPORTED, SEED_ERR_WORKSPACE, SEED_ERR_HIP = 0, -1, -2, -3, -4
 SEED_GDN, SEED_KDA, SEED_MAMBA2 = 0, 1, 2
 SEED_F32, SEED_BF16, SEED_F16 = 0, 1, 2
+SEED_ROUND_NEAREST, SEED_ROUND_STOCHASTIC = 0, 1
 SEED_OP_COMPRESS, SEED_OP_FROM_DENSE = 0, 1
 
 EXPORTS = [
@@ -29,7 +30,8 @@ class seed_shape(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("period", ctypes.c_int32), ("factor_dtype", ctypes.c_int32),
-                ("io_dtype", ctypes.c_int32)]
+                ("io_dtype", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("rng_key", ctypes.c_uint32)]
 
     @property
     def units(self) -> int:
@@ -81,12 +83,14 @@ LIB = _load()
 
 
 def make_shape(kind: int, batch: int, heads: int, d_k: int, d_v: int, rank: int, period: int,
-               factor_dtype: int = SEED_F32, io_dtype: int | None = None) -> seed_shape:
+               factor_dtype: int = SEED_F32, io_dtype: int | None = None,
+               rounding: int = SEED_ROUND_NEAREST, rng_key: int = 0) -> seed_shape:
     """A seed_shape; io_dtype defaults to the factor dtype (bf16 for fp16 factors, the one
     input format compiled with them)."""
     if io_dtype is None:
         io_dtype = SEED_BF16 if factor_dtype == SEED_F16 else factor_dtype
-    return seed_shape(kind, batch, heads, d_k, d_v, rank, period, factor_dtype, io_dtype)
+    return seed_shape(kind, batch, heads, d_k, d_v, rank, period, factor_dtype, io_dtype, rounding,
+                      rng_key & 0xFFFFFFFF)
 
 
 def _stream_ptr(stream):
@@ -147,7 +151,7 @@ class State:
         U = torch.zeros((n, shape.slots, shape.d_k), dtype=fdt, device=device)
         V = torch.zeros((n, shape.slots, shape.d_v), dtype=fdt, device=device)
         scale = torch.ones((n, seed_scale_len(shape)), dtype=torch.float32, device=device)
-        scale[:, seed_scale_len(shape) - shape.period:] = 0.0  # sink coefficients
+        scale[:, seed_scale_len(shape) - shape.period - 1:] = 0.0  # sink coefficients, window count
         return cls(a, U, V, scale)
 
     def tensors(self):

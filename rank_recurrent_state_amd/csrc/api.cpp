@@ -23,6 +23,9 @@ int check_shape(const seed_shape* sh) {
   if (sh->batch <= 0 || sh->heads <= 0 || sh->d_k <= 0 || sh->d_v <= 0) return SEED_ERR_ARG;
   if (sh->rank <= 0 || sh->period <= 0) return SEED_ERR_ARG;
   if (!dtype_ok(sh->factor_dtype) || !dtype_ok(sh->io_dtype)) return SEED_ERR_ARG;
+  if (sh->rounding != SEED_ROUND_NEAREST && sh->rounding != SEED_ROUND_STOCHASTIC) return SEED_ERR_ARG;
+  // stochastic rounding applies to the 16-bit factor formats
+  if (sh->rounding == SEED_ROUND_STOCHASTIC && sh->factor_dtype == SEED_F32) return SEED_ERR_ARG;
   if (sh->io_dtype == SEED_F16) return SEED_ERR_UNSUPPORTED;  // fp16 is a factor format only
   if (!dim_ok(sh->d_k) || !dim_ok(sh->d_v)) return SEED_ERR_UNSUPPORTED;
   if (sh->rank + sh->period > 64) return SEED_ERR_UNSUPPORTED;
@@ -38,7 +41,8 @@ int32_t coef_off(const seed_shape* sh) {
   return sh->kind == SEED_KDA ? sh->d_k : 1 + sh->period;
 }
 
-int32_t scale_len(const seed_shape* sh) { return coef_off(sh) + sh->period; }
+// decay scales, T sink coefficients, then the compression-window count
+int32_t scale_len(const seed_shape* sh) { return coef_off(sh) + sh->period + 1; }
 
 bool state_ok(const seed_state* st) {
   return st && st->a && st->U && st->V && st->scale;
@@ -55,6 +59,9 @@ seed::CompressArgs compress_args(const seed_shape* sh, const seed_state* st, int
   a.slots = sh->rank + sh->period;
   a.scale_len = scale_len(sh);
   a.coef_off = coef_off(sh);
+  a.win_off = coef_off(sh) + sh->period;
+  a.rounding = sh->rounding;
+  a.rng_key = sh->rng_key;
   a.a = st->a;
   a.U = st->U;
   a.V = st->V;
@@ -119,6 +126,9 @@ int seed_decode_step(const seed_shape* sh, const seed_state* st, int32_t m, cons
   a.slots = sh->rank + sh->period;
   a.scale_len = scale_len(sh);
   a.coef_off = coef_off(sh);
+  a.win_off = coef_off(sh) + sh->period;
+  a.rounding = sh->rounding;
+  a.rng_key = sh->rng_key;
   a.a = st->a;
   a.U = st->U;
   a.V = st->V;

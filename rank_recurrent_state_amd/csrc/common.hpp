@@ -146,6 +146,95 @@ __device__ __forceinline__ void store_f32(stor_t<DT>* __restrict__ p, const floa
   }
 }
 
+// ---- stochastic rounding ------------------------------------------------------------------------
+// Random bits: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+// 1, 2, 3", SC'11): ten rounds, each two 32 x 32 -> 64-bit products of counter words 0 and 2 with
+// the round multipliers, the halves recombined with words 1 and 3 and the key; the key is bumped
+// by the Weyl increments between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u, kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i > 0) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint32_t hi0 = __umulhi(kM0, c.x), lo0 = kM0 * c.x;
+    const uint32_t hi1 = __umulhi(kM1, c.z), lo1 = kM1 * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Store sites of the factors (part of the random-number counter).
+enum SrSite : uint32_t {
+  kSiteDecodeU = 0, kSiteDecodeV = 1, kSiteCompressU = 2, kSiteCompressV = 3,
+  kSiteFromDenseU = 4, kSiteFromDenseV = 5, kSiteFoldU = 6
+};
+
+// The Philox output of one group of eight consecutive elements of a stored column: key
+// (rng_key, 0), counter (element / 8, site << 16 | aux << 8 | slot, unit, window count).
+__device__ __forceinline__ uint4 sr_group(uint32_t rng_key, uint32_t site, uint32_t aux, int slot, int64_t unit,
+                                          uint32_t window, int elem) {
+  const uint4 c = make_uint4(static_cast<uint32_t>(elem) >> 3, (site << 16) | (aux << 8) | static_cast<uint32_t>(slot),
+                             static_cast<uint32_t>(unit), window);
+  return philox4x32_10(c, rng_key, 0u);
+}
+
+// The 16-bit draw of element e (0..7) of a group: half (e % 2) of word e / 2.
+__device__ __forceinline__ uint32_t draw16(const uint4& w, int e) {
+  const uint32_t x = (e >> 1) == 0 ? w.x : ((e >> 1) == 1 ? w.y : ((e >> 1) == 2 ? w.z : w.w));
+  return (e & 1) ? (x >> 16) : (x & 0xffffu);
+}
+
+// Stochastic rounding of x to the 16-bit format DT with the draw r (0 .. 65535): the neighbour
+// away from zero is taken exactly when r < 65536 f, f the fractional distance of x from its
+// neighbour towards zero. Every step below is exact in fp32.
+template <int DT> __device__ __forceinline__ uint16_t round_sr(float x, uint32_t r);
+template <> __device__ __forceinline__ uint16_t round_sr<1>(float x, uint32_t r) {
+  // bf16 is the upper half of the fp32 encoding: f = (low half) / 65536
+  const uint32_t b = __float_as_uint(x);
+  return static_cast<uint16_t>((b >> 16) + (r < (b & 0xffffu) ? 1u : 0u));
+}
+template <> __device__ __forceinline__ uint16_t round_sr<2>(float x, uint32_t r) {
+  // the neighbour towards zero by the round-towards-zero conversion, the other one a unit of
+  // the last place further out (65504 rounds to itself: its outer neighbour is the infinity)
+  const auto h2 = __builtin_amdgcn_cvt_pkrtz(x, 0.f);
+  const uint16_t lo = __builtin_bit_cast(uint16_t, h2[0]);
+  const float flo = static_cast<float>(h2[0]);
+  const float fhi = f16_to_f32(static_cast<uint16_t>(lo + 1u));
+  const float d = fabsf(x) - fabsf(flo);             // exact (the two are within a factor 2)
+  const float span = fabsf(fhi) - fabsf(flo);        // a power of two, or infinite
+  return (static_cast<float>(r) * span < d * 65536.f) ? static_cast<uint16_t>(lo + 1u) : lo;
+}
+
+// Store N fp32 values as the 16-bit format DT with stochastic rounding; r[e] is element e's draw.
+template <int DT, int N>
+__device__ __forceinline__ void store_sr(stor_t<DT>* __restrict__ p, const float (&in)[N], const uint32_t (&r)[N]) {
+  static_assert(DT == 1 || DT == 2, "stochastic rounding stores 16-bit formats");
+  if constexpr (N == 1) {
+    p[0] = round_sr<DT>(in[0], r[0]);
+  } else {
+    static_assert(N % 2 == 0, "16-bit vector width");
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int e = 0; e < N / 2; ++e)
+      w[e] = static_cast<uint32_t>(round_sr<DT>(in[2 * e], r[2 * e])) |
+             (static_cast<uint32_t>(round_sr<DT>(in[2 * e + 1], r[2 * e + 1])) << 16);
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 8; ++c)
+        reinterpret_cast<uint4*>(p)[c] = make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
+    } else if constexpr (N % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < N / 4; ++c) reinterpret_cast<uint2*>(p)[c] = make_uint2(w[2 * c], w[2 * c + 1]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < N / 2; ++c) reinterpret_cast<uint32_t*>(p)[c] = w[c];
+    }
+  }
+}
+
 // ---- cross-lane sums -------------------------------------------------------------------------
 // DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
 // row_half_mirror (i <-> 7 - i inside 8 lanes), row_mirror (i <-> 15 - i inside 16 lanes).

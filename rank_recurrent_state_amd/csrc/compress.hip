@@ -356,11 +356,30 @@ __device__ void gram_rows(Core<CT>& S, const stor_t<FDT>* __restrict__ base, con
   __syncthreads();
 }
 
+// How the factor stores of one call round: nearest-even, or stochastic with draws for the
+// store site (element e of column c of the unit takes its draw from the group e / 8).
+struct Rounding {
+  bool sr;
+  uint32_t key;
+  uint32_t site;
+  int64_t unit;
+  uint32_t window;
+};
+
+template <int FDT>
+__device__ __forceinline__ stor_t<FDT> round_store(float x, const Rounding& R, int col, int elem) {
+  if constexpr (FDT != 0) {
+    if (R.sr) return round_sr<FDT>(x, draw16(sr_group(R.key, R.site, 0u, col, R.unit, R.window, elem), elem & 7));
+  }
+  return from_f32<FDT>(x);
+}
+
 // Reconstruction: out[c][i] = post_i * sum_{a<n} st[a][i] * X[a][c] for c < r, with the n
 // source rows of length D staged in S.LM..S.YM (n * D <= 2 * MX * LD values).
 template <typename CT, int D, int FDT, bool ROWSCALE>
 __device__ void reconstruct_rows(Core<CT>& S, const CT* __restrict__ X, const int n, const int r,
-                                 const float* __restrict__ post, stor_t<FDT>* __restrict__ out) {
+                                 const float* __restrict__ post, stor_t<FDT>* __restrict__ out,
+                                 const Rounding& R) {
   const int t = threadIdx.x;
   constexpr int NCS = 256 / D;
   const int i = t % D, cset = t / D;
@@ -369,7 +388,7 @@ __device__ void reconstruct_rows(Core<CT>& S, const CT* __restrict__ X, const in
     CT acc = CT(0);
     for (int a = 0; a < n; ++a) acc += st[a * D + i] * X[a * LD + c];
     if constexpr (ROWSCALE) acc *= CT(post[i]);
-    out[static_cast<int64_t>(c) * D + i] = from_f32<FDT>(static_cast<float>(acc));
+    out[static_cast<int64_t>(c) * D + i] = round_store<FDT>(static_cast<float>(acc), R, c, i);
   }
 }
 
@@ -389,6 +408,10 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
   FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(C) * DK;
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
   float* __restrict__ sc = A.scale + unit * A.scale_len;
+  // the unit's compression-window count (stochastic rounding's counter; one more at the end)
+  const uint32_t window = __float_as_uint(sc[A.win_off]);
+  const Rounding RU{A.rounding != 0, A.rng_key, kSiteCompressU, unit, window};
+  const Rounding RV{A.rounding != 0, A.rng_key, kSiteCompressV, unit, window};
 
   // lazy decay: per-column scales (GDN, Mamba-2) or per-channel Gamma (KDA)
   if constexpr (DIAG) {
@@ -431,7 +454,7 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
     S.LM[a * DK + i] = CT(to_f32<FDT>(Ub[static_cast<int64_t>(S.perm[a]) * DK + i]));
   }
   __syncthreads();
-  reconstruct_rows<CT, DK, FDT, DIAG>(S, S.GB, k, r, gam, Ub);
+  reconstruct_rows<CT, DK, FDT, DIAG>(S, S.GB, k, r, gam, Ub, RU);
   __syncthreads();
   // V' = V X_V
   for (int idx = t; idx < m * DV; idx += 256) {
@@ -439,9 +462,10 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
     S.LM[j * DV + i] = CT(to_f32<FDT>(Vb[static_cast<int64_t>(j) * DV + i]));
   }
   __syncthreads();
-  reconstruct_rows<CT, DV, FDT, false>(S, S.GA, m, r, nullptr, Vb);
-  // decay scales back to 1, sink coefficients to 0
-  for (int i = t; i < A.scale_len; i += 256) sc[i] = i < A.coef_off ? 1.f : 0.f;
+  reconstruct_rows<CT, DV, FDT, false>(S, S.GA, m, r, nullptr, Vb, RV);
+  // decay scales back to 1, sink coefficients to 0, the window count one up
+  for (int i = t; i < A.scale_len; i += 256)
+    sc[i] = i < A.coef_off ? 1.f : (i < A.win_off ? 0.f : __uint_as_float(window + 1u));
 }
 
 template <int DK, int FDT>
@@ -708,6 +732,9 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
 
   core_truncate(S, M, r);
   const int k = S.kk;
+  // the first window (count 0)
+  const Rounding RU{A.rounding != 0, A.rng_key, kSiteFromDenseU, unit, 0u};
+  const Rounding RV{A.rounding != 0, A.rng_key, kSiteFromDenseV, unit, 0u};
 
   if constexpr (L::UC) {
     // U'[c][i] = sum_a C[i][perm[a]] X_U[a][c]; V'[c][j] = X_V[j][c]
@@ -719,11 +746,11 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
         const int j = S.perm[a];
         acc += CT(Sd[i * DV + j] - ai * svb[j]) * S.GB[a * LD + c];
       }
-      Ub[static_cast<int64_t>(c) * DK + i] = from_f32<FDT>(static_cast<float>(acc));
+      Ub[static_cast<int64_t>(c) * DK + i] = round_store<FDT>(static_cast<float>(acc), RU, c, i);
     }
     for (int c = t / DV; c < r; c += 256 / DV) {
       const int j = t % DV;
-      Vb[static_cast<int64_t>(c) * DV + j] = from_f32<FDT>(static_cast<float>(S.GA[j * LD + c]));
+      Vb[static_cast<int64_t>(c) * DV + j] = round_store<FDT>(static_cast<float>(S.GA[j * LD + c]), RV, c, j);
     }
   } else if constexpr (L::VC) {
     // U'[c][perm[a]] = X_U[a][c] (zero on non-pivot rows); V'[c][j] = sum_i C[i][j] X_V[i][c]
@@ -732,13 +759,13 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
       CT val = CT(0);
       for (int a = 0; a < k; ++a)
         if (S.perm[a] == i) val = S.GB[a * LD + c];
-      Ub[static_cast<int64_t>(c) * DK + i] = from_f32<FDT>(static_cast<float>(val));
+      Ub[static_cast<int64_t>(c) * DK + i] = round_store<FDT>(static_cast<float>(val), RU, c, i);
     }
     for (int c = t / DV; c < r; c += 256 / DV) {
       const int j = t % DV;
       CT acc = CT(0);
       for (int i = 0; i < DK; ++i) acc += CT(Sd[i * DV + j] - sa[i] * svb[j]) * S.GA[i * LD + c];
-      Vb[static_cast<int64_t>(c) * DV + j] = from_f32<FDT>(static_cast<float>(acc));
+      Vb[static_cast<int64_t>(c) * DV + j] = round_store<FDT>(static_cast<float>(acc), RV, c, j);
     }
   } else {
     // U'[c][i] = sum_a Z[perm[a]][i] X_U[a][c]; V'[c][j] = sum_b X[b][j] X_V[b][c]
@@ -746,15 +773,16 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
       const int i = t % DK;
       CT acc = CT(0);
       for (int a = 0; a < k; ++a) acc += CT(Z[S.perm[a] * L::LDZ + i]) * S.GB[a * LD + c];
-      Ub[static_cast<int64_t>(c) * DK + i] = from_f32<FDT>(static_cast<float>(acc));
+      Ub[static_cast<int64_t>(c) * DK + i] = round_store<FDT>(static_cast<float>(acc), RU, c, i);
     }
     for (int c = t / DV; c < r; c += 256 / DV) {
       const int j = t % DV;
       CT acc = CT(0);
       for (int b = 0; b < M; ++b) acc += CT(X[b * L::LDX + j]) * S.GA[b * LD + c];
-      Vb[static_cast<int64_t>(c) * DV + j] = from_f32<FDT>(static_cast<float>(acc));
+      Vb[static_cast<int64_t>(c) * DV + j] = round_store<FDT>(static_cast<float>(acc), RV, c, j);
     }
   }
+  // decay scales 1, sink coefficients 0, window count 0
   float* __restrict__ sc = A.scale + unit * A.scale_len;
   for (int i = t; i < A.scale_len; i += 256) sc[i] = i < A.coef_off ? 1.f : 0.f;
 }

@@ -411,6 +411,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   uint16_t* __restrict__ Ub = reinterpret_cast<uint16_t*>(A.U) + unit * static_cast<int64_t>(C) * DK;
   uint16_t* __restrict__ Vb = reinterpret_cast<uint16_t*>(A.V) + unit * static_cast<int64_t>(C) * DV;
   float* __restrict__ sc = A.scale + unit * A.scale_len;
+  // the unit's compression-window count (stochastic rounding's counter; one more at the end)
+  const uint32_t window = __float_as_uint(sc[A.win_off]);
+  const bool sr = A.rounding != 0;
 
   // ---- column scales (lazy decay), KDA's channel scales ----------------------------------------
   float csc;
@@ -904,10 +907,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   {
     f32x16 vt[NV];
     factor_times<DV, N, FDT>(Vb, m, xop, vt);
+    // elements d = NV i + (0 .. NV - 1) of column c32, i = 8 (j / 4) + 4 h + j % 4: the 8 / NV
+    // values of j from a multiple of 8 / NV share one group of 8 (one draw call)
+    uint4 dr = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
+      const int d0 = NV * (8 * (j >> 2) + 4 * h + (j & 3));
+      if (sr && j % (8 / NV) == 0) dr = sr_group(A.rng_key, kSiteCompressV, 0u, c32, unit, window, d0);
 #pragma unroll
-      for (int e = 0; e < NV / 2; ++e) vw[j * NV / 2 + e] = pack2<FDT>(vt[2 * e][j], vt[2 * e + 1][j]);
+      for (int e = 0; e < NV / 2; ++e) {
+        const float x0 = vt[2 * e][j], x1 = vt[2 * e + 1][j];
+        vw[j * NV / 2 + e] = sr ? (static_cast<uint32_t>(round_sr<FDT>(x0, draw16(dr, (d0 + 2 * e) & 7))) |
+                                   (static_cast<uint32_t>(round_sr<FDT>(x1, draw16(dr, (d0 + 2 * e + 1) & 7))) << 16))
+                                : pack2<FDT>(x0, x1);
+      }
     }
   }
   {
@@ -945,27 +958,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     }
   }
 
-  // ---- U' = U_s X_U (d_k x r) (KDA: rows times Gamma) ---------------------------------------------
-  uint32_t uw[16 * NU / 2];
-  {
-    f32x16 ut[NU];
-    factor_times<DK, N, FDT>(Ub, m, xop, ut);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int i = 8 * (j >> 2) + 4 * h + (j & 3);
-      float g[NU];
-#pragma unroll
-      for (int I = 0; I < NU; ++I) g[I] = 1.f;
-      if constexpr (DIAG) {
-#pragma unroll
-        for (int I = 0; I < NU; ++I) g[I] = S.gam[NU * i + I];
-      }
-#pragma unroll
-      for (int e = 0; e < NU / 2; ++e) uw[j * NU / 2 + e] = pack2<FDT>(ut[2 * e][j] * g[2 * e], ut[2 * e + 1][j] * g[2 * e + 1]);
-    }
-  }
-
-  // ---- write the r kept columns (every read of U_s and V_s is above) ------------------------------
+  // ---- write the r kept columns of V' (V_s is not read again: its last reads fed W, whose
+  // MFMAs waited for them); its registers are then free for U' ------------------------------------
+  __builtin_amdgcn_sched_barrier(0);
   if (c32 < r) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -974,14 +969,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
         *reinterpret_cast<uint2*>(Vb + c32 * DV + NV * i) = make_uint2(vw[2 * j], vw[2 * j + 1]);
       else
         *reinterpret_cast<uint32_t*>(Vb + c32 * DV + NV * i) = vw[j];
+    }
+  }
+
+  // ---- U' = U_s X_U (d_k x r) (KDA: rows times Gamma) ---------------------------------------------
+  uint32_t uw[16 * NU / 2];
+  {
+    f32x16 ut[NU];
+    factor_times<DK, N, FDT>(Ub, m, xop, ut);
+    uint4 dr = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = 8 * (j >> 2) + 4 * h + (j & 3);
+      const int d0 = NU * i;
+      if (sr && j % (8 / NU) == 0) dr = sr_group(A.rng_key, kSiteCompressU, 0u, c32, unit, window, d0);
+      float g[NU];
+#pragma unroll
+      for (int I = 0; I < NU; ++I) g[I] = 1.f;
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int I = 0; I < NU; ++I) g[I] = S.gam[NU * i + I];
+      }
+#pragma unroll
+      for (int e = 0; e < NU / 2; ++e) {
+        const float x0 = ut[2 * e][j] * g[2 * e], x1 = ut[2 * e + 1][j] * g[2 * e + 1];
+        uw[j * NU / 2 + e] = sr ? (static_cast<uint32_t>(round_sr<FDT>(x0, draw16(dr, (d0 + 2 * e) & 7))) |
+                                   (static_cast<uint32_t>(round_sr<FDT>(x1, draw16(dr, (d0 + 2 * e + 1) & 7))) << 16))
+                                : pack2<FDT>(x0, x1);
+      }
+    }
+  }
+
+  // ---- write the r kept columns of U' (every read of U_s is above) -------------------------------
+  __builtin_amdgcn_sched_barrier(0);
+  if (c32 < r) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int i = 8 * (j >> 2) + 4 * h + (j & 3);
       if constexpr (NU == 4)
         *reinterpret_cast<uint2*>(Ub + c32 * DK + NU * i) = make_uint2(uw[2 * j], uw[2 * j + 1]);
       else
         *reinterpret_cast<uint32_t*>(Ub + c32 * DK + NU * i) = uw[j];
     }
   }
-  // decay scales restart at 1, sink coefficients at 0
-  for (int i = lane; i < A.scale_len; i += 64) sc[i] = i < A.coef_off ? 1.f : 0.f;
+  // decay scales restart at 1, sink coefficients at 0, the window count goes one up
+  for (int i = lane; i < A.scale_len; i += 64)
+    sc[i] = i < A.coef_off ? 1.f : (i < A.win_off ? 0.f : __uint_as_float(window + 1u));
 }
 
 namespace {

@@ -88,6 +88,44 @@ __device__ __forceinline__ uint4 pack16(const float (&in)[VF]) {
   }
 }
 
+// Store N consecutive elements (elem0 .. elem0 + N - 1, inside one group of 8) of a factor
+// column: nearest-even, or, with sr, stochastic rounding drawn for that site, slot and unit.
+template <int FDT, int N>
+__device__ __forceinline__ void store_factor(stor_t<FDT>* __restrict__ p, const float (&x)[N], bool sr,
+                                             uint32_t key, uint32_t site, uint32_t aux, int slot, int64_t unit,
+                                             uint32_t window, int elem0) {
+  if constexpr (FDT == 0) {
+    store_f32<0, N>(p, x);
+  } else {
+    if (sr) {
+      const uint4 w = sr_group(key, site, aux, slot, unit, window, elem0);
+      uint32_t rr[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) rr[e] = draw16(w, (elem0 + e) & 7);
+      store_sr<FDT, N>(p, x, rr);
+    } else {
+      store_f32<FDT, N>(p, x);
+    }
+  }
+}
+
+// One 16-byte slice (VF elements from elem0, inside one group of 8 for 16-bit formats) of a factor
+// column, rounded as store_factor does.
+template <int FDT, int VF>
+__device__ __forceinline__ uint4 pack_factor(const float (&x)[VF], bool sr, uint32_t key, uint32_t site, uint32_t aux,
+                                             int slot, int64_t unit, uint32_t window, int elem0) {
+  if constexpr (FDT != 0) {
+    if (sr) {
+      const uint4 w = sr_group(key, site, aux, slot, unit, window, elem0);
+      uint32_t h[VF];
+#pragma unroll
+      for (int e = 0; e < VF; ++e) h[e] = round_sr<FDT>(x[e], draw16(w, (elem0 + e) & 7));
+      return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    }
+  }
+  return pack16<FDT, VF>(x);
+}
+
 // KDA: a channel's cumulative gate below this is folded into the stored factors: 2^-40 for
 // fp32 and bf16 storage, 2^-12 for fp16, whose range (65504) must hold kappa / Gamma.
 template <int FDT>
@@ -267,6 +305,9 @@ void k_decode(const StepArgs A) {
   // the lazy sink: a_0 (decayed like slot 0; KDA: by Gamma) plus c_j times each window column
   load_f32<0, VF>(A.a + unit * DK + uo, av);
   const float cw = (jt >= r && jt < m) ? sc[A.coef_off + jt - r] : 0.f;
+  // stochastic rounding of the stores (16-bit factors): the unit's compression-window count
+  const bool sr = FDT != 0 && A.rounding != 0;
+  const uint32_t window = sr ? __float_as_uint(sc[A.win_off]) : 0u;
 
   __builtin_amdgcn_sched_barrier(0);
 
@@ -312,8 +353,10 @@ void k_decode(const StepArgs A) {
         unpack16<FDT, VF>(ur[i], u);
 #pragma unroll
         for (int e = 0; e < VF; ++e) u[e] *= f[e];
-        if (j < m) store_f32<FDT, VF>(Ub + static_cast<int64_t>(j) * DK + uo, u);
-        ur[i] = pack16<FDT, VF>(u);
+        // the U pass below uses exactly the rewritten bits
+        ur[i] = pack_factor<FDT, VF>(u, sr, A.rng_key, kSiteFoldU, static_cast<uint32_t>(m), j, unit, window, uo);
+        if (j < m) *reinterpret_cast<uint4*>(Ub + static_cast<int64_t>(j) * DK + uo) = ur[i];
+        __builtin_amdgcn_sched_barrier(0);  // one column at a time (keeps the draws' registers few)
       }
       // a_0 carries the same per-channel factor as the stored columns
 #pragma unroll
@@ -321,12 +364,16 @@ void k_decode(const StepArgs A) {
       if (ug == 0) store_f32<0, VF>(A.a + unit * DK + uo, av);
     }
     // the new U column kappa / Gamma and Gamma itself do not depend on the passes: written now
-    // (the U pass reads only the columns before m), their registers are free for the U pass
+    // (the U pass reads only the columns before m), their registers are free for the U pass.
+    // With stochastic rounding the column is written at the end instead, where the draws do not
+    // compete with the factor loads for registers.
     if (ug == 0) {
-      float nu[VF];
+      if (!sr) {
+        float nu[VF];
 #pragma unroll
-      for (int e = 0; e < VF; ++e) nu[e] = kt[e] / Gn[e];
-      store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
+        for (int e = 0; e < VF; ++e) nu[e] = kt[e] / Gn[e];
+        store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
+      }
       store_f32<0, VF>(sc + uo, Gn);
     }
     float pkq = 0.f, pka = 0.f, paq = 0.f;
@@ -351,7 +398,8 @@ void k_decode(const StepArgs A) {
 #pragma unroll
         for (int e = 0; e < VF; ++e) nu[e] = kt[e];
       }
-      store_f32<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu);
+      store_factor<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu, sr, A.rng_key, kSiteDecodeU, 0u, m, unit,
+                            window, uo);
     }
     col_scale *= gs;
     float kv[VF], qv[VF];
@@ -480,8 +528,22 @@ void k_decode(const StepArgs A) {
     w[e] = beta * (DELTA ? (eps - accx[e]) : eps);
     o[e] = vb[e] * aq + accy[e] + s * w[e];
   }
-  store_f32<FDT, NB>(Vb + static_cast<int64_t>(m) * DV + ve, w);
+  store_factor<FDT, NB>(Vb + static_cast<int64_t>(m) * DV + ve, w, sr, A.rng_key, kSiteDecodeV, 0u, m, unit, window,
+                        ve);
   store_f32<IDT, NB>(reinterpret_cast<IT*>(A.o) + unit * DV + ve, o);
+  if constexpr (DIAG && FDT != 0) {
+    // KDA with stochastic rounding: the new U column kappa / Gamma, from the key read again and
+    // the Gamma this lane stored above (the same quotients as the early store would take)
+    if (sr && ug == 0) {
+      float kk[VF], gg[VF], nu[VF];
+      load_f32<IDT, VF>(kp, kk);
+      load_f32<0, VF>(sc + uo, gg);
+#pragma unroll
+      for (int e = 0; e < VF; ++e) nu[e] = kk[e] / gg[e];
+      store_factor<FDT, VF>(Ub + static_cast<int64_t>(m) * DK + uo, nu, true, A.rng_key, kSiteDecodeU, 0u, m, unit,
+                            window, uo);
+    }
+  }
 }
 
 // ---- host-side dispatch ----------------------------------------------------------------------

@@ -14,8 +14,11 @@ struct StepArgs {
   int32_t m;          // columns held before the step
   int32_t rank;       // r
   int32_t slots;      // r + T: column slots per unit
-  int32_t scale_len;  // per-unit floats of the scale buffer: decay scales, then sink coefficients
+  int32_t scale_len;  // per-unit floats of the scale buffer: decay scales, sink coefficients, window count
   int32_t coef_off;   // where the T sink coefficients start: 1 + T (GDN, Mamba-2) or d_k (KDA)
+  int32_t win_off;    // the compression-window count (a uint32 in the float buffer): coef_off + T
+  int32_t rounding;   // 0: nearest-even factor stores; 1: stochastic
+  uint32_t rng_key;   // key of the stochastic-rounding draws
   float* a;
   void* U;
   void* V;
@@ -48,6 +51,9 @@ struct CompressArgs {
   int32_t slots;
   int32_t scale_len;
   int32_t coef_off;
+  int32_t win_off;
+  int32_t rounding;
+  uint32_t rng_key;
   float* a;
   void* U;
   void* V;

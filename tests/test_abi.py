@@ -35,13 +35,13 @@ def test_every_declared_symbol_is_exported():
 def test_size_queries():
     rrs = _lib()
     sh = rrs.make_shape(rrs.SEED_GDN, 64, 16, 128, 128, 16, 16, rrs.SEED_BF16)
-    # a (4 d_k) + U, V (2 bytes x 32 slots x (128 + 128)) + scale (4 ((1 + T) + T): decay scales,
-    # then the sink coefficients)
-    assert rrs.seed_state_bytes(sh) == 4 * 128 + 2 * 32 * 256 + 4 * 33
-    assert rrs.seed_scale_len(sh) == 33
+    # a (4 d_k) + U, V (2 bytes x 32 slots x (128 + 128)) + scale (4 ((1 + T) + T + 1): decay
+    # scales, the sink coefficients, the compression-window count)
+    assert rrs.seed_state_bytes(sh) == 4 * 128 + 2 * 32 * 256 + 4 * 34
+    assert rrs.seed_scale_len(sh) == 34
     kda = rrs.make_shape(rrs.SEED_KDA, 2, 2, 128, 128, 32, 32, rrs.SEED_F32)
-    assert rrs.seed_scale_len(kda) == 128 + 32
-    assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 160
+    assert rrs.seed_scale_len(kda) == 128 + 32 + 1
+    assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 161
     # fp16 factors take the bytes of bf16 ones; their default inputs are bf16
     f16 = rrs.make_shape(rrs.SEED_GDN, 64, 16, 128, 128, 16, 16, rrs.SEED_F16)
     assert f16.io_dtype == rrs.SEED_BF16
@@ -113,6 +113,10 @@ def test_invalid_arguments_are_rejected_on_the_host():
     f16_f32 = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_F16, rrs.SEED_F32)
     assert decode(f16_f32, 16) == rrs.SEED_ERR_UNSUPPORTED
     assert decode(rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, 3, 3), 16) == rrs.SEED_ERR_ARG
+    # rounding: an unknown mode, or stochastic rounding of fp32 factors, is an argument error
+    assert decode(rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16, rounding=2), 16) == rrs.SEED_ERR_ARG
+    assert decode(rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_F32,
+                                 rounding=rrs.SEED_ROUND_STOCHASTIC), 16) == rrs.SEED_ERR_ARG
     st = _FakeState(rrs)
     with pytest.raises(rrs.SeedError) as e:
         rrs.seed_compress(sh, st, 33, stream=0)
