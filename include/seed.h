@@ -102,9 +102,10 @@ typedef struct seed_shape {
  *   a      float [units][d_k]      sink at the last compression (a_0).
  *   U      [units][C][d_k]         slot j holds column j of U, contiguous over d_k (factor_dtype).
  *   V      [units][C][d_v]         slot j holds column j of V, contiguous over d_v (factor_dtype).
- *   scale  float [units][s]        s = s0 + T + 1: the lazy decay of U (scale[0 .. s0)), so that U
+ *   scale  float [units][s]        s = s0 + T + 2: the lazy decay of U (scale[0 .. s0)), so that U
  *          is never rewritten by a decay, then the sink coefficients c (scale[s0 .. s0 + T)), then
- *          the compression-window count (scale[s0 + T], the bits of a uint32):
+ *          the compression-window count (scale[s0 + T]) and the unit's column count m
+ *          (scale[s0 + T + 1]), both the bits of a uint32:
  *            GDN, Mamba-2: the true column j of U is scale[0] * U[j] for j < r and
  *              scale[1 + j - r] * U[j] for j >= r; the true sink is
  *              a_true = scale[0] * a + sum_{r <= j < m} c[j - r] * U_true[:, j].
@@ -113,7 +114,9 @@ typedef struct seed_shape {
  *          The sink is thus kept lazily like the decay: a decode step appends the new column's
  *          coefficient instead of rewriting a. seed_state_from_dense and seed_compress leave
  *          a = a_true, the decay scales at 1 and the coefficients at 0; seed_state_from_dense
- *          sets the window count to 0 and every compression that runs adds one.
+ *          sets the window count to 0 and every compression that runs adds one. Every call
+ *          keeps the column count: r after seed_state_from_dense and a compression, one more
+ *          after each decode step.
  * The true state is a_true vbar^T + sum_{j<m} U_true[:, j] V[:, j]^T.
  */
 typedef struct seed_state {
@@ -172,12 +175,28 @@ int32_t seed_from_dense_iterations(void);
  *          the stored columns first (that row of U is multiplied by it, the scale restarts at
  *          1, and a carries the same factor), so that the new column k / scale stays finite;
  *          the true state is unchanged.
- * Afterwards the caller holds m + 1 columns. Source: picx.dev summary, "Exact Update
- * (Lemma 2)" and "SEED Architecture".
+ * Afterwards the caller holds m + 1 columns (also recorded as every unit's column count in the
+ * state). Source: picx.dev summary, "Exact Update (Lemma 2)" and "SEED Architecture".
  */
 int seed_decode_step(const seed_shape *shape, const seed_state *state, int32_t m,
                      const void *q, const void *k, const void *v, const float *beta,
                      const float *g, const float *vbar, void *o, void *stream);
+
+/*
+ * The decode step for a ragged batch: every unit takes its own column count m from its state
+ * (see the scale buffer above), as requests that joined at different times hold different
+ * counts. A unit runs the step of seed_decode_step with that m, and its count goes one up, when
+ *   - active is NULL or active[u] != 0 (active: uint8 [units], device memory), and
+ *   - rank <= m < rank + period (a unit that holds rank + period columns is full: compress it
+ *     first, with seed_compress_ragged).
+ * Any other unit is left untouched and its row of o is not written. Arguments otherwise as for
+ * seed_decode_step. Source: the step of seed_decode_step; serving with a batch whose requests
+ * differ in length is the continuous batching of the pages' throughput section.
+ */
+int seed_decode_step_ragged(const seed_shape *shape, const seed_state *state,
+                            const uint8_t *active, const void *q, const void *k, const void *v,
+                            const float *beta, const float *g, const float *vbar, void *o,
+                            void *stream);
 
 /*
  * Compression of the content back to rank r (leaves m = r; nothing is done when m <= r).
@@ -196,6 +215,16 @@ int seed_decode_step(const seed_shape *shape, const seed_state *state, int32_t m
  */
 int seed_compress(const seed_shape *shape, const seed_state *state, int32_t m, void *ws,
                   size_t ws_bytes, void *stream);
+
+/*
+ * Compression of the units whose own column count m_u (from the state) satisfies
+ * m_u >= min_m, with rank < min_m <= rank + period: each is compressed as by seed_compress with
+ * m = m_u and left with count rank; the other units are not touched. min_m = rank + period
+ * compresses exactly the full units ("compress when full"), so that a ragged batch compresses
+ * each unit every period steps, on the step it fills. SEED_ERR_ARG for min_m outside that range.
+ */
+int seed_compress_ragged(const seed_shape *shape, const seed_state *state, int32_t min_m,
+                         void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Dense-state step (the uncompressed baseline): S <- the dense recurrence of `kind`, then

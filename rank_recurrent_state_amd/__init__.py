@@ -16,7 +16,8 @@ _NAMES = {
     "SEED_ERR_WORKSPACE", "SEED_F16", "SEED_F32", "SEED_GDN", "SEED_KDA", "SEED_MAMBA2", "SEED_OK",
     "SEED_OP_COMPRESS", "SEED_OP_FROM_DENSE", "SEED_ROUND_NEAREST", "SEED_ROUND_STOCHASTIC",
     "SeedError", "State", "make_shape",
-    "seed_compress", "seed_decode_step", "seed_dense_decode_step", "seed_from_dense_iterations",
+    "column_counts", "seed_compress", "seed_compress_ragged", "seed_decode_step",
+    "seed_decode_step_ragged", "seed_dense_decode_step", "seed_from_dense_iterations",
     "seed_scale_len", "seed_shape", "seed_state", "seed_state_bytes", "seed_state_from_dense",
     "seed_status_string", "seed_version", "seed_workspace_bytes",
 }

@@ -21,8 +21,8 @@ SEED_OP_COMPRESS, SEED_OP_FROM_DENSE = 0, 1
 
 EXPORTS = [
     "seed_state_bytes", "seed_scale_len", "seed_workspace_bytes", "seed_state_from_dense",
-    "seed_from_dense_iterations", "seed_decode_step", "seed_compress", "seed_dense_decode_step",
-    "seed_status_string", "seed_version",
+    "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
+    "seed_compress_ragged", "seed_dense_decode_step", "seed_status_string", "seed_version",
 ]
 
 
@@ -67,7 +67,9 @@ def _load():
         "seed_state_from_dense": (ctypes.c_int, [Sp, P, P, Stp, P, ctypes.c_size_t, P]),
         "seed_from_dense_iterations": (ctypes.c_int32, []),
         "seed_decode_step": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, P, P, P, P, P, P, P]),
+        "seed_decode_step_ragged": (ctypes.c_int, [Sp, Stp, P, P, P, P, P, P, P, P, P]),
         "seed_compress": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, ctypes.c_size_t, P]),
+        "seed_compress_ragged": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, ctypes.c_size_t, P]),
         "seed_dense_decode_step": (ctypes.c_int, [Sp, P, P, P, P, P, P, P, P]),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "seed_version": (ctypes.c_char_p, []),
@@ -151,7 +153,7 @@ class State:
         U = torch.zeros((n, shape.slots, shape.d_k), dtype=fdt, device=device)
         V = torch.zeros((n, shape.slots, shape.d_v), dtype=fdt, device=device)
         scale = torch.ones((n, seed_scale_len(shape)), dtype=torch.float32, device=device)
-        scale[:, seed_scale_len(shape) - shape.period - 1:] = 0.0  # sink coefficients, window count
+        scale[:, seed_scale_len(shape) - shape.period - 2:] = 0.0  # coefficients, window and column counts
         return cls(a, U, V, scale)
 
     def tensors(self):
@@ -222,6 +224,37 @@ def seed_decode_step(shape: seed_shape, state, m: int, q, k, v, beta, g, vbar, o
     _check("seed_decode_step", LIB.seed_decode_step(
         ctypes.byref(shape), _state_c(state), m, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
         _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_decode_step_ragged(shape: seed_shape, state, q, k, v, beta, g, vbar, o, active=None,
+                            stream=None) -> None:
+    """Every unit steps from its own column count (kept in the state); active (uint8 [units] on
+    the device, or None for all) masks units out."""
+    import torch
+    _expect_state(shape, state)
+    _expect_io(shape, q, k, v, beta, g, o)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    if active is not None and hasattr(active, "is_cuda"):
+        _expect("active", active, shape.units)
+        if active.dtype != torch.uint8:
+            raise ValueError(f"active: expected dtype torch.uint8, got {active.dtype}")
+    _check("seed_decode_step_ragged", LIB.seed_decode_step_ragged(
+        ctypes.byref(shape), _state_c(state), _ptr(active), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+        _ptr(g), _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_compress_ragged(shape: seed_shape, state, min_m: int, ws=None, stream=None) -> None:
+    """Compress the units whose own column count is >= min_m (min_m = r + T: the full ones)."""
+    _expect_state(shape, state)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("seed_compress_ragged", LIB.seed_compress_ragged(
+        ctypes.byref(shape), _state_c(state), min_m, _ptr(ws), ws_bytes, _stream_ptr(stream)))
+
+
+def column_counts(shape: seed_shape, state):
+    """Every unit's column count m, read from its state (a host-side int64 tensor)."""
+    import torch
+    return state.scale[:, seed_scale_len(shape) - 1].contiguous().view(torch.int32).long().cpu()
 
 
 def seed_compress(shape: seed_shape, state, m: int, ws=None, stream=None) -> None:

@@ -41,8 +41,8 @@ int32_t coef_off(const seed_shape* sh) {
   return sh->kind == SEED_KDA ? sh->d_k : 1 + sh->period;
 }
 
-// decay scales, T sink coefficients, then the compression-window count
-int32_t scale_len(const seed_shape* sh) { return coef_off(sh) + sh->period + 1; }
+// decay scales, T sink coefficients, the compression-window count, the column count
+int32_t scale_len(const seed_shape* sh) { return coef_off(sh) + sh->period + 2; }
 
 bool state_ok(const seed_state* st) {
   return st && st->a && st->U && st->V && st->scale;
@@ -60,8 +60,10 @@ seed::CompressArgs compress_args(const seed_shape* sh, const seed_state* st, int
   a.scale_len = scale_len(sh);
   a.coef_off = coef_off(sh);
   a.win_off = coef_off(sh) + sh->period;
+  a.m_off = a.win_off + 1;
   a.rounding = sh->rounding;
   a.rng_key = sh->rng_key;
+  a.ragged = 0;
   a.a = st->a;
   a.U = st->U;
   a.V = st->V;
@@ -70,6 +72,65 @@ seed::CompressArgs compress_args(const seed_shape* sh, const seed_state* st, int
   a.vbar = nullptr;
   a.iters = seed::from_dense_iterations();
   return a;
+}
+
+// The decode step's arguments; ragged calls take every unit's m from its state.
+seed::StepArgs step_args(const seed_shape* sh, const seed_state* st, int32_t m, const uint8_t* active,
+                         bool ragged) {
+  seed::StepArgs a{};
+  a.units = units_of(sh);
+  a.heads = sh->heads;
+  a.m = m;
+  a.rank = sh->rank;
+  a.slots = sh->rank + sh->period;
+  a.scale_len = scale_len(sh);
+  a.coef_off = coef_off(sh);
+  a.win_off = coef_off(sh) + sh->period;
+  a.m_off = a.win_off + 1;
+  a.rounding = sh->rounding;
+  a.rng_key = sh->rng_key;
+  a.ragged = ragged ? 1 : 0;
+  a.active = active;
+  a.a = st->a;
+  a.U = st->U;
+  a.V = st->V;
+  a.scale = st->scale;
+  return a;
+}
+
+int decode_call(const seed_shape* sh, const seed_state* st, int32_t m, const uint8_t* active, bool ragged,
+                const void* q, const void* k, const void* v, const float* beta, const float* g,
+                const float* vbar, void* o, void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st) || !q || !k || !v || !beta || !g || !vbar || !o) return SEED_ERR_ARG;
+  if (!ragged && (m < sh->rank || m >= sh->rank + sh->period)) return SEED_ERR_ARG;
+  if (!seed::decode_supported(*sh)) return SEED_ERR_UNSUPPORTED;
+  seed::StepArgs a = step_args(sh, st, m, active, ragged);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.vbar = vbar;
+  a.o = o;
+  return hip_status(seed::launch_decode(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
+int compress_call(const seed_shape* sh, const seed_state* st, int32_t m, bool ragged, void* ws,
+                  size_t ws_bytes, void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st)) return SEED_ERR_ARG;
+  if (ragged ? (m <= sh->rank || m > sh->rank + sh->period) : (m < 0 || m > sh->rank + sh->period))
+    return SEED_ERR_ARG;
+  if (ws_bytes < seed_workspace_bytes(sh, SEED_OP_COMPRESS)) return SEED_ERR_WORKSPACE;
+  (void)ws;
+  if (!seed::compress_supported(*sh)) return SEED_ERR_UNSUPPORTED;
+  if (!ragged && m <= sh->rank) return SEED_OK;
+  seed::CompressArgs a = compress_args(sh, st, m);
+  a.ragged = ragged ? 1 : 0;
+  return hip_status(seed::launch_compress(*sh, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -113,48 +174,23 @@ int seed_state_from_dense(const seed_shape* sh, const float* S, const float* vba
 int seed_decode_step(const seed_shape* sh, const seed_state* st, int32_t m, const void* q,
                      const void* k, const void* v, const float* beta, const float* g,
                      const float* vbar, void* o, void* stream) {
-  const int c = check_shape(sh);
-  if (c != SEED_OK) return c;
-  if (!state_ok(st) || !q || !k || !v || !beta || !g || !vbar || !o) return SEED_ERR_ARG;
-  if (m < sh->rank || m >= sh->rank + sh->period) return SEED_ERR_ARG;
-  if (!seed::decode_supported(*sh)) return SEED_ERR_UNSUPPORTED;
-  seed::StepArgs a{};
-  a.units = units_of(sh);
-  a.heads = sh->heads;
-  a.m = m;
-  a.rank = sh->rank;
-  a.slots = sh->rank + sh->period;
-  a.scale_len = scale_len(sh);
-  a.coef_off = coef_off(sh);
-  a.win_off = coef_off(sh) + sh->period;
-  a.rounding = sh->rounding;
-  a.rng_key = sh->rng_key;
-  a.a = st->a;
-  a.U = st->U;
-  a.V = st->V;
-  a.scale = st->scale;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.beta = beta;
-  a.g = g;
-  a.vbar = vbar;
-  a.o = o;
-  return hip_status(seed::launch_decode(*sh, a, static_cast<hipStream_t>(stream)));
+  return decode_call(sh, st, m, nullptr, false, q, k, v, beta, g, vbar, o, stream);
+}
+
+int seed_decode_step_ragged(const seed_shape* sh, const seed_state* st, const uint8_t* active,
+                            const void* q, const void* k, const void* v, const float* beta,
+                            const float* g, const float* vbar, void* o, void* stream) {
+  return decode_call(sh, st, 0, active, true, q, k, v, beta, g, vbar, o, stream);
+}
+
+int seed_compress_ragged(const seed_shape* sh, const seed_state* st, int32_t min_m, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return compress_call(sh, st, min_m, true, ws, ws_bytes, stream);
 }
 
 int seed_compress(const seed_shape* sh, const seed_state* st, int32_t m, void* ws, size_t ws_bytes,
                   void* stream) {
-  const int c = check_shape(sh);
-  if (c != SEED_OK) return c;
-  if (!state_ok(st)) return SEED_ERR_ARG;
-  if (m < 0 || m > sh->rank + sh->period) return SEED_ERR_ARG;
-  if (ws_bytes < seed_workspace_bytes(sh, SEED_OP_COMPRESS)) return SEED_ERR_WORKSPACE;
-  (void)ws;
-  if (!seed::compress_supported(*sh)) return SEED_ERR_UNSUPPORTED;
-  if (m <= sh->rank) return SEED_OK;
-  seed::CompressArgs a = compress_args(sh, st, m);
-  return hip_status(seed::launch_compress(*sh, a, static_cast<hipStream_t>(stream)));
+  return compress_call(sh, st, m, false, ws, ws_bytes, stream);
 }
 
 int seed_dense_decode_step(const seed_shape* sh, float* S, const void* q, const void* k,

@@ -404,10 +404,18 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
   float* gam = reinterpret_cast<float*>(reinterpret_cast<char*>(lds4) + sizeof(Core<CT>));
   const int t = threadIdx.x;
   const int64_t unit = blockIdx.x;
-  const int m = A.m, r = A.rank, C = A.slots;
+  const int r = A.rank, C = A.slots;
+  float* __restrict__ sc = A.scale + unit * A.scale_len;
+  int m = A.m;
+  if (A.ragged) {
+    // only the units whose own column count reached A.m (and holds columns beyond r); the
+    // count is the same for every thread, so the whole block leaves together
+    const int mu = static_cast<int>(__float_as_uint(sc[A.m_off]));
+    if (mu < A.m || mu <= r || mu > C) return;
+    m = mu;
+  }
   FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(C) * DK;
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
-  float* __restrict__ sc = A.scale + unit * A.scale_len;
   // the unit's compression-window count (stochastic rounding's counter; one more at the end)
   const uint32_t window = __float_as_uint(sc[A.win_off]);
   const Rounding RU{A.rounding != 0, A.rng_key, kSiteCompressU, unit, window};
@@ -463,9 +471,11 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
   }
   __syncthreads();
   reconstruct_rows<CT, DV, FDT, false>(S, S.GA, m, r, nullptr, Vb, RV);
-  // decay scales back to 1, sink coefficients to 0, the window count one up
+  // decay scales back to 1, sink coefficients to 0, the window count one up, m to r
   for (int i = t; i < A.scale_len; i += 256)
-    sc[i] = i < A.coef_off ? 1.f : (i < A.win_off ? 0.f : __uint_as_float(window + 1u));
+    sc[i] = i < A.coef_off ? 1.f
+            : (i < A.win_off ? 0.f
+                             : __uint_as_float(i == A.win_off ? window + 1u : static_cast<uint32_t>(r)));
 }
 
 template <int DK, int FDT>
@@ -782,9 +792,10 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
       Vb[static_cast<int64_t>(c) * DV + j] = round_store<FDT>(static_cast<float>(acc), RV, c, j);
     }
   }
-  // decay scales 1, sink coefficients 0, window count 0
+  // decay scales 1, sink coefficients 0, window count 0, m = r
   float* __restrict__ sc = A.scale + unit * A.scale_len;
-  for (int i = t; i < A.scale_len; i += 256) sc[i] = i < A.coef_off ? 1.f : 0.f;
+  for (int i = t; i < A.scale_len; i += 256)
+    sc[i] = i < A.coef_off ? 1.f : (i == A.m_off ? __uint_as_float(static_cast<uint32_t>(r)) : 0.f);
 }
 
 // ---- host dispatch ---------------------------------------------------------------------------

@@ -407,10 +407,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   const int h = lane >> 5, c32 = lane & 31;
   const int row = N == 64 ? lane : c32;  // the core row this lane holds
   const int64_t unit = blockIdx.x;
-  const int m = A.m, r = A.rank, C = A.slots;
+  const int r = A.rank, C = A.slots;
+  float* __restrict__ sc = A.scale + unit * A.scale_len;
+  int m = A.m;
+  if (A.ragged) {
+    // only the units whose own column count reached A.m (and holds columns beyond r)
+    const int mu = static_cast<int>(__float_as_uint(sc[A.m_off]));
+    if (mu < A.m || mu <= r || mu > C) return;
+    m = mu;
+  }
   uint16_t* __restrict__ Ub = reinterpret_cast<uint16_t*>(A.U) + unit * static_cast<int64_t>(C) * DK;
   uint16_t* __restrict__ Vb = reinterpret_cast<uint16_t*>(A.V) + unit * static_cast<int64_t>(C) * DV;
-  float* __restrict__ sc = A.scale + unit * A.scale_len;
   // the unit's compression-window count (stochastic rounding's counter; one more at the end)
   const uint32_t window = __float_as_uint(sc[A.win_off]);
   const bool sr = A.rounding != 0;
@@ -869,7 +876,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   const bool live = c32 < rr && lam > lmax * 1e-14f;
   const float q4 = live ? sqrtf(sqrtf(lam * bs)) : 1.f;   // of the unscaled eigenvalue
   const float qv = live ? 1.f / q4 : 0.f;          // lambda^(-1/4)
-  const float qu = live ? 1.f / (q4 * q4) : 0.f;   // lambda^(-1/2)
+  const float ql = live ? 1.f / (q4 * q4) : 0.f;   // lambda^(-1/2)
 
   // ---- X_V = diag(ibal) L Y lambda^(-1/4) (m x r) ----------------------------------------------
   constexpr int NTI = N / 32;  // 32-row tiles of an m x r operand
@@ -923,6 +930,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       }
     }
   }
+  // U' = M V' q with q = 1 / sigma, estimated twice: lambda^(-1/2) from the core, and
+  // 1 / |V'|^2 from the stored (rounded) V' column, since |V'_c|^2 = lambda_c^(1/2) in exact
+  // arithmetic. The two agree on every direction the fp32 core resolves. Below its resolution
+  // either can be far off: a rounded lambda far below the column's true Rayleigh quotient makes
+  // lambda^(-1/2) inflate the product, while a column tilted towards a strong direction makes
+  // 1 / |V'|^2 count that direction twice. The smaller of the two keeps every column's term
+  // M V' V'^T q within both a projection of M and the eigenvalue-scaled term.
+  float vss = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16 * NV / 2; ++t) {
+    const float x0 = lo16<FDT>(vw[t]), x1 = hi16<FDT>(vw[t]);
+    vss = fmaf(x0, x0, fmaf(x1, x1, vss));
+  }
+  vss += partner(vss);
+  const float qu = (live && vss > 0.f) ? fminf(ql, 1.f / vss) : 0.f;
   {
     f32x16 w[2] = {zero16(), zero16()};
     const bool ok0 = c32 < m, ok1 = N == 64 && c32 + 32 < m;
@@ -943,7 +965,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       w[0] = MF::mfma(__builtin_bit_cast(V8, u0), bop, w[0]);
       if constexpr (N == 64) w[1] = MF::mfma(__builtin_bit_cast(V8, u1), bop, w[1]);
     }
-    // X_U = diag(colsc) W lambda^(-1/2) (U' = U_s D_c V_s^T V' / sigma), as B operands
+    // X_U = diag(colsc) W / |V'|^2 (U' = U_s D_c V_s^T V' / sigma), as B operands
 #pragma unroll
     for (int I = 0; I < NTI; ++I) {
 #pragma unroll
@@ -1012,9 +1034,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
         *reinterpret_cast<uint32_t*>(Ub + c32 * DK + NU * i) = uw[j];
     }
   }
-  // decay scales restart at 1, sink coefficients at 0, the window count goes one up
+  // decay scales restart at 1, sink coefficients at 0, the window count goes one up, m is r
   for (int i = lane; i < A.scale_len; i += 64)
-    sc[i] = i < A.coef_off ? 1.f : (i < A.win_off ? 0.f : __uint_as_float(window + 1u));
+    sc[i] = i < A.coef_off ? 1.f
+            : (i < A.win_off ? 0.f
+                             : __uint_as_float(i == A.win_off ? window + 1u : static_cast<uint32_t>(r)));
 }
 
 namespace {

@@ -259,7 +259,15 @@ void k_decode(const StepArgs A) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * 4 + wv;
   if (unit >= A.units) return;  // whole wave leaves together
-  const int m = A.m, r = A.rank, C = A.slots;
+  float* __restrict__ sc = A.scale + unit * A.scale_len;
+  const int r = A.rank, C = A.slots;
+  int m = A.m;
+  if (A.ragged) {
+    // the unit's own column count; inactive units, and counts outside [r, r + T) (a full unit
+    // awaiting its compression), are left as they are (whole wave)
+    m = static_cast<int>(__float_as_uint(sc[A.m_off]));
+    if ((A.active != nullptr && A.active[unit] == 0) || m < r || m >= C) return;
+  }
   const int head = static_cast<int>(unit % A.heads);
 
   const int ug = lane / LPU, uo = (lane % LPU) * VF;  // U column group and d_k offset
@@ -290,7 +298,6 @@ void k_decode(const StepArgs A) {
   }
   const float beta = A.beta[unit];
   const float gs = DIAG ? 0.f : A.g[unit];
-  float* __restrict__ sc = A.scale + unit * A.scale_len;
   float own_scale = 0.f, col_scale = 1.f, slot0 = 1.f, Gm[VF], alpha[VF], av[VF];
   if constexpr (DIAG) {
     load_f32<0, VF>(A.g + unit * DK + uo, alpha);
@@ -493,7 +500,10 @@ void k_decode(const StepArgs A) {
   const float aq = aq0 + cy + coef * s;
 
   // the coefficient and the decay state are final: write them now
-  if (lane == 0) sc[A.coef_off + m - r] = coef;
+  if (lane == 0) {
+    sc[A.coef_off + m - r] = coef;
+    sc[A.m_off] = __uint_as_float(static_cast<uint32_t>(m + 1));
+  }
   if constexpr (!DIAG) {
     if (lane <= m - r) sc[lane] = gs * own_scale;
     else if (lane == m - r + 1) sc[lane] = 1.f;

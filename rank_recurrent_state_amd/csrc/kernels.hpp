@@ -14,11 +14,15 @@ struct StepArgs {
   int32_t m;          // columns held before the step
   int32_t rank;       // r
   int32_t slots;      // r + T: column slots per unit
-  int32_t scale_len;  // per-unit floats of the scale buffer: decay scales, sink coefficients, window count
+  int32_t scale_len;  // per-unit floats of the scale buffer: decay scales, sink coefficients, window
+                      // count, column count
   int32_t coef_off;   // where the T sink coefficients start: 1 + T (GDN, Mamba-2) or d_k (KDA)
   int32_t win_off;    // the compression-window count (a uint32 in the float buffer): coef_off + T
+  int32_t m_off;      // the unit's column count m (a uint32 in the float buffer): win_off + 1
   int32_t rounding;   // 0: nearest-even factor stores; 1: stochastic
   uint32_t rng_key;   // key of the stochastic-rounding draws
+  int32_t ragged;     // 1: every unit's m is its own column count; 0: m above for all
+  const uint8_t* active;  // ragged: units with active[u] == 0 are skipped (nullptr: none)
   float* a;
   void* U;
   void* V;
@@ -52,8 +56,10 @@ struct CompressArgs {
   int32_t scale_len;
   int32_t coef_off;
   int32_t win_off;
+  int32_t m_off;
   int32_t rounding;
   uint32_t rng_key;
+  int32_t ragged;     // 1: compress the units whose own count is >= m (and > r); 0: all, at m
   float* a;
   void* U;
   void* V;

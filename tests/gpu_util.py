@@ -43,33 +43,38 @@ def host_inputs(dx: dict, units) -> list:
     return [{k: h[k][u] for k in h} for u in units]
 
 
-def host_state(shape, st, units, m: int):
-    """Read back (a, U, V) in true (decay- and sink-folded) form, float64, for the given units.
+def host_state(shape, st, units, m):
+    """Read back (a, U, V) in true (decay- and sink-folded) form, float64, for the given units
+    (m: the column count, one for all units or one per unit).
 
     The scale buffer holds the lazy decay (GDN / Mamba-2: slot 0 for the columns j < r, slot
     1 + j - r after; KDA: the per-channel Gamma), then the sink coefficients c of the window's
     columns: the true sink is the decayed stored a plus sum_{j >= r} c[j - r] times true column j.
     """
     import torch
-    idx = torch.as_tensor(list(units), device=st.a.device)
+    units = list(units)
+    ms = [int(m)] * len(units) if np.ndim(m) == 0 else [int(x) for x in m]
+    idx = torch.as_tensor(units, device=st.a.device)
     a = st.a.index_select(0, idx).double().cpu().numpy()
-    Us = st.U.index_select(0, idx)[:, :m].double().cpu().numpy()
-    Vs = st.V.index_select(0, idx)[:, :m].double().cpu().numpy()
+    Ua = st.U.index_select(0, idx).double().cpu().numpy()
+    Va = st.V.index_select(0, idx).double().cpu().numpy()
     sc = st.scale.index_select(0, idx).double().cpu().numpy()
     s0 = shape.d_k if shape.kind == synth.KDA else 1 + shape.period
     r = shape.rank
     out = []
     for n in range(len(units)):
+        m = ms[n]
+        Us, Vs = Ua[n, :m], Va[n, :m]
         if shape.kind == synth.KDA:
-            U = (Us[n] * sc[n][None, :s0]).T
+            U = (Us * sc[n][None, :s0]).T
             a_true = sc[n][:s0] * a[n]
         else:
             c = np.array([sc[n][0] if j < r else sc[n][1 + j - r] for j in range(m)])
-            U = (Us[n] * c[:, None]).T
+            U = (Us * c[:, None]).T
             a_true = sc[n][0] * a[n]
         for j in range(r, m):
             a_true = a_true + sc[n][s0 + j - r] * U[:, j]
-        out.append((a_true, U, Vs[n].T))
+        out.append((a_true, U, Vs.T))
     return out
 
 

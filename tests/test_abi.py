@@ -35,13 +35,13 @@ def test_every_declared_symbol_is_exported():
 def test_size_queries():
     rrs = _lib()
     sh = rrs.make_shape(rrs.SEED_GDN, 64, 16, 128, 128, 16, 16, rrs.SEED_BF16)
-    # a (4 d_k) + U, V (2 bytes x 32 slots x (128 + 128)) + scale (4 ((1 + T) + T + 1): decay
-    # scales, the sink coefficients, the compression-window count)
-    assert rrs.seed_state_bytes(sh) == 4 * 128 + 2 * 32 * 256 + 4 * 34
-    assert rrs.seed_scale_len(sh) == 34
+    # a (4 d_k) + U, V (2 bytes x 32 slots x (128 + 128)) + scale (4 ((1 + T) + T + 2): decay
+    # scales, the sink coefficients, the compression-window and column counts)
+    assert rrs.seed_state_bytes(sh) == 4 * 128 + 2 * 32 * 256 + 4 * 35
+    assert rrs.seed_scale_len(sh) == 35
     kda = rrs.make_shape(rrs.SEED_KDA, 2, 2, 128, 128, 32, 32, rrs.SEED_F32)
-    assert rrs.seed_scale_len(kda) == 128 + 32 + 1
-    assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 161
+    assert rrs.seed_scale_len(kda) == 128 + 32 + 2
+    assert rrs.seed_state_bytes(kda) == 4 * 128 + 4 * 64 * 256 + 4 * 162
     # fp16 factors take the bytes of bf16 ones; their default inputs are bf16
     f16 = rrs.make_shape(rrs.SEED_GDN, 64, 16, 128, 128, 16, 16, rrs.SEED_F16)
     assert f16.io_dtype == rrs.SEED_BF16
@@ -123,6 +123,15 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert e.value.status == rrs.SEED_ERR_ARG
     # compress with m <= r is a no-op that touches nothing
     rrs.seed_compress(sh, st, 16, stream=0)
+    # ragged compression: min_m must lie in (r, r + T]
+    for bad in (16, 33, 0):
+        with pytest.raises(rrs.SeedError) as e:
+            rrs.seed_compress_ragged(sh, st, bad, stream=0)
+        assert e.value.status == rrs.SEED_ERR_ARG
+    f = _Fake()
+    with pytest.raises(rrs.SeedError) as e:
+        rrs.seed_decode_step_ragged(sh, st, f, f, f, f, f, _Fake(0), f, stream=0)
+    assert e.value.status == rrs.SEED_ERR_ARG
     with pytest.raises(rrs.SeedError) as e:
         rrs.seed_state_from_dense(sh, _Fake(0), _Fake(), st, stream=0)
     assert e.value.status == rrs.SEED_ERR_ARG

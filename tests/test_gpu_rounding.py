@@ -51,8 +51,10 @@ def _setup(kind, fdt, key, r=8, T=8, batch=2, heads=3, prefill=24, seed=71):
 
 
 def _window_count(st, sh):
-    sc = st.scale.detach().cpu().numpy()
-    return sc[:, -1].view(np.uint32).astype(np.int64)
+    """The compression-window count: the scale buffer's second-to-last float (a uint32), before
+    the column count."""
+    sc = np.ascontiguousarray(st.scale.detach().cpu().numpy()[:, -2])
+    return sc.view(np.uint32).astype(np.int64)
 
 
 def _bits(t, fdt):
