@@ -61,6 +61,9 @@ def parse():
                     help="factor storage other than the workload's own (fp16: with bf16 inputs)")
     ap.add_argument("--rounding", choices=["nearest", "stochastic"], default="nearest",
                     help="rounding of the 16-bit factor stores")
+    ap.add_argument("--staggered", action="store_true",
+                    help="requests at staggered column counts (request b at r + b mod T): ragged "
+                         "decode steps, each followed by a compression of the units that filled")
     ap.add_argument("--pool", type=int, default=64, help="steps of resident inputs, cycled")
     ap.add_argument("--dense-steps", type=int, default=32, help="timed dense-baseline steps")
     ap.add_argument("--prefill", type=int, default=None, help="override the prefill length")
@@ -276,6 +279,10 @@ def main():
         else:
             rrs.seed_compress(sh_all, state_all, w.rank + T)
 
+    if args.staggered:
+        return run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vbars, o,
+                             prefill, N, U1, L, T, P, nwin, Wu, K)
+
     for i in range(Wu // T):               # eager warmup (also the first launch of every kernel)
         enqueue_window(i % nwin)
         enqueue_compress()
@@ -422,6 +429,80 @@ def main():
                              "decode_only": dense_step_ms / dec_step_ms,
                              "state_byte_ratio_target": state_ratio},
         "setup_s": {"prefill_end_compression": t_from_dense},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vbars, o, prefill, N,
+                  U1, L, T, P, nwin, Wu, K):
+    """Ragged serving: request b of every layer holds r + (b mod T) columns when the timed steps
+    start, so that every step fills, and compresses, the units of one T-th of the requests. A
+    step is one ragged decode launch per layer and one compression launch over the stack that
+    compresses exactly the full units. Whole-job throughput only: the per-step compressions sit
+    in the same graph as the decode launches."""
+    dev = torch.device("cuda", 0)
+    phase = (torch.arange(U1, device=dev) // w.heads) % T
+    # stagger: request b sits out the steps from its phase on
+    for s_ in range(T - 1):
+        act = (phase > s_).to(torch.uint8)
+        xl = pool[s_ % P]
+        for l in range(L):
+            x = xl[l]
+            rrs.seed_decode_step_ragged(sh_l[l], states[l], x["q"], x["k"], x["v"], x["beta"], x["g"],
+                                        vbars[l], o[l], active=act)
+    torch.cuda.synchronize()
+    counts = rrs.column_counts(sh_all, state_all)
+    assert int(counts.min()) == w.rank and int(counts.max()) == w.rank + T - 1, "stagger"
+
+    def enqueue_steps(wi):
+        for j in range(T):
+            xl = pool[wi * T + j]
+            for l in range(L):
+                x = xl[l]
+                rrs.seed_decode_step_ragged(sh_l[l], states[l], x["q"], x["k"], x["v"], x["beta"],
+                                            x["g"], vbars[l], o[l])
+            rrs.seed_compress_ragged(sh_all, state_all, w.rank + T)
+
+    for i in range(max(1, Wu // T)):
+        enqueue_steps(i % nwin)
+    torch.cuda.synchronize()
+    graphs = not args.eager
+    if graphs:
+        g_win = []
+        for wi in range(nwin):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                enqueue_steps(wi)
+            g_win.append(g)
+        torch.cuda.synchronize()
+        log(f"[bench] captured {nwin} graphs of {T} staggered steps ({T * (L + 1)} launches each)")
+    nw = K // T
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(nw):
+        wi = i % nwin
+        if graphs:
+            g_win[wi].replay()
+        else:
+            enqueue_steps(wi)
+    e1.record()
+    torch.cuda.synchronize()
+    t_total = e0.elapsed_time(e1) / 1e3
+    counts = rrs.column_counts(sh_all, state_all)
+    assert int(counts.min()) >= w.rank and int(counts.max()) <= w.rank + T - 1, "every full unit compressed"
+    step_ms = t_total / K * 1e3
+    value = N * K / t_total
+    log(f"[bench] staggered: {K} steps in {t_total * 1e3:.1f} ms ({step_ms:.3f} ms/step)")
+    res = {
+        "metric": "factored decode head-steps/s (staggered requests, compression when full)",
+        "value": value, "unit": "head-steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.describe()}, staggered requests", "units": N,
+                   "launch_units": U1, "layers": L, "prefill_tokens": prefill,
+                   "rounding": args.rounding},
+        "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
 
