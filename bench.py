@@ -343,6 +343,25 @@ def main():
         f"{t_dec * 1e3:.1f} ms over {n_dec_launch} launches ({dec_gbs:.0f} GB/s), compress "
         f"{t_cmp * 1e3:.1f} ms over {n_cmp_launch} launches")
 
+    # ---- the state-energy diagnostic (not part of a step): one launch per layer ----------------
+    en_out = [torch.empty((U1, 3), dtype=torch.float32, device=dev) for _ in range(L)]
+    for l in range(L):
+        rrs.seed_state_energy(sh_l[l], states[l], vbars[l], out=en_out[l])
+    e_a, e_b = ev(), ev()
+    torch.cuda.synchronize()
+    e_a.record()
+    for l in range(L):
+        rrs.seed_state_energy(sh_l[l], states[l], vbars[l], out=en_out[l])
+    e_b.record()
+    torch.cuda.synchronize()
+    t_en = e_a.elapsed_time(e_b) / 1e3
+    m_now = int(rrs.column_counts(sh_l[0], states[0])[0])
+    f_b = 2 if w.factor_dtype else 4
+    en_bytes = N * (f_b * (w.d_k + w.d_v) * m_now + 4 * w.d_k + 4 * rrs.seed_scale_len(sh) + 12)
+    sink_share = float(sum(e[:, 1].sum() for e in en_out) / sum(e[:, 0].sum() for e in en_out))
+    log(f"[bench] energy diagnostic: {t_en * 1e3:.2f} ms over the stack at m = {m_now} "
+        f"({en_bytes / t_en / 1e9:.0f} GB/s); sink share of the energy {sink_share:.3f}")
+
     # ---- dense-state baseline ----------------------------------------------------------------
     KD = args.dense_steps
     d_ev = [(ev(), ev()) for _ in range(KD)]
@@ -429,6 +448,8 @@ def main():
                              "decode_only": dense_step_ms / dec_step_ms,
                              "state_byte_ratio_target": state_ratio},
         "setup_s": {"prefill_end_compression": t_from_dense},
+        "energy_diagnostic": {"ms_per_stack": t_en * 1e3, "columns": m_now, "gbs": en_bytes / t_en / 1e9,
+                              "sink_share": sink_share},
     }
     print(json.dumps(res), flush=True)
 

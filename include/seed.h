@@ -227,6 +227,19 @@ int seed_compress_ragged(const seed_shape *shape, const seed_state *state, int32
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Energy of every unit's state (a diagnostic): with S~ = a_true vbar^T + U_true V^T over the
+ * unit's own column count (kept in the state),
+ *   out[u][0] = |S~|_F^2,  out[u][1] = |a_true vbar^T|_F^2 (the sink),  out[u][2] = |U V^T|_F^2.
+ * The sink's share of the energy, out[u][1] / out[u][0], summed over heads first when pooled,
+ * is the statistic the pages report for trained models.
+ *   vbar   float [heads][d_v];  out  float [units][3], written.
+ * Source: picx.dev summary, key finding 2 and "Introduction and Theoretical Foundation" (the
+ * state sink holds most of the state energy).
+ */
+int seed_state_energy(const seed_shape *shape, const seed_state *state, const float *vbar,
+                      float *out, void *stream);
+
+/*
  * Dense-state step (the uncompressed baseline): S <- the dense recurrence of `kind`, then
  * o = S^T q.
  *   S      float [units][d_k][d_v], read once and written once.

@@ -46,7 +46,7 @@ __all__ = [
     "GDN", "KDA", "MAMBA2", "decay", "dense_step", "readout", "sink_split", "truncate",
     "factored_step", "compress", "from_dense", "reconstruct", "decay_bound",
     "corollary4_bound", "run_dense", "run_factored", "run_compressed", "singular_values",
-    "relative_gap", "truncation_is_optimal", "state_bytes", "dense_state_bytes",
+    "relative_gap", "truncation_is_optimal", "state_bytes", "dense_state_bytes", "state_energy",
 ]
 
 
@@ -299,3 +299,15 @@ def state_bytes(n_heads: int, d_k: int, d_v: int, m: float, bytes_per: int = 4) 
 def dense_state_bytes(n_heads: int, d_k: int, d_v: int, bytes_per: int = 4) -> float:
     """Bytes of the dense recurrent states: one d_k x d_v matrix per head."""
     return bytes_per * n_heads * d_k * d_v
+
+
+def state_energy(a, vbar, U, V):
+    """(|S~|_F^2, |a vbar^T|_F^2, |U V^T|_F^2) of S~ = a vbar^T + U V^T, from the explicit
+    matrices. picx.dev summary, key finding 2 and "Introduction and Theoretical Foundation": the
+    state sink's share of the state energy is the sink term's squared Frobenius norm over the
+    whole state's."""
+    a, vbar, U, V = _f64(a), _f64(vbar), _f64(U), _f64(V)
+    sink = np.outer(a, vbar)
+    content = U @ V.T
+    S = sink + content
+    return float(np.sum(S * S)), float(np.sum(sink * sink)), float(np.sum(content * content))

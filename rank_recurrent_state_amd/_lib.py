@@ -22,7 +22,8 @@ SEED_OP_COMPRESS, SEED_OP_FROM_DENSE = 0, 1
 EXPORTS = [
     "seed_state_bytes", "seed_scale_len", "seed_workspace_bytes", "seed_state_from_dense",
     "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
-    "seed_compress_ragged", "seed_dense_decode_step", "seed_status_string", "seed_version",
+    "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_status_string",
+    "seed_version",
 ]
 
 
@@ -70,6 +71,7 @@ def _load():
         "seed_decode_step_ragged": (ctypes.c_int, [Sp, Stp, P, P, P, P, P, P, P, P, P]),
         "seed_compress": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, ctypes.c_size_t, P]),
         "seed_compress_ragged": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, ctypes.c_size_t, P]),
+        "seed_state_energy": (ctypes.c_int, [Sp, Stp, P, P, P]),
         "seed_dense_decode_step": (ctypes.c_int, [Sp, P, P, P, P, P, P, P, P]),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "seed_version": (ctypes.c_char_p, []),
@@ -249,6 +251,19 @@ def seed_compress_ragged(shape: seed_shape, state, min_m: int, ws=None, stream=N
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("seed_compress_ragged", LIB.seed_compress_ragged(
         ctypes.byref(shape), _state_c(state), min_m, _ptr(ws), ws_bytes, _stream_ptr(stream)))
+
+
+def seed_state_energy(shape: seed_shape, state, vbar, out=None, stream=None):
+    """Per unit (|S~|^2, |a vbar^T|^2, |U V^T|^2) as a float32 [units, 3] device tensor."""
+    import torch
+    _expect_state(shape, state)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    if out is None:
+        out = torch.empty((shape.units, 3), dtype=torch.float32, device=state.a.device)
+    _expect("out", out, shape.units * 3, SEED_F32)
+    _check("seed_state_energy", LIB.seed_state_energy(
+        ctypes.byref(shape), _state_c(state), _ptr(vbar), _ptr(out), _stream_ptr(stream)))
+    return out
 
 
 def column_counts(shape: seed_shape, state):

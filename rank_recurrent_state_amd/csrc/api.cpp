@@ -193,6 +193,28 @@ int seed_compress(const seed_shape* sh, const seed_state* st, int32_t m, void* w
   return compress_call(sh, st, m, false, ws, ws_bytes, stream);
 }
 
+int seed_state_energy(const seed_shape* sh, const seed_state* st, const float* vbar, float* out,
+                      void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st) || !vbar || !out) return SEED_ERR_ARG;
+  seed::EnergyArgs a{};
+  a.units = units_of(sh);
+  a.heads = sh->heads;
+  a.rank = sh->rank;
+  a.slots = sh->rank + sh->period;
+  a.scale_len = scale_len(sh);
+  a.coef_off = coef_off(sh);
+  a.m_off = coef_off(sh) + sh->period + 1;
+  a.a = st->a;
+  a.U = st->U;
+  a.V = st->V;
+  a.scale = st->scale;
+  a.vbar = vbar;
+  a.out = out;
+  return hip_status(seed::launch_energy(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
 int seed_dense_decode_step(const seed_shape* sh, float* S, const void* q, const void* k,
                            const void* v, const float* beta, const float* g, void* o,
                            void* stream) {

@@ -1041,6 +1041,130 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
                              : __uint_as_float(i == A.win_off ? window + 1u : static_cast<uint32_t>(r)));
 }
 
+// ---- state energy (the diagnostic of seed_state_energy) for 16-bit factors ---------------------
+// One wavefront per unit: the Grams of the stored columns by the MFMA routine above (KDA's
+// Gamma^2 on the U side), the content energy sum_{i,j} G_U[i][j] G_V[i][j] (with the lazy column
+// scales c_i c_j for GDN and Mamba-2) from the row-per-lane tiles; the sink a_true and the cross
+// term (U^T a) . (V^T vbar) by lanes over d and over columns. Reads the factors once.
+template <int DK, int DV, bool DIAG, int N, int FDT>
+__global__ __launch_bounds__(64) void k_energy_wave(const EnergyArgs A) {
+  using namespace cw;
+  __shared__ float gam[DK];
+  __shared__ float at[DK];
+  __shared__ float colsc[N];
+  const int lane = threadIdx.x;
+  const int col = N == 64 ? lane : (lane & 31);
+  const int64_t unit = blockIdx.x;
+  const int r = A.rank, C = A.slots;
+  const float* __restrict__ sc = A.scale + unit * A.scale_len;
+  const uint32_t mu = __float_as_uint(sc[A.m_off]);   // unsigned; beyond the slots: all of them
+  const int m = mu > static_cast<uint32_t>(C) ? C : static_cast<int>(mu);
+  const uint16_t* __restrict__ Ub = reinterpret_cast<const uint16_t*>(A.U) + unit * static_cast<int64_t>(C) * DK;
+  const uint16_t* __restrict__ Vb = reinterpret_cast<const uint16_t*>(A.V) + unit * static_cast<int64_t>(C) * DV;
+  const float* __restrict__ vb = A.vbar + static_cast<int64_t>(unit % A.heads) * DV;
+
+  if constexpr (DIAG) {
+    for (int d = lane; d < DK; d += 64) gam[d] = sc[d];
+  }
+  const float cs = col < m ? (DIAG ? 1.f : sc[col < r ? 0 : 1 + col - r]) : 0.f;
+  colsc[col] = cs;
+  wave_lds_sync();
+
+  // content: the Grams (zero beyond m), then sum over rho of c_rho G_U[rho][col] G_V[rho][col]
+  float content;
+  {
+    const M64 gu = gram<DK, DIAG, N, FDT>(Ub, m, gam);
+    const M64 gv = gram<DV, false, N, FDT>(Vb, m, nullptr);
+    const f32x32 GU_lo = gu.lo, GU_hi = gu.hi, GV_lo = gv.lo, GV_hi = gv.hi;
+    float p = 0.f;
+#pragma unroll
+    for (int rho = 0; rho < N; ++rho) p = fmaf(colsc[rho] * MGET(GU, rho), MGET(GV, rho), p);
+    content = rsum<N>(p * cs);
+  }
+
+  // a_true = (slot-0 decay, or Gamma) a_0 + sum_{j >= r} c_j U_true[j], lanes over d
+  for (int d = lane; d < DK; d += 64) {
+    float acc = (DIAG ? gam[d] : sc[0]) * A.a[unit * DK + d];
+    for (int j = r; j < m; ++j)
+      acc = fmaf(sc[A.coef_off + j - r] * (DIAG ? gam[d] : colsc[j]), to_f32<FDT>(Ub[static_cast<int64_t>(j) * DK + d]), acc);
+    at[d] = acc;
+  }
+  wave_lds_sync();
+  float pa = 0.f, pv = 0.f;
+  for (int d = lane; d < DK; d += 64) pa = fmaf(at[d], at[d], pa);
+  for (int d = lane; d < DV; d += 64) pv = fmaf(vb[d], vb[d], pv);
+  const float sink = wave_sum(pa) * wave_sum(pv);
+  // cross: x_col = U_true[col] . a_true, y_col = V[col] . vbar (one lane per column)
+  float xy = 0.f;
+  if (col < m && (N == 64 || lane < 32)) {
+    float x = 0.f, y = 0.f;
+    const uint16_t* pu = Ub + static_cast<int64_t>(col) * DK;
+    const uint16_t* pv2 = Vb + static_cast<int64_t>(col) * DV;
+#pragma unroll 4
+    for (int d = 0; d < DK; d += 8) {
+      const uint4 w4 = *reinterpret_cast<const uint4*>(pu + d);
+      const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d0 = d + 2 * e;
+        x = fmaf((DIAG ? gam[d0] : 1.f) * lo16<FDT>(ww[e]), at[d0], x);
+        x = fmaf((DIAG ? gam[d0 + 1] : 1.f) * hi16<FDT>(ww[e]), at[d0 + 1], x);
+      }
+    }
+#pragma unroll 4
+    for (int d = 0; d < DV; d += 8) {
+      const uint4 w4 = *reinterpret_cast<const uint4*>(pv2 + d);
+      const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y = fmaf(lo16<FDT>(ww[e]), vb[d + 2 * e], y);
+        y = fmaf(hi16<FDT>(ww[e]), vb[d + 2 * e + 1], y);
+      }
+    }
+    xy = (DIAG ? 1.f : cs) * x * y;
+  }
+  const float cross = wave_sum(xy);
+  if (lane == 0) {
+    A.out[unit * 3 + 0] = sink + 2.f * cross + content;
+    A.out[unit * 3 + 1] = sink;
+    A.out[unit * 3 + 2] = content;
+  }
+}
+
+namespace {
+using EnergyWaveFn = void (*)(const EnergyArgs);
+
+template <int N, int FDT>
+EnergyWaveFn pick_energy_width(const seed_shape& sh) {
+  const bool diag = sh.kind == SEED_KDA;
+  if (sh.d_k == 128 && sh.d_v == 128)
+    return diag ? k_energy_wave<128, 128, true, N, FDT> : k_energy_wave<128, 128, false, N, FDT>;
+  if (sh.d_k == 128 && sh.d_v == 64)
+    return diag ? k_energy_wave<128, 64, true, N, FDT> : k_energy_wave<128, 64, false, N, FDT>;
+  if (sh.d_k == 64 && sh.d_v == 128)
+    return diag ? k_energy_wave<64, 128, true, N, FDT> : k_energy_wave<64, 128, false, N, FDT>;
+  if (sh.d_k == 64 && sh.d_v == 64)
+    return diag ? k_energy_wave<64, 64, true, N, FDT> : k_energy_wave<64, 64, false, N, FDT>;
+  return nullptr;
+}
+
+EnergyWaveFn pick_energy_wave(const seed_shape& sh) {
+  if (sh.rank + sh.period > 64) return nullptr;
+  const bool narrow = sh.rank + sh.period <= 32;
+  if (sh.factor_dtype == SEED_BF16) return narrow ? pick_energy_width<32, 1>(sh) : pick_energy_width<64, 1>(sh);
+  if (sh.factor_dtype == SEED_F16) return narrow ? pick_energy_width<32, 2>(sh) : pick_energy_width<64, 2>(sh);
+  return nullptr;
+}
+}  // namespace
+
+hipError_t launch_energy_wave(const seed_shape& sh, const EnergyArgs& a, hipStream_t s, bool* used) {
+  EnergyWaveFn fn = pick_energy_wave(sh);
+  *used = fn != nullptr;
+  if (!fn) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(a.units)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
 namespace {
 using WaveFn = void (*)(const CompressArgs);
 

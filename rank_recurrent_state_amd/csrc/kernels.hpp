@@ -69,11 +69,31 @@ struct CompressArgs {
   int32_t iters;      // from_dense only: subspace iterations (128 x 128 states)
 };
 
+struct EnergyArgs {
+  int64_t units;
+  int32_t heads;
+  int32_t rank;
+  int32_t slots;
+  int32_t scale_len;
+  int32_t coef_off;
+  int32_t m_off;
+  const float* a;
+  const void* U;
+  const void* V;
+  const float* scale;
+  const float* vbar;
+  float* out;         // [units][3]: |S~|^2, |a vbar^T|^2, |U V^T|^2
+};
+
 // Each returns hipSuccess or the launch error. Shapes are validated by the caller.
 hipError_t launch_decode(const seed_shape& sh, const StepArgs& a, hipStream_t s);
 hipError_t launch_dense(const seed_shape& sh, const DenseArgs& a, hipStream_t s);
 hipError_t launch_compress(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
 hipError_t launch_from_dense(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
+hipError_t launch_energy(const seed_shape& sh, const EnergyArgs& a, hipStream_t s);
+// The energy diagnostic for 16-bit factors (one wavefront per unit, MFMA Grams); *used tells
+// whether it took the call.
+hipError_t launch_energy_wave(const seed_shape& sh, const EnergyArgs& a, hipStream_t s, bool* used);
 // One-wavefront-per-unit compression with the core in registers (bf16 factors, r <= 32,
 // r + T <= 64); *used tells whether it took the call.
 hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used);

@@ -96,3 +96,26 @@ def test_value_along_vbar_only_feeds_the_sink():
     np.testing.assert_allclose(a1, 0.5 * 3.0 * kap)
     np.testing.assert_allclose(V1, 0.0)
     np.testing.assert_allclose(o1, 1.5 * vbar)
+
+
+def test_state_energy_pins():
+    """The energy split: a worked 2 x 2 case, Pythagoras when the content is orthogonal to vbar,
+    and the sink split of a dense state, whose content is orthogonal to vbar by construction."""
+    tot, sink, cont = orc.state_energy([2.0, 0.0], [3.0, 0.0], np.array([[0.0], [1.0]]), np.array([[0.0], [5.0]]))
+    assert (tot, sink, cont) == (36.0 + 25.0, 36.0, 25.0)
+    g = np.random.default_rng(3)
+    vb = g.standard_normal(6)
+    V = g.standard_normal((6, 3))
+    V -= np.outer(vb, vb @ V) / (vb @ vb)          # columns orthogonal to vbar
+    a, U = g.standard_normal(5), g.standard_normal((5, 3))
+    tot, sink, cont = orc.state_energy(a, vb, U, V)
+    assert tot == pytest.approx(sink + cont, rel=1e-12)
+    assert sink == pytest.approx(float(a @ a) * float(vb @ vb), rel=1e-12)
+    S = g.standard_normal((5, 6))
+    a_s, C = orc.sink_split(S, vb)
+    tot, sink, cont = orc.state_energy(a_s, vb, C, np.eye(6))
+    assert tot == pytest.approx(float(np.sum(S * S)), rel=1e-12)
+    assert tot == pytest.approx(sink + cont, rel=1e-12)
+    # a cross term that does not vanish: the total is not the sum of the parts
+    tot, sink, cont = orc.state_energy([1.0, 0.0], [1.0, 0.0], np.array([[1.0], [0.0]]), np.array([[1.0], [0.0]]))
+    assert (tot, sink, cont) == (4.0, 1.0, 1.0)
