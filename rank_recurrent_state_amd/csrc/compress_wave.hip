@@ -33,7 +33,11 @@
 //                         I, so that each lane loads NT consecutive elements of a column);
 //                         W = V_s^T V' by MFMA 32x32x16 bf16 (fp16) on the rounded V' that is
 //                         stored,
-//                         so that U' = M V' / sigma holds for the stored pair.
+//                         so that U' = M V' / sigma holds for the stored pair;
+//   lazy sink             a = (slot-0 decay) a_0 + U_s f (f_j: column j's sink coefficient
+//                         times its decay scale), accumulated on the A operands of the U'
+//                         product (no separate pass over the columns).
+// Stochastic rounding of the stored factors is a separate instance of the kernel.
 // LDS holds L (N x (N + 1) fp32) and a few vectors: about 19.5 KB for N = 64, so eight units
 // share a CU (two waves per SIMD), and 6 KB for N = 32 (three waves per SIMD).
 #include <float.h>
@@ -270,6 +274,7 @@ struct Smem {
   alignas(16) float bal[N];
   alignas(16) float ibal[N];
   alignas(16) float colsc[N];
+  alignas(16) float cf[N];         // sink fold coefficients, column j at (j % 2) N / 2 + j / 2
   alignas(16) float gam[128];
 };
 
@@ -341,35 +346,51 @@ __device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, con
 // of tile I is d = NT i + I, so that one lane's A operands of a column are NT consecutive
 // elements (one load per K-step). Output: y[I][j] is Y[d][lane % 32] with
 // d = NT (8 (j / 4) + 4 (lane / 32) + j % 4) + I.
-template <int D, int N, int FDT>
+// With FOLD, the same A operands also give F f for the vector f (cf: f_j at (j % 2) N / 2 + j / 2):
+// fold[I] is lane half lane / 32's share of (F f)[NT (lane % 32) + I] (the other half's share is
+// in the partner lane).
+template <int D, int N, int FDT, bool FOLD = false>
 __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, const int m, const float (&xop)[N / 2],
-                                             f32x16 (&y)[D / 32]) {
+                                             f32x16 (&y)[D / 32], const float* __restrict__ cf = nullptr,
+                                             float* fold = nullptr) {
   constexpr int NT = D / 32;
   static_assert(NT == 2 || NT == 4, "d of 64 or 128");
   const int lane = threadIdx.x;
   const int c = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int I = 0; I < NT; ++I) y[I] = zero16();
+  if constexpr (FOLD) {
 #pragma unroll
-  for (int s = 0; s < N / 2; ++s) {
-    const int col = 2 * s + kh;
-    const bool ok = col < m;
-    const uint16_t* p = base + (ok ? col : 0) * D + NT * c;
-    uint32_t w[2];
-    if constexpr (NT == 4) {
-      const uint2 u = *reinterpret_cast<const uint2*>(p);
-      w[0] = ok ? u.x : 0u;
-      w[1] = ok ? u.y : 0u;
-    } else {
-      const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-      w[0] = ok ? u : 0u;
-      w[1] = 0u;
-    }
+    for (int I = 0; I < NT; ++I) fold[I] = 0.f;
+  }
 #pragma unroll
-    for (int I = 0; I < NT; ++I) {
-      const uint32_t wi = w[I >> 1];
-      const float a = (I & 1) ? hi16<FDT>(wi) : lo16<FDT>(wi);
-      y[I] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xop[s], y[I], 0, 0, 0);
+  for (int s4 = 0; s4 < N / 8; ++s4) {
+    float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (FOLD) f4 = *reinterpret_cast<const float4*>(cf + kh * (N / 2) + 4 * s4);
+    const float fs[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+    for (int s1 = 0; s1 < 4; ++s1) {
+      const int s = 4 * s4 + s1;
+      const int col = 2 * s + kh;
+      const bool ok = col < m;
+      const uint16_t* p = base + (ok ? col : 0) * D + NT * c;
+      uint32_t w[2];
+      if constexpr (NT == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        w[0] = ok ? u.x : 0u;
+        w[1] = ok ? u.y : 0u;
+      } else {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+        w[0] = ok ? u : 0u;
+        w[1] = 0u;
+      }
+#pragma unroll
+      for (int I = 0; I < NT; ++I) {
+        const uint32_t wi = w[I >> 1];
+        const float a = (I & 1) ? hi16<FDT>(wi) : lo16<FDT>(wi);
+        y[I] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, xop[s], y[I], 0, 0, 0);
+        if constexpr (FOLD) fold[I] = fmaf(fs[s1], a, fold[I]);
+      }
     }
   }
 }
@@ -397,7 +418,7 @@ __device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float
 
 }  // namespace cw
 
-template <int DK, int DV, bool DIAG, int N, int FDT>
+template <int DK, int DV, bool DIAG, int N, int FDT, bool SR>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 : 3))) void k_compress_wave(const CompressArgs A) {
   using namespace cw;
   static_assert(N == 64 || N == 32, "core width");
@@ -420,7 +441,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   uint16_t* __restrict__ Vb = reinterpret_cast<uint16_t*>(A.V) + unit * static_cast<int64_t>(C) * DV;
   // the unit's compression-window count (stochastic rounding's counter; one more at the end)
   const uint32_t window = __float_as_uint(sc[A.win_off]);
-  const bool sr = A.rounding != 0;
+  // stochastic rounding is a separate instance: the nearest-rounding kernel carries none of its
+  // code (a larger kernel misses the instruction cache more often)
+  constexpr bool sr = SR;
 
   // ---- column scales (lazy decay), KDA's channel scales ----------------------------------------
   float csc;
@@ -431,39 +454,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     csc = row < m ? sc[row < r ? 0 : 1 + row - r] : 0.f;
   }
   S.colsc[row] = csc;
+  // ---- the lazy sink: a = (slot-0 decay) a_0 + sum_{j >= r} c_j (true column j) (KDA:
+  // Gamma . (a_0 + sum_j c_j U_j)). The sum U_s f, f_j = c_j (column scale j), rides on the
+  // A operands of the U' product below (the same column reads); here only f goes to LDS.
+  {
+    const float f = row >= r && row < m ? sc[A.coef_off + row - r] * csc : 0.f;
+    S.cf[(row & 1) * (N / 2) + (row >> 1)] = f;
+  }
   wave_lds_sync();
 
-  // ---- the lazy sink folded into a: a = (slot-0 decay) a_0 + sum_{j >= r} c_j (true column j)
-  // (KDA: Gamma . (a_0 + sum_j c_j U_j)); the window columns are not rewritten below. A lane
-  // holds DK / 64 consecutive channels; the column reads go out 16 at a time, independent of
-  // one another, so a unit waits on memory about twice rather than once per column.
-  {
-    constexpr int EPL = DK / 64;
-    static_assert(EPL == 1 || EPL == 2, "d_k of 64 or 128");
-    const int d0 = EPL * lane;
-    float acc[EPL] = {};
-    for (int j0 = r; j0 < m; j0 += 16) {
-      uint32_t w[16];
-      float cj[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = j0 + i < m ? j0 + i : m - 1;
-        cj[i] = j0 + i < m ? sc[A.coef_off + j - r] * (DIAG ? 1.f : sc[1 + j - r]) : 0.f;
-        const uint16_t* p = Ub + static_cast<int64_t>(j) * DK + d0;
-        if constexpr (EPL == 2) w[i] = *reinterpret_cast<const uint32_t*>(p);
-        else w[i] = p[0];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        acc[0] = fmaf(cj[i], lo16<FDT>(w[i]), acc[0]);
-        if constexpr (EPL == 2) acc[1] = fmaf(cj[i], hi16<FDT>(w[i]), acc[1]);
-      }
-    }
-    float* __restrict__ ap = A.a + unit * DK + d0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      ap[e] = DIAG ? S.gam[d0 + e] * (ap[e] + acc[e]) : sc[0] * ap[e] + acc[e];
-  }
+
 
   // ---- Grams of the stored columns -------------------------------------------------------------
   f32x32 GU_lo, GU_hi, GV_lo, GV_hi;
@@ -998,7 +998,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   uint32_t uw[16 * NU / 2];
   {
     f32x16 ut[NU];
-    factor_times<DK, N, FDT>(Ub, m, xop, ut);
+    float* __restrict__ ap = A.a + unit * DK + NU * c32;
+    float a0[NU], fold[NU];
+    if (h == 0) {
+      if constexpr (NU == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(ap);
+        a0[0] = v.x; a0[1] = v.y; a0[2] = v.z; a0[3] = v.w;
+      } else {
+        const float2 v = *reinterpret_cast<const float2*>(ap);
+        a0[0] = v.x; a0[1] = v.y;
+      }
+    }
+    const float s0 = sc[0];
+    factor_times<DK, N, FDT, true>(Ub, m, xop, ut, S.cf, fold);
+#pragma unroll
+    for (int I = 0; I < NU; ++I) fold[I] += partner(fold[I]);
+    if (h == 0) {
+      float an[NU];
+#pragma unroll
+      for (int I = 0; I < NU; ++I)
+        an[I] = DIAG ? S.gam[NU * c32 + I] * (a0[I] + fold[I]) : fmaf(s0, a0[I], fold[I]);
+      if constexpr (NU == 4) *reinterpret_cast<float4*>(ap) = make_float4(an[0], an[1], an[2], an[3]);
+      else *reinterpret_cast<float2*>(ap) = make_float2(an[0], an[1]);
+    }
     uint4 dr = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -1168,23 +1190,28 @@ hipError_t launch_energy_wave(const seed_shape& sh, const EnergyArgs& a, hipStre
 namespace {
 using WaveFn = void (*)(const CompressArgs);
 
-template <int N, int FDT>
+template <int N, int FDT, bool SR>
 WaveFn pick_width(const seed_shape& sh) {
   const bool diag = sh.kind == SEED_KDA;
   if (sh.d_k == 128 && sh.d_v == 128)
-    return diag ? k_compress_wave<128, 128, true, N, FDT> : k_compress_wave<128, 128, false, N, FDT>;
+    return diag ? k_compress_wave<128, 128, true, N, FDT, SR> : k_compress_wave<128, 128, false, N, FDT, SR>;
   if (sh.d_k == 128 && sh.d_v == 64)
-    return diag ? k_compress_wave<128, 64, true, N, FDT> : k_compress_wave<128, 64, false, N, FDT>;
+    return diag ? k_compress_wave<128, 64, true, N, FDT, SR> : k_compress_wave<128, 64, false, N, FDT, SR>;
   if (sh.d_k == 64 && sh.d_v == 128)
-    return diag ? k_compress_wave<64, 128, true, N, FDT> : k_compress_wave<64, 128, false, N, FDT>;
+    return diag ? k_compress_wave<64, 128, true, N, FDT, SR> : k_compress_wave<64, 128, false, N, FDT, SR>;
   if (sh.d_k == 64 && sh.d_v == 64)
-    return diag ? k_compress_wave<64, 64, true, N, FDT> : k_compress_wave<64, 64, false, N, FDT>;
+    return diag ? k_compress_wave<64, 64, true, N, FDT, SR> : k_compress_wave<64, 64, false, N, FDT, SR>;
   return nullptr;
+}
+
+template <int N, int FDT>
+WaveFn pick_rounding(const seed_shape& sh) {
+  return sh.rounding == SEED_ROUND_STOCHASTIC ? pick_width<N, FDT, true>(sh) : pick_width<N, FDT, false>(sh);
 }
 
 template <int FDT>
 WaveFn pick_format(const seed_shape& sh) {
-  return sh.rank + sh.period <= 32 ? pick_width<32, FDT>(sh) : pick_width<64, FDT>(sh);
+  return sh.rank + sh.period <= 32 ? pick_rounding<32, FDT>(sh) : pick_rounding<64, FDT>(sh);
 }
 
 // 16-bit factors (bf16, fp16) with r <= 32
