@@ -362,6 +362,46 @@ def main():
     log(f"[bench] energy diagnostic: {t_en * 1e3:.2f} ms over the stack at m = {m_now} "
         f"({en_bytes / t_en / 1e9:.0f} GB/s); sink share of the energy {sink_share:.3f}")
 
+    # ---- the chunked update (not part of a step): len tokens per unit in one launch, on a copy
+    # of layer 0's state, against len decode launches -----------------------------------------
+    chunk = None
+    if w.kind != rrs.SEED_KDA and args.rounding == "nearest":
+        chunk = {}
+        st_c = rrs.State(*[t.clone() for t in states[0].tensors()])
+        m0 = int(rrs.column_counts(sh_l[0], st_c)[0])
+        io_t = {rrs.SEED_BF16: torch.bfloat16, rrs.SEED_F32: torch.float32}[w.io_dtype]
+        Bq, Hq = w.batch, w.heads
+        for Lc in (16, 32):
+            if m0 + Lc > w.rank + T:
+                continue
+            gq = torch.Generator(device=dev).manual_seed(Lc)
+            q_c = torch.randn(Bq, Lc, Hq, w.d_k, device=dev, generator=gq)
+            k_c = torch.randn(Bq, Lc, Hq, w.d_k, device=dev, generator=gq)
+            if w.kind != rrs.SEED_MAMBA2:
+                q_c = q_c / q_c.norm(dim=-1, keepdim=True)
+                k_c = k_c / k_c.norm(dim=-1, keepdim=True)
+            v_c = torch.randn(Bq, Lc, Hq, w.d_v, device=dev, generator=gq).to(io_t)
+            q_c, k_c = q_c.to(io_t), k_c.to(io_t)
+            b_c = torch.rand(Bq, Lc, Hq, device=dev, generator=gq)
+            g_c = 0.9 + 0.1 * torch.rand(Bq, Lc, Hq, device=dev, generator=gq)
+            o_c = torch.empty(Bq, Lc, Hq, w.d_v, dtype=io_t, device=dev)
+            rrs.seed_decode_chunk(sh_l[0], st_c, m0, Lc, q_c, k_c, v_c, b_c, g_c, vbars[0], o_c)
+            c_ev = [(ev(), ev()) for _ in range(5)]
+            torch.cuda.synchronize()
+            for a_, b_ in c_ev:
+                a_.record()
+                rrs.seed_decode_chunk(sh_l[0], st_c, m0, Lc, q_c, k_c, v_c, b_c, g_c, vbars[0], o_c)
+                b_.record()
+            torch.cuda.synchronize()
+            t_c = sorted(a_.elapsed_time(b_) for a_, b_ in c_ev)[2] / 1e3   # median launch
+            dec_launch = t_dec / n_dec_launch
+            chunk[str(Lc)] = {"us_per_launch": t_c * 1e6, "head_tokens_per_s": U1 * Lc / t_c,
+                              "m": m0, "speedup_vs_decode_launches": Lc * dec_launch / t_c}
+            log(f"[bench] chunked update, {Lc} tokens x {U1} units at m = {m0}: {t_c * 1e6:.0f} us "
+                f"({U1 * Lc / t_c / 1e6:.0f} M head-tokens/s; {Lc * dec_launch / t_c:.2f}x {Lc} decode "
+                f"launches)")
+        del st_c
+
     # ---- dense-state baseline ----------------------------------------------------------------
     KD = args.dense_steps
     d_ev = [(ev(), ev()) for _ in range(KD)]
@@ -450,6 +490,7 @@ def main():
         "setup_s": {"prefill_end_compression": t_from_dense},
         "energy_diagnostic": {"ms_per_stack": t_en * 1e3, "columns": m_now, "gbs": en_bytes / t_en / 1e9,
                               "sink_share": sink_share},
+        "chunked_update": chunk,
     }
     print(json.dumps(res), flush=True)
 

@@ -199,6 +199,37 @@ int seed_decode_step_ragged(const seed_shape *shape, const seed_state *state,
                             void *stream);
 
 /*
+ * Chunked update: len consecutive tokens of every unit in one call (GDN and Mamba-2).
+ * It appends the len columns and writes the len read-outs that len calls of seed_decode_step
+ * would give for the same inputs (equal in exact arithmetic; fp32 arithmetic in another order).
+ * Each token's value residual is found by a forward substitution over the chunk:
+ * (I + A) [c | W] = beta (omega - gamma a~ . kappa | eps - gamma V U~^T kappa), with
+ * A[t][s] = beta_t Gamma(t,s) kappa_t . kappa_s (s < t) and Gamma(t,s) the product of the gates
+ * after token s up to token t (Mamba-2: A = 0).
+ *   m      columns held before the chunk, rank <= m and m + len <= rank + period.
+ *   len    tokens, 1 <= len <= 32.
+ *   q, k   [batch][len][heads][d_k] (io_dtype), v [batch][len][heads][d_v]: token t of unit
+ *          (b, h) is row (b len + t) heads + h, the layout of a projection over a batch of
+ *          sequences.
+ *   beta, g float [batch][len][heads] (one scalar gate per token).
+ *   vbar   float [heads][d_v].
+ *   o      written, [batch][len][heads][d_v] (io_dtype): token t's read-out S_t^T q_t.
+ *   state  as after len decode steps: the keys become columns m .. m + len - 1 of U (decay
+ *          scale: the gates of the later tokens), W columns m .. of V, c their sink
+ *          coefficients; the scales held before take the product of all len gates; the column
+ *          count becomes m + len.
+ * SEED_ERR_UNSUPPORTED for KDA (a gate per key channel) and for stochastic rounding.
+ * Source: picx.dev summary, "Exact Update (Lemma 2)" applied token after token, and
+ * "Theoretical and Practical Implications", Lemma 1 (each part follows the head's recurrence).
+ */
+int seed_decode_chunk(const seed_shape *shape, const seed_state *state, int32_t m, int32_t len,
+                      const void *q, const void *k, const void *v, const float *beta,
+                      const float *g, const float *vbar, void *o, void *stream);
+
+/* The largest len seed_decode_chunk takes. */
+int32_t seed_chunk_max_tokens(void);
+
+/*
  * Compression of the content back to rank r (leaves m = r; nothing is done when m <= r).
  * The content U V^T (m columns) is replaced by its best rank-r approximation, with
  * sqrt(sigma_i) on both factors; a becomes a_true, the decay scales 1 and the sink

@@ -44,7 +44,7 @@ GDN, KDA, MAMBA2 = 0, 1, 2
 
 __all__ = [
     "GDN", "KDA", "MAMBA2", "decay", "dense_step", "readout", "sink_split", "truncate",
-    "factored_step", "compress", "from_dense", "reconstruct", "decay_bound",
+    "factored_step", "factored_chunk", "compress", "from_dense", "reconstruct", "decay_bound",
     "corollary4_bound", "run_dense", "run_factored", "run_compressed", "singular_values",
     "relative_gap", "truncation_is_optimal", "state_bytes", "dense_state_bytes", "state_energy",
 ]
@@ -222,6 +222,22 @@ def run_factored(kind: int, a0, U0, V0, vbar, inputs: list):
         a, U, V, o = factored_step(kind, a, U, V, vbar, x["q"], x["k"], x["v"], x["beta"], x["g"])
         traj.append((a, U, V, o))
     return traj
+
+
+def factored_chunk(kind: int, a, U, V, vbar, inputs: list):
+    """A chunk of tokens on the factored state: the Lemma 2 step of each token in turn.
+
+    A chunked update is defined by the steps it stands for (picx.dev summary, "Exact Update
+    (Lemma 2)"; Lemma 1: the sink and the content follow the head's recurrence token by token),
+    so the oracle is the plain loop. Returns (a, U, V, outputs) after the last token; U and V
+    hold one more column per token, and outputs[t] is token t's read-out.
+    """
+    a, U, V = _f64(a).copy(), _f64(U).copy(), _f64(V).copy()
+    outs = []
+    for x in inputs:
+        a, U, V, o = factored_step(kind, a, U, V, vbar, x["q"], x["k"], x["v"], x["beta"], x["g"])
+        outs.append(o)
+    return a, U, V, outs
 
 
 def run_compressed(kind: int, S0, vbar, inputs: list, r: int, T: int):

@@ -2,8 +2,8 @@
 
 The library (libseed.so, hand-written HIP kernels behind a C ABI declared in include/seed.h)
 holds each Gated DeltaNet, Kimi Delta Attention or Mamba-2 head's recurrent state as a sink
-a vbar^T plus rank-r factors U V^T, runs the fused read-out + exact update per decode step,
-compresses back to rank r every T steps, and provides the dense-state step as a baseline.
+a vbar^T plus rank-r factors U V^T, runs the fused read-out + exact update per decode step (or
+per chunk of tokens), compresses back to rank r every T steps, and provides the dense-state step as a baseline.
 
 This package is the thin Python binding over that C ABI (rank_recurrent_state_amd._lib). The
 binding is loaded on first use of any of its names, and raises ImportError if libseed.so has
@@ -18,7 +18,7 @@ _NAMES = {
     "SeedError", "State", "make_shape",
     "column_counts", "seed_compress", "seed_compress_ragged", "seed_decode_step",
     "seed_decode_step_ragged", "seed_dense_decode_step", "seed_from_dense_iterations",
-    "seed_state_energy",
+    "seed_state_energy", "seed_decode_chunk", "seed_chunk_max_tokens",
     "seed_scale_len", "seed_shape", "seed_state", "seed_state_bytes", "seed_state_from_dense",
     "seed_status_string", "seed_version", "seed_workspace_bytes",
 }

@@ -22,8 +22,8 @@ SEED_OP_COMPRESS, SEED_OP_FROM_DENSE = 0, 1
 EXPORTS = [
     "seed_state_bytes", "seed_scale_len", "seed_workspace_bytes", "seed_state_from_dense",
     "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
-    "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_status_string",
-    "seed_version",
+    "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_decode_chunk",
+    "seed_chunk_max_tokens", "seed_status_string", "seed_version",
 ]
 
 
@@ -73,6 +73,9 @@ def _load():
         "seed_compress_ragged": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, ctypes.c_size_t, P]),
         "seed_state_energy": (ctypes.c_int, [Sp, Stp, P, P, P]),
         "seed_dense_decode_step": (ctypes.c_int, [Sp, P, P, P, P, P, P, P, P]),
+        "seed_decode_chunk": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P,
+                                             P, P]),
+        "seed_chunk_max_tokens": (ctypes.c_int32, []),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "seed_version": (ctypes.c_char_p, []),
     }
@@ -242,6 +245,28 @@ def seed_decode_step_ragged(shape: seed_shape, state, q, k, v, beta, g, vbar, o,
             raise ValueError(f"active: expected dtype torch.uint8, got {active.dtype}")
     _check("seed_decode_step_ragged", LIB.seed_decode_step_ragged(
         ctypes.byref(shape), _state_c(state), _ptr(active), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+        _ptr(g), _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_chunk_max_tokens() -> int:
+    return int(LIB.seed_chunk_max_tokens())
+
+
+def seed_decode_chunk(shape: seed_shape, state, m: int, length: int, q, k, v, beta, g, vbar, o,
+                      stream=None) -> None:
+    """`length` tokens of every unit in one call: q, k [batch, length, heads, d_k], v and o
+    [batch, length, heads, d_v], beta and g [batch, length, heads] (float32)."""
+    _expect_state(shape, state)
+    n = shape.units * length
+    _expect("q", q, n * shape.d_k, shape.io_dtype)
+    _expect("k", k, n * shape.d_k, shape.io_dtype)
+    _expect("v", v, n * shape.d_v, shape.io_dtype)
+    _expect("beta", beta, n, SEED_F32)
+    _expect("g", g, n, SEED_F32)
+    _expect("o", o, n * shape.d_v, shape.io_dtype)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    _check("seed_decode_chunk", LIB.seed_decode_chunk(
+        ctypes.byref(shape), _state_c(state), m, length, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
         _ptr(g), _ptr(vbar), _ptr(o), _stream_ptr(stream)))
 
 

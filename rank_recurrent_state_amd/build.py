@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libseed.so")
-SOURCES = ["api.cpp", "decode.hip", "dense.hip", "compress.hip", "compress_wave.hip", "energy.hip"]
+SOURCES = ["api.cpp", "decode.hip", "dense.hip", "compress.hip", "compress_wave.hip", "energy.hip", "chunk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

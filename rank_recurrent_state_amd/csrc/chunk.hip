@@ -1,0 +1,409 @@
+// Chunked factored update: L consecutive tokens of every unit in one call. It gives each
+// token's read-out and leaves the state that L decode steps would leave (equal in exact
+// arithmetic; the rounding order differs).
+//
+// Method: pages titled "Shallow Encoding Emits Deep Memories", picx.dev summary, "Exact Update
+// (Lemma 2)" (one token: a+ = g a + beta (omega - g kappa^T a) kappa, U+ = [g U, kappa],
+// V+ = [V, beta (eps - g V U^T kappa)]) and "Theoretical and Practical Implications", Lemma 1
+// (the sink coefficient and the content each follow the head's own recurrence). The pages give
+// the one-token form; unrolled over a chunk of L tokens t = 0 .. L-1 it reads
+//   Gamma(t, s) = prod_{s < u <= t} g_u (Gamma(t, t) = 1), gamma_t = Gamma(t, -1);
+//   S_t = gamma_t S_0 + sum_{s <= t} Gamma(t, s) kappa_s delta_s^T, delta_s = c_s vbar + w_s;
+//   (I + A) c = beta (omega - gamma a~ . kappa),  (I + A) W = beta (eps - gamma V (U~^T kappa)),
+//   A[t][s] = beta_t Gamma(t, s) kappa_t . kappa_s for s < t (Mamba-2: A = 0 and no state term);
+//   o_t = vbar (gamma_t a~ . q_t + sum_{s <= t} Gamma(t, s) (q_t . kappa_s) c_s)
+//         + gamma_t V (U~^T q_t) + sum_{s <= t} Gamma(t, s) (q_t . kappa_s) w_s,
+// with a~ and U~ the true (decayed) sink and columns at the start of the chunk. c_s and w_s are
+// the sink coefficient and V column that decode step s produces, so the chunk appends exactly
+// the columns of L steps: kappa_s to U with lazy decay scale Gamma(L-1, s), w_s to V, and c_s
+// to the sink coefficients; the decay scales held before the chunk take gamma_{L-1}.
+//
+// Design (gfx950): one 256-thread workgroup per unit; the scalar-decay kinds (GDN, Mamba-2).
+// The token count is padded to LM = 16 or 32 (a compiled width): the padding tokens have zero
+// inputs, so every loop runs to LM without a test, and only the stores look at L.
+//   staging      keys and queries of the chunk in LDS as fp32 (row stride d_k + 4: the
+//                pair products below read rows t and s in one access without bank conflicts);
+//   U pass       thread (j, w) holds column j of U and forms U~_j . kappa_t and U~_j . q_t for
+//                the tokens t = w, w + 4, ... (the key and query rows are LDS broadcasts);
+//   pair terms   kappa_t . kappa_s and q_t . kappa_s over the lower triangle, and the decay
+//                products Gamma(t, s) by running products;
+//   V pass       thread d of the first half owns value channel d: V (U~^T kappa) in registers,
+//                then the forward substitution for W (every thread its own channel, no
+//                exchange) and, alongside, for the scalar c (the same matrix); thread d of the
+//                second half forms V (U~^T q);
+//   read-out     the second half combines its V (U~^T q) with the residuals w_s + c_s vbar
+//                from LDS.
+// U and V are each read once; the chunk's keys become the new U columns unchanged (rounded to
+// the factor format), its W the new V columns.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace seed {
+
+namespace {
+
+constexpr int kChunkMax = 32;  // tokens per call
+constexpr int kColsMax = 64;   // column slots per unit
+
+template <int DK, int DV, int LM>
+struct ChunkSmem {
+  union {
+    alignas(16) float K[LM][DK + 4];  // the chunk's keys (until the pair terms are done)
+    alignas(16) float W[LM][DV];      // then the chunk's residuals delta_t = w_t + c_t vbar
+  };
+  alignas(16) float Q[LM][DK + 4];
+  alignas(16) float PK[kColsMax][LM];  // U~^T kappa_t (row j: column j of U)
+  alignas(16) float PQ[kColsMax][LM];  // U~^T q_t
+  float Gm[LM][LM + 1];                // Gm[t][s + 1] = Gamma(t, s), s = -1 .. t
+  float Akk[LM][LM + 1];               // A[t][s] = beta_t Gamma(t, s) kappa_t . kappa_s, s < t
+  float Aqk[LM][LM + 1];               // Gamma(t, s) q_t . kappa_s, s <= t
+  float vb[DV];
+  float a0[DK];
+  float g[LM], beta[LM], omega[LM], aK[LM], aQ[LM], c[LM];
+};
+
+}  // namespace
+
+template <int DK, int DV, bool DELTA, int FDT, int IDT, int LM>
+__global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
+  static_assert(DV <= 128 && DK <= 128 && LM % 4 == 0 && LM <= kChunkMax, "shapes");
+  using FT = stor_t<FDT>;
+  using IT = stor_t<IDT>;
+  __shared__ ChunkSmem<DK, DV, LM> S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t unit = blockIdx.x;
+  const int H = A.heads;
+  const int64_t bq = unit / H;
+  const int hd = static_cast<int>(unit - bq * H);
+  const int L = A.len, m = A.m, r = A.rank, C = A.slots;
+  float* __restrict__ sc = A.scale + unit * A.scale_len;
+  FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(C) * DK;
+  FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
+  // row of token t in the [batch][L][heads] layout of the chunk's inputs and outputs
+  auto tok = [&](int t) { return (bq * L + t) * H + hd; };
+
+  // ---- staging (padding tokens: zero inputs, zero pair terms) ---------------------------------
+  for (int i = tid; i < LM * (DK / 4); i += 256) {
+    const int t = i / (DK / 4), d = 4 * (i - t * (DK / 4));
+    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < L) {
+      load_f32<IDT, 4>(reinterpret_cast<const IT*>(A.k) + tok(t) * DK + d, x);
+      load_f32<IDT, 4>(reinterpret_cast<const IT*>(A.q) + tok(t) * DK + d, y);
+    }
+    *reinterpret_cast<float4*>(&S.K[t][d]) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(&S.Q[t][d]) = make_float4(y[0], y[1], y[2], y[3]);
+  }
+  for (int i = tid; i < kColsMax * LM; i += 256) {
+    (&S.PK[0][0])[i] = 0.f;
+    (&S.PQ[0][0])[i] = 0.f;
+  }
+  for (int i = tid; i < LM * (LM + 1); i += 256) {
+    (&S.Akk[0][0])[i] = 0.f;
+    (&S.Aqk[0][0])[i] = 0.f;
+    (&S.Gm[0][0])[i] = 0.f;
+  }
+  for (int i = tid; i < DV; i += 256) S.vb[i] = A.vbar[static_cast<int64_t>(hd) * DV + i];
+  for (int i = tid; i < DK; i += 256) S.a0[i] = A.a[unit * DK + i];
+  if (tid < LM) {
+    S.g[tid] = tid < L ? A.g[tok(tid)] : 0.f;
+    S.beta[tid] = tid < L ? A.beta[tok(tid)] : 0.f;
+    S.omega[tid] = 0.f;
+    S.aK[tid] = 0.f;
+    S.aQ[tid] = 0.f;
+  }
+  __syncthreads();
+
+  // ---- decay products, the new U columns, U~^T kappa and U~^T q, the value split ----------------
+  if (tid < L) {
+    const int t = tid;
+    float p = 1.f;
+    S.Gm[t][t + 1] = 1.f;
+    for (int s = t - 1; s >= -1; --s) {
+      p *= S.g[s + 1];
+      S.Gm[t][s + 1] = p;
+    }
+  }
+  for (int i = tid; i < L * (DK / 4); i += 256) {
+    const int t = i / (DK / 4), d = 4 * (i - t * (DK / 4));
+    const float4 x4 = *reinterpret_cast<const float4*>(&S.K[t][d]);
+    const float x[4] = {x4.x, x4.y, x4.z, x4.w};
+    store_f32<FDT, 4>(Ub + static_cast<int64_t>(m + t) * DK + d, x);
+  }
+  {
+    const int j = lane;  // column of U; tokens wv, wv + 4, ...
+    constexpr int TPW = LM / 4;
+    float pk[TPW], pq[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) { pk[i] = 0.f; pq[i] = 0.f; }
+    if (j < m) {
+      const FT* __restrict__ up = Ub + static_cast<int64_t>(j) * DK;
+      // the column in batches of 32 elements, all of a batch's loads in flight at once
+#pragma unroll 1
+      for (int d0 = 0; d0 < DK; d0 += 32) {
+        float u[4][8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) load_f32<FDT, 8>(up + d0 + 8 * c, u[c]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d = d0 + 8 * c;
+#pragma unroll
+          for (int i = 0; i < TPW; ++i) {
+            const int t = wv + 4 * i;
+            const float4 k0 = *reinterpret_cast<const float4*>(&S.K[t][d]);
+            const float4 k1 = *reinterpret_cast<const float4*>(&S.K[t][d + 4]);
+            const float4 q0 = *reinterpret_cast<const float4*>(&S.Q[t][d]);
+            const float4 q1 = *reinterpret_cast<const float4*>(&S.Q[t][d + 4]);
+            const float* uc = u[c];
+            pk[i] += uc[0] * k0.x + uc[1] * k0.y + uc[2] * k0.z + uc[3] * k0.w +
+                     uc[4] * k1.x + uc[5] * k1.y + uc[6] * k1.z + uc[7] * k1.w;
+            pq[i] += uc[0] * q0.x + uc[1] * q0.y + uc[2] * q0.z + uc[3] * q0.w +
+                     uc[4] * q1.x + uc[5] * q1.y + uc[6] * q1.z + uc[7] * q1.w;
+          }
+          __builtin_amdgcn_sched_barrier(0);  // the key and query reads of one slice at a time
+        }
+      }
+      // true columns: slot 0 scales the r columns kept by the last compression, slot 1 + i
+      // window column r + i
+      const float s = sc[j < r ? 0 : 1 + j - r];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int t = wv + 4 * i;
+        S.PK[j][t] = s * pk[i];
+        S.PQ[j][t] = s * pq[i];
+      }
+    }
+  }
+  {
+    // omega_t = v_t . vbar / |vbar|^2 (wave wv: tokens wv, wv + 4, ...)
+    constexpr int NB = DV / 64;
+    float nn = 0.f;
+#pragma unroll
+    for (int e = 0; e < NB; ++e) nn += S.vb[NB * lane + e] * S.vb[NB * lane + e];
+    nn = wave_sum(nn);
+    // every token's values first (the loads in flight together), then the sums
+    float vv[LM / 4][NB];
+#pragma unroll
+    for (int i = 0; i < LM / 4; ++i) {
+      const int t = wv + 4 * i;
+      load_f32<IDT, NB>(reinterpret_cast<const IT*>(A.v) + tok(t < L ? t : L - 1) * DV + NB * lane, vv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < LM / 4; ++i) {
+      const int t = wv + 4 * i;
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < NB; ++e) p += vv[i][e] * S.vb[NB * lane + e];
+      p = wave_sum(p);
+      if (lane == 0 && t < L) S.omega[t] = nn > 0.f ? p / nn : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- pair terms; the sink's share a~ . kappa_t and a~ . q_t ----------------------------------
+  const int npairs = L * (L + 1) / 2;
+  for (int p = tid; p < npairs; p += 256) {
+    int t = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+    while (t * (t + 1) / 2 > p) --t;
+    while ((t + 1) * (t + 2) / 2 <= p) ++t;
+    const int s = p - t * (t + 1) / 2;
+    float kk = 0.f, qk = 0.f;
+#pragma unroll 4
+    for (int d = 0; d < DK; d += 4) {
+      const float4 ks = *reinterpret_cast<const float4*>(&S.K[s][d]);
+      const float4 kt = *reinterpret_cast<const float4*>(&S.K[t][d]);
+      const float4 qt = *reinterpret_cast<const float4*>(&S.Q[t][d]);
+      kk += kt.x * ks.x + kt.y * ks.y + kt.z * ks.z + kt.w * ks.w;
+      qk += qt.x * ks.x + qt.y * ks.y + qt.z * ks.z + qt.w * ks.w;
+    }
+    const float G = S.Gm[t][s + 1];
+    S.Akk[t][s] = (DELTA && s < t) ? S.beta[t] * G * kk : 0.f;
+    S.Aqk[t][s] = G * qk;
+  }
+  {
+    // a~ = (slot-0 decay) a_0 + sum_{j >= r} c_j U~_j: lanes over channels for a_0, over
+    // columns for the window's coefficients
+    constexpr int NA = DK / 64;
+    const float s0 = sc[0];
+    const float cj = (lane >= r && lane < m) ? sc[A.coef_off + lane - r] : 0.f;
+    for (int t = wv; t < L; t += 4) {
+      float xk = 0.f, xq = 0.f;
+#pragma unroll
+      for (int e = 0; e < NA; ++e) {
+        xk += S.a0[NA * lane + e] * S.K[t][NA * lane + e];
+        xq += S.a0[NA * lane + e] * S.Q[t][NA * lane + e];
+      }
+      xk = s0 * xk + cj * S.PK[lane][t];
+      xq = s0 * xq + cj * S.PQ[lane][t];
+      xk = wave_sum(xk);
+      xq = wave_sum(xq);
+      if (lane == 0) {
+        S.aK[t] = xk;
+        S.aQ[t] = xq;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- V pass: W and c by forward substitution (first half), V (U~^T q) (second half) ---------
+  // Each half reads its channel of the m stored V columns, sixteen loads in flight at a time.
+  const int d = tid < DV ? tid : tid - DV;
+  auto v_times = [&](const float (*P)[LM], float (&acc)[LM]) {
+#pragma unroll
+    for (int t = 0; t < LM; ++t) acc[t] = 0.f;
+#pragma unroll 1
+    for (int j0 = 0; j0 < m; j0 += 16) {
+      // sixteen columns' loads in flight at once (a column past m reads column m - 1; its row of
+      // P is zero)
+      float vj[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vj[e] = to_f32<FDT>(Vb[static_cast<int64_t>(j0 + e < m ? j0 + e : m - 1) * DV + d]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+#pragma unroll
+        for (int t4 = 0; t4 < LM / 4; ++t4) {
+          const float4 p = *reinterpret_cast<const float4*>(&P[j0 + e][4 * t4]);
+          acc[4 * t4] = fmaf(vj[e], p.x, acc[4 * t4]);
+          acc[4 * t4 + 1] = fmaf(vj[e], p.y, acc[4 * t4 + 1]);
+          acc[4 * t4 + 2] = fmaf(vj[e], p.z, acc[4 * t4 + 2]);
+          acc[4 * t4 + 3] = fmaf(vj[e], p.w, acc[4 * t4 + 3]);
+        }
+        // one row of P at a time (hoisted, the rows' reads would take 512 registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  float y[LM];
+  if (tid < DV) {
+    // the chunk's values in this channel (a padding token reads token L - 1's; its beta is 0)
+    float vt[LM];
+#pragma unroll
+    for (int t = 0; t < LM; ++t)
+      vt[t] = to_f32<IDT>(reinterpret_cast<const IT*>(A.v)[tok(t < L ? t : L - 1) * DV + d]);
+    float x[LM];
+    if constexpr (DELTA) {
+      v_times(S.PK, x);
+    } else {
+#pragma unroll
+      for (int t = 0; t < LM; ++t) x[t] = 0.f;
+    }
+    // the content residuals w (this thread's channel) and the sink coefficients c (the same
+    // scalar system, solved by every thread of the half alongside its channel); padding tokens
+    // have beta = 0 and zero rows of A, so they solve to zero
+    const float vbd = S.vb[d];
+    float cc[LM];
+#pragma unroll
+    for (int t = 0; t < LM; ++t) {
+      const float bt = S.beta[t];
+      float w = bt * ((vt[t] - S.omega[t] * vbd) - (DELTA ? S.Gm[t][0] * x[t] : 0.f));
+      float ct = bt * (S.omega[t] - (DELTA ? S.Gm[t][0] * S.aK[t] : 0.f));
+      if constexpr (DELTA) {
+#pragma unroll
+        for (int s = 0; s < t; ++s) {
+          const float a = S.Akk[t][s];
+          w = fmaf(-a, x[s], w);
+          ct = fmaf(-a, cc[s], ct);
+        }
+        // finish the row here: left to itself the compiler sinks the arithmetic of every row
+        // to the stores below and holds all 528 entries of A in registers meanwhile
+        asm volatile("" : "+v"(w), "+v"(ct));
+      }
+      x[t] = w;
+      cc[t] = ct;
+    }
+    // K is dead (every reader of it is above the last barrier): the full residuals
+    // delta_t = w_t + c_t vbar go to LDS for the read-outs
+#pragma unroll
+    for (int t = 0; t < LM; ++t) {
+      S.W[t][d] = fmaf(cc[t], vbd, x[t]);
+      if (t < L) Vb[static_cast<int64_t>(m + t) * DV + d] = from_f32<FDT>(x[t]);
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int t = 0; t < LM; ++t) S.c[t] = cc[t];
+    }
+  } else if (tid < 2 * DV) {
+    v_times(S.PQ, y);
+  }
+  __syncthreads();
+
+  // ---- read-outs: o_t = vbar gamma_t a~ . q_t + gamma_t V (U~^T q_t) + sum_{s <= t}
+  // Gamma(t, s) (q_t . kappa_s) delta_s; then the decay scales, coefficients and column count --
+  if (tid >= DV && tid < 2 * DV) {
+    const float vbd = S.vb[d];
+#pragma unroll
+    for (int t = 0; t < LM; ++t) {
+      float o = S.Gm[t][0] * fmaf(vbd, S.aQ[t], y[t]);
+#pragma unroll
+      for (int s = 0; s <= t; ++s) o = fmaf(S.Aqk[t][s], S.W[s][d], o);
+      if (t < L) reinterpret_cast<IT*>(A.o)[tok(t) * DV + d] = from_f32<IDT>(o);
+    }
+  }
+  const float gL = S.Gm[L - 1][0];
+  if (tid <= m - r) sc[tid] *= gL;  // slot 0 and the window columns held before the chunk
+  if (tid < L) {
+    sc[1 + m + tid - r] = S.Gm[L - 1][tid + 1];
+    sc[A.coef_off + m + tid - r] = S.c[tid];
+  }
+  if (tid == 0) sc[A.m_off] = __uint_as_float(static_cast<uint32_t>(m + L));
+}
+
+namespace {
+using ChunkFn = void (*)(const StepArgs);
+
+template <int DK, int DV, bool DELTA, int LM>
+ChunkFn pick_chunk_dt(int fdt, int idt) {
+  if (idt == SEED_BF16) {
+    switch (fdt) {
+      case SEED_F32: return k_decode_chunk<DK, DV, DELTA, 0, 1, LM>;
+      case SEED_BF16: return k_decode_chunk<DK, DV, DELTA, 1, 1, LM>;
+      case SEED_F16: return k_decode_chunk<DK, DV, DELTA, 2, 1, LM>;
+      default: return nullptr;
+    }
+  }
+  if (idt == SEED_F32) {
+    switch (fdt) {
+      case SEED_F32: return k_decode_chunk<DK, DV, DELTA, 0, 0, LM>;
+      case SEED_BF16: return k_decode_chunk<DK, DV, DELTA, 1, 0, LM>;
+      default: return nullptr;
+    }
+  }
+  return nullptr;
+}
+
+template <bool DELTA, int LM>
+ChunkFn pick_chunk_dims(const seed_shape& sh) {
+  const int f = sh.factor_dtype, i = sh.io_dtype;
+  if (sh.d_k == 128 && sh.d_v == 128) return pick_chunk_dt<128, 128, DELTA, LM>(f, i);
+  if (sh.d_k == 128 && sh.d_v == 64) return pick_chunk_dt<128, 64, DELTA, LM>(f, i);
+  if (sh.d_k == 64 && sh.d_v == 128) return pick_chunk_dt<64, 128, DELTA, LM>(f, i);
+  if (sh.d_k == 64 && sh.d_v == 64) return pick_chunk_dt<64, 64, DELTA, LM>(f, i);
+  return nullptr;
+}
+
+template <int LM>
+ChunkFn pick_chunk_kind(const seed_shape& sh) {
+  if (sh.rank + sh.period > kColsMax) return nullptr;
+  if (sh.rounding != SEED_ROUND_NEAREST) return nullptr;
+  if (sh.kind == SEED_GDN) return pick_chunk_dims<true, LM>(sh);
+  if (sh.kind == SEED_MAMBA2) return pick_chunk_dims<false, LM>(sh);
+  return nullptr;  // KDA's per-channel gate: not on this path
+}
+
+ChunkFn pick_chunk(const seed_shape& sh, int len) {
+  return len <= 16 ? pick_chunk_kind<16>(sh) : pick_chunk_kind<32>(sh);
+}
+}  // namespace
+
+int32_t chunk_max_tokens() { return kChunkMax; }
+
+bool chunk_supported(const seed_shape& sh) { return pick_chunk(sh, kChunkMax) != nullptr; }
+
+hipError_t launch_decode_chunk(const seed_shape& sh, const StepArgs& a, hipStream_t s) {
+  ChunkFn fn = pick_chunk(sh, a.len);
+  if (!fn) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(a.units)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace seed

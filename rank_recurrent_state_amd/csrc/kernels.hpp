@@ -23,6 +23,7 @@ struct StepArgs {
   uint32_t rng_key;   // key of the stochastic-rounding draws
   int32_t ragged;     // 1: every unit's m is its own column count; 0: m above for all
   const uint8_t* active;  // ragged: units with active[u] == 0 are skipped (nullptr: none)
+  int32_t len;        // chunked update: tokens per call (q, k, v, beta, g, o are [batch][len][heads])
   float* a;
   void* U;
   void* V;
@@ -98,8 +99,13 @@ hipError_t launch_energy_wave(const seed_shape& sh, const EnergyArgs& a, hipStre
 // r + T <= 64); *used tells whether it took the call.
 hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used);
 
+// The chunked update of len tokens per unit (scalar-decay kinds, nearest rounding).
+hipError_t launch_decode_chunk(const seed_shape& sh, const StepArgs& a, hipStream_t s);
+int32_t chunk_max_tokens();
+
 // Whether a compiled instance exists for this shape (host-side dispatch tables).
 bool decode_supported(const seed_shape& sh);
 bool compress_supported(const seed_shape& sh);
+bool chunk_supported(const seed_shape& sh);
 
 }  // namespace seed

@@ -138,5 +138,24 @@ def test_invalid_arguments_are_rejected_on_the_host():
     with pytest.raises(rrs.SeedError) as e:
         rrs.seed_dense_decode_step(sh, _Fake(), _Fake(), _Fake(), _Fake(0), _Fake(), _Fake(), _Fake(), stream=0)
     assert e.value.status == rrs.SEED_ERR_ARG
+    # chunked update: 1 <= len <= 32, r <= m and m + len <= r + T; KDA and stochastic rounding
+    # are not compiled for it
+    assert rrs.seed_chunk_max_tokens() == 32
+
+    def chunk(shape, m, length, q=None):
+        with pytest.raises(rrs.SeedError) as e:
+            rrs.seed_decode_chunk(shape, st, m, length, q if q is not None else f, f, f, f, f, f, f, stream=0)
+        return e.value.status
+
+    assert chunk(sh, 16, 0) == rrs.SEED_ERR_ARG
+    assert chunk(sh, 16, 33) == rrs.SEED_ERR_ARG
+    assert chunk(sh, 15, 4) == rrs.SEED_ERR_ARG          # m < r
+    assert chunk(sh, 30, 3) == rrs.SEED_ERR_ARG          # 30 + 3 > r + T
+    assert chunk(sh, 16, 4, q=_Fake(0)) == rrs.SEED_ERR_ARG
+    kda = rrs.make_shape(rrs.SEED_KDA, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16)
+    assert chunk(kda, 16, 4) == rrs.SEED_ERR_UNSUPPORTED
+    srd = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16,
+                         rounding=rrs.SEED_ROUND_STOCHASTIC)
+    assert chunk(srd, 16, 4) == rrs.SEED_ERR_UNSUPPORTED
     for code in (0, -1, -2, -3, -4, 5):
         assert isinstance(rrs.seed_status_string(code), str)
