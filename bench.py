@@ -362,6 +362,27 @@ def main():
     log(f"[bench] energy diagnostic: {t_en * 1e3:.2f} ms over the stack at m = {m_now} "
         f"({en_bytes / t_en / 1e9:.0f} GB/s); sink share of the energy {sink_share:.3f}")
 
+    # ---- the content spectrum (not part of a step): one launch per layer ------------------------
+    spectrum = None
+    if w.factor_dtype != rrs.SEED_F32 and w.rank <= 32:
+        sp_out = [torch.empty((U1, rrs.SEED_SPECTRUM_LEN), dtype=torch.float32, device=dev) for _ in range(L)]
+        for l in range(L):
+            rrs.seed_state_spectrum(sh_l[l], states[l], out=sp_out[l])
+        s_a, s_b = ev(), ev()
+        torch.cuda.synchronize()
+        s_a.record()
+        for l in range(L):
+            rrs.seed_state_spectrum(sh_l[l], states[l], out=sp_out[l])
+        s_b.record()
+        torch.cuda.synchronize()
+        t_sp = s_a.elapsed_time(s_b) / 1e3
+        tot_c = float(sum(x[:, 32].double().sum() for x in sp_out))
+        kept = {k: float(sum(x[:, :k].double().sum() for x in sp_out)) / tot_c for k in (1, 4, 16)}
+        spectrum = {"ms_per_stack": t_sp * 1e3, "columns": m_now,
+                    "content_energy_share_top_k": {str(k): v for k, v in kept.items()}}
+        log(f"[bench] content spectrum: {t_sp * 1e3:.2f} ms over the stack at m = {m_now}; share of the "
+            f"content energy in the top 1 / 4 / 16 directions: {kept[1]:.3f} / {kept[4]:.3f} / {kept[16]:.3f}")
+
     # ---- the chunked update (not part of a step): len tokens per unit in one launch, on a copy
     # of layer 0's state, against len decode launches -----------------------------------------
     chunk = None
@@ -490,6 +511,7 @@ def main():
         "setup_s": {"prefill_end_compression": t_from_dense},
         "energy_diagnostic": {"ms_per_stack": t_en * 1e3, "columns": m_now, "gbs": en_bytes / t_en / 1e9,
                               "sink_share": sink_share},
+        "spectrum_diagnostic": spectrum,
         "chunked_update": chunk,
     }
     print(json.dumps(res), flush=True)

@@ -198,6 +198,23 @@ int seed_decode_step_ragged(const seed_shape *shape, const seed_state *state,
                             const float *beta, const float *g, const float *vbar, void *o,
                             void *stream);
 
+/* Floats per unit written by seed_state_spectrum. */
+#define SEED_SPECTRUM_LEN 33
+
+/*
+ * Rank-energy spectrum of the content, per unit at its own column count m (taken from the
+ * state): out[u][i] for i < 32 is sigma_i^2, the i-th largest squared singular value of
+ * U V^T (true, decayed columns; zero past its rank), and out[u][32] is |U V^T|_F^2 = sum over
+ * all i of sigma_i^2. So out[u][32] - sum_{i<k} out[u][i] is the energy that a rank-k
+ * truncation would drop. The sink a vbar^T is not part of it (its share: seed_state_energy).
+ *   out    float [units][SEED_SPECTRUM_LEN], device memory, written.
+ * Reads the state and writes nothing else. 16-bit factors with rank <= 32 (the compression
+ * kernel's core, stopped after its eigenvalues); otherwise SEED_ERR_UNSUPPORTED.
+ * Source: picx.dev summary, key finding 2 (after the sink the remaining content is low-rank),
+ * and thelatestinai.com figures & tables, overview table (the rest of the state is low-rank).
+ */
+int seed_state_spectrum(const seed_shape *shape, const seed_state *state, float *out, void *stream);
+
 /*
  * Chunked update: len consecutive tokens of every unit in one call (GDN and Mamba-2).
  * It appends the len columns and writes the len read-outs that len calls of seed_decode_step

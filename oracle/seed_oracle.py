@@ -47,6 +47,7 @@ __all__ = [
     "factored_step", "factored_chunk", "compress", "from_dense", "reconstruct", "decay_bound",
     "corollary4_bound", "run_dense", "run_factored", "run_compressed", "singular_values",
     "relative_gap", "truncation_is_optimal", "state_bytes", "dense_state_bytes", "state_energy",
+    "content_spectrum",
 ]
 
 
@@ -327,3 +328,19 @@ def state_energy(a, vbar, U, V):
     content = U @ V.T
     S = sink + content
     return float(np.sum(S * S)), float(np.sum(sink * sink)), float(np.sum(content * content))
+
+
+def content_spectrum(U, V, k: int = 32):
+    """Rank-energy spectrum of the content C = U V^T: (sigma_1^2 .. sigma_k^2, |C|_F^2).
+
+    picx.dev summary, key finding 2, and thelatestinai.com figures & tables, overview table:
+    after the sink, the rest of the state is low-rank, i.e. its energy sits in few singular
+    directions. The squared singular values, largest first (zeros past the rank), and the total
+    squared Frobenius norm, from the explicit matrix.
+    """
+    C = _f64(U) @ _f64(V).T
+    s = np.linalg.svd(C, compute_uv=False) if C.size else np.zeros(0)
+    out = np.zeros(k)
+    n = min(k, s.size)
+    out[:n] = s[:n] ** 2
+    return out, float(np.sum(C * C))

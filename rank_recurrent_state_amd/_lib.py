@@ -23,8 +23,10 @@ EXPORTS = [
     "seed_state_bytes", "seed_scale_len", "seed_workspace_bytes", "seed_state_from_dense",
     "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
     "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_decode_chunk",
-    "seed_chunk_max_tokens", "seed_status_string", "seed_version",
+    "seed_chunk_max_tokens", "seed_state_spectrum", "seed_status_string", "seed_version",
 ]
+
+SEED_SPECTRUM_LEN = 33
 
 
 class seed_shape(ctypes.Structure):
@@ -76,6 +78,7 @@ def _load():
         "seed_decode_chunk": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P,
                                              P, P]),
         "seed_chunk_max_tokens": (ctypes.c_int32, []),
+        "seed_state_spectrum": (ctypes.c_int, [Sp, Stp, P, P]),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "seed_version": (ctypes.c_char_p, []),
     }
@@ -246,6 +249,19 @@ def seed_decode_step_ragged(shape: seed_shape, state, q, k, v, beta, g, vbar, o,
     _check("seed_decode_step_ragged", LIB.seed_decode_step_ragged(
         ctypes.byref(shape), _state_c(state), _ptr(active), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
         _ptr(g), _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_state_spectrum(shape: seed_shape, state, out=None, stream=None):
+    """Per unit the 32 largest squared singular values of the content U V^T, then |U V^T|^2,
+    as a float32 [units, 33] device tensor."""
+    import torch
+    _expect_state(shape, state)
+    if out is None:
+        out = torch.empty((shape.units, SEED_SPECTRUM_LEN), dtype=torch.float32, device=state.a.device)
+    _expect("out", out, shape.units * SEED_SPECTRUM_LEN, SEED_F32)
+    _check("seed_state_spectrum", LIB.seed_state_spectrum(ctypes.byref(shape), _state_c(state), _ptr(out),
+                                                          _stream_ptr(stream)))
+    return out
 
 
 def seed_chunk_max_tokens() -> int:

@@ -238,6 +238,17 @@ int seed_state_energy(const seed_shape* sh, const seed_state* st, const float* v
   return hip_status(seed::launch_energy(*sh, a, static_cast<hipStream_t>(stream)));
 }
 
+int seed_state_spectrum(const seed_shape* sh, const seed_state* st, float* out, void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st) || !out) return SEED_ERR_ARG;
+  // the one-wavefront compression kernel's eigen phase: 16-bit factors, r <= 32
+  if (sh->factor_dtype == SEED_F32 || sh->rank > SEED_SPECTRUM_LEN - 1) return SEED_ERR_UNSUPPORTED;
+  seed::CompressArgs a = compress_args(sh, st, 0);
+  a.spectrum = out;
+  return hip_status(seed::launch_spectrum(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
 int seed_dense_decode_step(const seed_shape* sh, float* S, const void* q, const void* k,
                            const void* v, const float* beta, const float* g, void* o,
                            void* stream) {

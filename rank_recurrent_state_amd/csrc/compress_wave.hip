@@ -431,7 +431,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   const int r = A.rank, C = A.slots;
   float* __restrict__ sc = A.scale + unit * A.scale_len;
   int m = A.m;
-  if (A.ragged) {
+  // spectrum mode (the diagnostic of seed_state_spectrum): every unit at its own column count,
+  // the eigenvalues written out, the state left untouched
+  float* __restrict__ spec = A.spectrum;
+  if (spec != nullptr) {
+    const uint32_t mu = __float_as_uint(sc[A.m_off]);
+    m = mu > static_cast<uint32_t>(C) ? C : static_cast<int>(mu);
+    if (m == 0) {
+      if (lane <= RX) spec[unit * (RX + 1) + lane] = 0.f;
+      return;
+    }
+  } else if (A.ragged) {
     // only the units whose own column count reached A.m (and holds columns beyond r)
     const int mu = static_cast<int>(__float_as_uint(sc[A.m_off]));
     if (mu < A.m || mu <= r || mu > C) return;
@@ -647,7 +657,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   wave_lds_sync();
 
   // ---- the rr largest eigenvalues by Sturm-count multisection --------------------------------------
-  const int rr = r < k ? r : k;
+  const int rr = spec != nullptr ? (RX < k ? RX : k) : (r < k ? r : k);
   float lam;
   {
     const float di = S.dg[row], ei = S.e[row], em = row > 0 ? S.e[row - 1] : 0.f;
@@ -691,6 +701,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       hi = fminf(hi, fminf(chi, partner(chi)));
     }
     lam = 0.5f * (lo + hi);
+  }
+  if (spec != nullptr) {
+    // the RX largest eigenvalues of B (sigma_i^2 of U V^T; zero past the core's rank), then
+    // their total, the trace (Householder keeps it: the sum of the tridiagonal's diagonal)
+    float tr = S.dg[row];   // rows of unchosen pivots are zero
+    tr = N == 64 ? wave_sum(tr) : group_sum<32>(tr);
+    if (lane < RX) spec[unit * (RX + 1) + lane] = c32 < rr ? fmaxf(lam, 0.f) * bs : 0.f;
+    if (lane == 0) spec[unit * (RX + 1) + RX] = fmaxf(tr, 0.f) * bs;
+    return;
   }
 
   // ---- eigenvectors of the tridiagonal: twisted factorisation per eigenvalue ------------------
@@ -1222,6 +1241,15 @@ WaveFn pick_compress_wave(const seed_shape& sh) {
   return nullptr;
 }
 }  // namespace
+
+hipError_t launch_spectrum(const seed_shape& sh, const CompressArgs& a, hipStream_t s) {
+  seed_shape nr = sh;
+  nr.rounding = SEED_ROUND_NEAREST;  // no store is made: the nearest-rounding instance serves
+  WaveFn fn = pick_compress_wave(nr);
+  if (!fn) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(a.units)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hipStream_t s, bool* used) {
   WaveFn fn = pick_compress_wave(sh);

@@ -68,6 +68,7 @@ struct CompressArgs {
   const float* S;     // from_dense only: dense states
   const float* vbar;  // from_dense only
   int32_t iters;      // from_dense only: subspace iterations (128 x 128 states)
+  float* spectrum;    // spectrum mode only ([units][33]): the state is read, not written
 };
 
 struct EnergyArgs {
@@ -102,6 +103,8 @@ hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hip
 // The chunked update of len tokens per unit (scalar-decay kinds, nearest rounding).
 hipError_t launch_decode_chunk(const seed_shape& sh, const StepArgs& a, hipStream_t s);
 int32_t chunk_max_tokens();
+// The content spectrum (spectrum mode of the one-wavefront compression kernel).
+hipError_t launch_spectrum(const seed_shape& sh, const CompressArgs& a, hipStream_t s);
 
 // Whether a compiled instance exists for this shape (host-side dispatch tables).
 bool decode_supported(const seed_shape& sh);

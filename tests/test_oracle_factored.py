@@ -119,3 +119,32 @@ def test_state_energy_pins():
     # a cross term that does not vanish: the total is not the sum of the parts
     tot, sink, cont = orc.state_energy([1.0, 0.0], [1.0, 0.0], np.array([[1.0], [0.0]]), np.array([[1.0], [0.0]]))
     assert (tot, sink, cont) == (4.0, 1.0, 1.0)
+
+
+def test_content_spectrum_pins():
+    """The spectrum of the content: a planted spectrum (random orthonormal singular vectors,
+    chosen singular values) comes back exactly; a worked rank-one case; the total is the sum of
+    all squared singular values (Frobenius); past the rank the values are at the rounding level,
+    and past the matrix's smaller dimension they are zero."""
+    g = np.random.default_rng(11)
+    sig = np.array([5.0, 3.0, 2.0, 0.5, 0.25])
+    Y, _ = np.linalg.qr(g.standard_normal((9, 5)))
+    Z, _ = np.linalg.qr(g.standard_normal((7, 5)))
+    U = Y * sig                                     # C = Y diag(sig) Z^T, split as U V^T
+    spec, tot = orc.content_spectrum(U, Z, k=8)
+    np.testing.assert_allclose(spec[:5], sig ** 2, rtol=1e-12)
+    assert np.all(spec[5:7] < 1e-24 * float(np.sum(sig ** 2)))   # rank 5: rounding-level values
+    assert spec[7] == 0.0                                          # past min(9, 7): zero
+    assert tot == pytest.approx(float(np.sum(sig ** 2)), rel=1e-12)
+    # rank one: u v^T has the single singular value |u| |v|
+    spec, tot = orc.content_spectrum(np.array([[3.0], [4.0]]), np.array([[1.0], [0.0], [0.0]]), k=3)
+    np.testing.assert_allclose(spec, [25.0, 0.0, 0.0], atol=1e-12)
+    assert tot == pytest.approx(25.0)
+    # more columns than the rank: 6 columns spanning 2 directions
+    A = g.standard_normal((8, 2)) @ g.standard_normal((2, 6))
+    B = g.standard_normal((5, 6))
+    spec, tot = orc.content_spectrum(A, B, k=4)
+    C = A @ B.T
+    assert tot == pytest.approx(float(np.sum(C * C)), rel=1e-12)
+    assert spec[0] + spec[1] == pytest.approx(tot, rel=1e-10)
+    assert spec[2] < 1e-20 * tot and spec[3] < 1e-20 * tot
