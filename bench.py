@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--workload", default="gdn-stack36")
     ap.add_argument("--factor-dtype", choices=["fp32", "bf16", "fp16"], default=None,
                     help="factor storage other than the workload's own (fp16: with bf16 inputs)")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="skip the overlapped-schedule measurement (decode and compression on "
+                         "disjoint XCDs, compressions shifted per layer)")
     ap.add_argument("--rounding", choices=["nearest", "stochastic"], default="nearest",
                     help="rounding of the 16-bit factor stores")
     ap.add_argument("--staggered", action="store_true",
@@ -423,6 +426,10 @@ def main():
                 f"launches)")
         del st_c
 
+    # ---- the overlapped schedule (reported beside the lockstep step) ---------------------------
+    overlapped = None if args.no_overlap else run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T,
+                                                            P, ev, log)
+
     # ---- dense-state baseline ----------------------------------------------------------------
     KD = args.dense_steps
     d_ev = [(ev(), ev()) for _ in range(KD)]
@@ -511,10 +518,103 @@ def main():
         "setup_s": {"prefill_end_compression": t_from_dense},
         "energy_diagnostic": {"ms_per_stack": t_en * 1e3, "columns": m_now, "gbs": en_bytes / t_en / 1e9,
                               "sink_share": sink_share},
+        "overlapped_schedule": overlapped,
         "spectrum_diagnostic": spectrum,
         "chunked_update": chunk,
     }
     print(json.dumps(res), flush=True)
+
+
+def _partition_streams(torch, split):
+    """Two streams on disjoint sets of XCDs (CU masks of whole 32-CU blocks; masks that split an
+    XCD were refused by the runtime here): the decode on the first `split` XCDs, the compression
+    on the rest. None when the runtime does not provide them."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    words = (ncu + 31) // 32
+    out = []
+    for pick in (lambda i: i // 32 < split, lambda i: i // 32 >= split):
+        mask = (ctypes.c_uint32 * words)()
+        for i in range(ncu):
+            if pick(i):
+                mask[i // 32] |= 1 << (i % 32)
+        h = ctypes.c_void_p()
+        if hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), mask) != 0:
+            return None
+        out.append(torch.cuda.ExternalStream(h.value))
+    return out
+
+
+def run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T, P, ev, log, steps=64, split=4):
+    """The same work as the lockstep step, with the compressions overlapped with the decode.
+
+    Decode is bound by HBM bandwidth, compression by vector arithmetic, so they can share the
+    chip: the decode launches go to a stream on half of the XCDs, each layer's compression to a
+    stream on the other half. Layer l's compression window is shifted by l mod T steps, so that
+    every step compresses one or two layers instead of every layer compressing on the same step.
+    Layer l's compression waits for its T-th decode launch (an event), and its next decode
+    launch waits for the compression. Every layer still decodes every step and compresses every
+    T steps at r + T columns. Returns ms per step and head-steps/s, or None."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        return None
+    streams = _partition_streams(torch, split)
+    if streams is None:
+        log("[bench] overlapped schedule: CU-masked streams not available, skipped")
+        return None
+    sA, sB = streams
+    cur = torch.cuda.current_stream()
+    # layer l's window starts at step l mod T: layers that share a start (l and l + T) are T
+    # launches apart in the step, so the first compression is done before the second starts
+    phase = [l % T for l in range(L)]
+    pending = [None] * L
+
+    def run(s0, n):
+        for s in range(s0, s0 + n):
+            xl = pool[s % P]
+            for l in range(L):
+                m = w.rank + (s - phase[l]) % T
+                if pending[l] is not None:
+                    sA.wait_event(pending[l])
+                    pending[l] = None
+                x = xl[l]
+                rrs.seed_decode_step(sh_l[l], states[l], m, x["q"], x["k"], x["v"], x["beta"], x["g"],
+                                     vbars[l], o[l], stream=sA)
+                if m + 1 == w.rank + T:
+                    e = torch.cuda.Event()
+                    e.record(sA)
+                    sB.wait_event(e)
+                    rrs.seed_compress(sh_l[l], states[l], w.rank + T, stream=sB)
+                    ec = torch.cuda.Event()
+                    ec.record(sB)
+                    pending[l] = ec
+
+    sA.wait_stream(cur)
+    sB.wait_stream(cur)
+    run(0, T)                      # warmup: brings every layer onto its shifted window
+    e0, e1 = ev(), ev()
+    cur.wait_stream(sA)
+    cur.wait_stream(sB)
+    torch.cuda.synchronize()
+    e0.record(cur)
+    sA.wait_stream(cur)
+    sB.wait_stream(cur)
+    run(T, steps)
+    cur.wait_stream(sA)
+    cur.wait_stream(sB)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3
+    units = sum(sh.units for sh in sh_l)
+    res = {"ms_per_step": t / steps * 1e3, "head_steps_per_s": units * steps / t, "steps": steps,
+           "decode_xcds": split, "compress_xcds": 8 - split}
+    log(f"[bench] overlapped schedule (decode on {split} XCDs, per-layer compressions shifted over the "
+        f"window on the other {8 - split}): {res['ms_per_step']:.3f} ms per step, "
+        f"{res['head_steps_per_s'] / 1e6:.1f} M head-steps/s")
+    return res
 
 
 def run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vbars, o, prefill, N,
