@@ -216,26 +216,29 @@ int seed_decode_step_ragged(const seed_shape *shape, const seed_state *state,
 int seed_state_spectrum(const seed_shape *shape, const seed_state *state, float *out, void *stream);
 
 /*
- * Chunked update: len consecutive tokens of every unit in one call (GDN and Mamba-2).
+ * Chunked update: len consecutive tokens of every unit in one call.
  * It appends the len columns and writes the len read-outs that len calls of seed_decode_step
  * would give for the same inputs (equal in exact arithmetic; fp32 arithmetic in another order).
  * Each token's value residual is found by a forward substitution over the chunk:
  * (I + A) [c | W] = beta (omega - gamma a~ . kappa | eps - gamma V U~^T kappa), with
  * A[t][s] = beta_t Gamma(t,s) kappa_t . kappa_s (s < t) and Gamma(t,s) the product of the gates
- * after token s up to token t (Mamba-2: A = 0).
+ * after token s up to token t (Mamba-2: A = 0; KDA: the gates are per key channel, so
+ * kappa_t . kappa_s is weighted by each channel's product of gates).
  *   m      columns held before the chunk, rank <= m and m + len <= rank + period.
- *   len    tokens, 1 <= len <= 32.
+ *   len    tokens, 1 <= len <= 32 (KDA: 16; a longer KDA chunk is SEED_ERR_UNSUPPORTED).
  *   q, k   [batch][len][heads][d_k] (io_dtype), v [batch][len][heads][d_v]: token t of unit
  *          (b, h) is row (b len + t) heads + h, the layout of a projection over a batch of
  *          sequences.
- *   beta, g float [batch][len][heads] (one scalar gate per token).
+ *   beta   float [batch][len][heads]. g: float [batch][len][heads] (GDN, Mamba-2) or
+ *          [batch][len][heads][d_k] (KDA).
  *   vbar   float [heads][d_v].
  *   o      written, [batch][len][heads][d_v] (io_dtype): token t's read-out S_t^T q_t.
  *   state  as after len decode steps: the keys become columns m .. m + len - 1 of U (decay
  *          scale: the gates of the later tokens), W columns m .. of V, c their sink
  *          coefficients; the scales held before take the product of all len gates; the column
- *          count becomes m + len.
- * SEED_ERR_UNSUPPORTED for KDA (a gate per key channel) and for stochastic rounding.
+ *          count becomes m + len. KDA: a channel whose scale would fall below the floor of
+ *          seed_decode_step is folded into the stored columns and a as there.
+ * SEED_ERR_UNSUPPORTED for stochastic rounding.
  * Source: picx.dev summary, "Exact Update (Lemma 2)" applied token after token, and
  * "Theoretical and Practical Implications", Lemma 1 (each part follows the head's recurrence).
  */

@@ -271,14 +271,15 @@ def seed_chunk_max_tokens() -> int:
 def seed_decode_chunk(shape: seed_shape, state, m: int, length: int, q, k, v, beta, g, vbar, o,
                       stream=None) -> None:
     """`length` tokens of every unit in one call: q, k [batch, length, heads, d_k], v and o
-    [batch, length, heads, d_v], beta and g [batch, length, heads] (float32)."""
+    [batch, length, heads, d_v], beta [batch, length, heads] and g [batch, length, heads]
+    (KDA: [batch, length, heads, d_k]), float32."""
     _expect_state(shape, state)
     n = shape.units * length
     _expect("q", q, n * shape.d_k, shape.io_dtype)
     _expect("k", k, n * shape.d_k, shape.io_dtype)
     _expect("v", v, n * shape.d_v, shape.io_dtype)
     _expect("beta", beta, n, SEED_F32)
-    _expect("g", g, n, SEED_F32)
+    _expect("g", g, n * (shape.d_k if shape.kind == SEED_KDA else 1), SEED_F32)
     _expect("o", o, n * shape.d_v, shape.io_dtype)
     _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
     _check("seed_decode_chunk", LIB.seed_decode_chunk(

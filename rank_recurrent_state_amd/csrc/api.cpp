@@ -8,6 +8,7 @@
 
 namespace seed {
 int32_t from_dense_iterations();
+bool chunk_supported_len(const seed_shape& sh, int32_t len);  // chunk.hip: KDA takes up to 16 tokens
 }
 
 namespace {
@@ -191,7 +192,7 @@ int seed_decode_chunk(const seed_shape* sh, const seed_state* st, int32_t m, int
   if (!state_ok(st) || !q || !k || !v || !beta || !g || !vbar || !o) return SEED_ERR_ARG;
   if (len < 1 || len > seed::chunk_max_tokens()) return SEED_ERR_ARG;
   if (m < sh->rank || m + len > sh->rank + sh->period) return SEED_ERR_ARG;
-  if (!seed::chunk_supported(*sh)) return SEED_ERR_UNSUPPORTED;
+  if (!seed::chunk_supported_len(*sh, len)) return SEED_ERR_UNSUPPORTED;
   seed::StepArgs a = step_args(sh, st, m, nullptr, false);
   a.len = len;
   a.q = q;

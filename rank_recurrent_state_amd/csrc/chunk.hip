@@ -42,10 +42,11 @@ namespace seed {
 
 namespace {
 
-constexpr int kChunkMax = 32;  // tokens per call
+constexpr int kChunkMax = 32;      // tokens per call
+constexpr int kChunkMaxDiag = 16;  // tokens per call, KDA
 constexpr int kColsMax = 64;   // column slots per unit
 
-template <int DK, int DV, int LM>
+template <int DK, int DV, int LM, bool DIAG>
 struct ChunkSmem {
   union {
     alignas(16) float K[LM][DK + 4];  // the chunk's keys (until the pair terms are done)
@@ -60,16 +61,27 @@ struct ChunkSmem {
   float vb[DV];
   float a0[DK];
   float g[LM], beta[LM], omega[LM], aK[LM], aQ[LM], c[LM];
+  // KDA only: the gates, and the keys and queries decayed to the chunk's start and through the
+  // state's own channel scales (Gamma P_t kappa_t, Gamma P_t q_t)
+  float Al[DIAG ? LM : 1][DIAG ? DK : 1];
+  alignas(16) float Kh[DIAG ? LM : 1][DIAG ? DK + 4 : 4];
+  alignas(16) float Qh[DIAG ? LM : 1][DIAG ? DK + 4 : 4];
 };
+
+// KDA: a channel whose scale would fall below this is folded into the stored columns (as in the
+// decode step), so that a new column k / scale stays finite in the factor format
+template <int FDT> constexpr float kChunkFoldFloor = 0x1p-40f;
+template <> constexpr float kChunkFoldFloor<2> = 0x1p-12f;
 
 }  // namespace
 
-template <int DK, int DV, bool DELTA, int FDT, int IDT, int LM>
+template <int DK, int DV, bool DELTA, bool DIAG, int FDT, int IDT, int LM>
 __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   static_assert(DV <= 128 && DK <= 128 && LM % 4 == 0 && LM <= kChunkMax, "shapes");
+  static_assert(!DIAG || DELTA, "the diagonal gate comes with the delta rule (KDA)");
   using FT = stor_t<FDT>;
   using IT = stor_t<IDT>;
-  __shared__ ChunkSmem<DK, DV, LM> S;
+  __shared__ ChunkSmem<DK, DV, LM, DIAG> S;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int64_t unit = blockIdx.x;
@@ -105,8 +117,15 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   }
   for (int i = tid; i < DV; i += 256) S.vb[i] = A.vbar[static_cast<int64_t>(hd) * DV + i];
   for (int i = tid; i < DK; i += 256) S.a0[i] = A.a[unit * DK + i];
+  if constexpr (DIAG) {
+    // the gates, one per key channel ([batch][L][heads][d_k]); padding tokens keep 1
+    for (int i = tid; i < LM * DK; i += 256) {
+      const int t = i / DK, dd = i - t * DK;
+      S.Al[t][dd] = t < L ? A.g[tok(t) * DK + dd] : 1.f;
+    }
+  }
   if (tid < LM) {
-    S.g[tid] = tid < L ? A.g[tok(tid)] : 0.f;
+    S.g[tid] = (!DIAG && tid < L) ? A.g[tok(tid)] : 0.f;
     S.beta[tid] = tid < L ? A.beta[tok(tid)] : 0.f;
     S.omega[tid] = 0.f;
     S.aK[tid] = 0.f;
@@ -115,21 +134,45 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   __syncthreads();
 
   // ---- decay products, the new U columns, U~^T kappa and U~^T q, the value split ----------------
-  if (tid < L) {
-    const int t = tid;
-    float p = 1.f;
-    S.Gm[t][t + 1] = 1.f;
-    for (int s = t - 1; s >= -1; --s) {
-      p *= S.g[s + 1];
-      S.Gm[t][s + 1] = p;
+  if constexpr (DIAG) {
+    // channel d: P_t = prod_{u <= t} alpha_u (running), the true-state keys and queries
+    // Gamma P_t kappa_t, Gamma P_t q_t for the terms of the state held before the chunk
+    for (int dd = tid; dd < DK; dd += 256) {
+      float p = sc[dd];
+      for (int t = 0; t < LM; ++t) {
+        p *= S.Al[t][dd];
+        S.Kh[t][dd] = p * S.K[t][dd];
+        S.Qh[t][dd] = p * S.Q[t][dd];
+      }
+    }
+    __syncthreads();
+  } else {
+    if (tid < L) {
+      const int t = tid;
+      float p = 1.f;
+      S.Gm[t][t + 1] = 1.f;
+      for (int s = t - 1; s >= -1; --s) {
+        p *= S.g[s + 1];
+        S.Gm[t][s + 1] = p;
+      }
+    }
+    for (int i = tid; i < L * (DK / 4); i += 256) {
+      const int t = i / (DK / 4), d = 4 * (i - t * (DK / 4));
+      const float4 x4 = *reinterpret_cast<const float4*>(&S.K[t][d]);
+      const float x[4] = {x4.x, x4.y, x4.z, x4.w};
+      store_f32<FDT, 4>(Ub + static_cast<int64_t>(m + t) * DK + d, x);
     }
   }
-  for (int i = tid; i < L * (DK / 4); i += 256) {
-    const int t = i / (DK / 4), d = 4 * (i - t * (DK / 4));
-    const float4 x4 = *reinterpret_cast<const float4*>(&S.K[t][d]);
-    const float x[4] = {x4.x, x4.y, x4.z, x4.w};
-    store_f32<FDT, 4>(Ub + static_cast<int64_t>(m + t) * DK + d, x);
-  }
+  // the keys and queries the U pass uses: as given (the slot scales apply per column), or KDA's
+  // decayed ones
+  auto krow = [&](int t) -> const float* {
+    if constexpr (DIAG) return &S.Kh[t][0];
+    else return &S.K[t][0];
+  };
+  auto qrow = [&](int t) -> const float* {
+    if constexpr (DIAG) return &S.Qh[t][0];
+    else return &S.Q[t][0];
+  };
   {
     const int j = lane;  // column of U; tokens wv, wv + 4, ...
     constexpr int TPW = LM / 4;
@@ -150,10 +193,10 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
 #pragma unroll
           for (int i = 0; i < TPW; ++i) {
             const int t = wv + 4 * i;
-            const float4 k0 = *reinterpret_cast<const float4*>(&S.K[t][d]);
-            const float4 k1 = *reinterpret_cast<const float4*>(&S.K[t][d + 4]);
-            const float4 q0 = *reinterpret_cast<const float4*>(&S.Q[t][d]);
-            const float4 q1 = *reinterpret_cast<const float4*>(&S.Q[t][d + 4]);
+            const float4 k0 = *reinterpret_cast<const float4*>(krow(t) + d);
+            const float4 k1 = *reinterpret_cast<const float4*>(krow(t) + d + 4);
+            const float4 q0 = *reinterpret_cast<const float4*>(qrow(t) + d);
+            const float4 q1 = *reinterpret_cast<const float4*>(qrow(t) + d + 4);
             const float* uc = u[c];
             pk[i] += uc[0] * k0.x + uc[1] * k0.y + uc[2] * k0.z + uc[3] * k0.w +
                      uc[4] * k1.x + uc[5] * k1.y + uc[6] * k1.z + uc[7] * k1.w;
@@ -165,7 +208,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
       }
       // true columns: slot 0 scales the r columns kept by the last compression, slot 1 + i
       // window column r + i
-      const float s = sc[j < r ? 0 : 1 + j - r];
+      const float s = DIAG ? 1.f : sc[j < r ? 0 : 1 + j - r];
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int t = wv + 4 * i;
@@ -201,7 +244,36 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   __syncthreads();
 
   // ---- pair terms; the sink's share a~ . kappa_t and a~ . q_t ----------------------------------
-  const int npairs = L * (L + 1) / 2;
+  if constexpr (DIAG) {
+    // Gamma(t, s) is a vector here: wave wv takes s = wv, wv + 4, ..., runs t up from s with
+    // the running product of the gates per channel (lanes over channels) and sums over them
+    constexpr int NA = DK / 64;
+    for (int s = wv; s < L; s += 4) {
+      float G[NA], ks[NA];
+#pragma unroll
+      for (int e = 0; e < NA; ++e) {
+        G[e] = 1.f;
+        ks[e] = S.K[s][NA * lane + e];
+      }
+      for (int t = s; t < L; ++t) {
+        float kk = 0.f, qk = 0.f;
+#pragma unroll
+        for (int e = 0; e < NA; ++e) {
+          if (t > s) G[e] *= S.Al[t][NA * lane + e];
+          const float gk = G[e] * ks[e];
+          kk = fmaf(S.K[t][NA * lane + e], gk, kk);
+          qk = fmaf(S.Q[t][NA * lane + e], gk, qk);
+        }
+        kk = wave_sum(kk);
+        qk = wave_sum(qk);
+        if (lane == 0) {
+          S.Akk[t][s] = s < t ? S.beta[t] * kk : 0.f;
+          S.Aqk[t][s] = qk;
+        }
+      }
+    }
+  }
+  const int npairs = DIAG ? 0 : L * (L + 1) / 2;
   for (int p = tid; p < npairs; p += 256) {
     int t = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
     while (t * (t + 1) / 2 > p) --t;
@@ -224,14 +296,14 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     // a~ = (slot-0 decay) a_0 + sum_{j >= r} c_j U~_j: lanes over channels for a_0, over
     // columns for the window's coefficients
     constexpr int NA = DK / 64;
-    const float s0 = sc[0];
+    const float s0 = DIAG ? 1.f : sc[0];
     const float cj = (lane >= r && lane < m) ? sc[A.coef_off + lane - r] : 0.f;
     for (int t = wv; t < L; t += 4) {
       float xk = 0.f, xq = 0.f;
 #pragma unroll
       for (int e = 0; e < NA; ++e) {
-        xk += S.a0[NA * lane + e] * S.K[t][NA * lane + e];
-        xq += S.a0[NA * lane + e] * S.Q[t][NA * lane + e];
+        xk += S.a0[NA * lane + e] * krow(t)[NA * lane + e];
+        xq += S.a0[NA * lane + e] * qrow(t)[NA * lane + e];
       }
       xk = s0 * xk + cj * S.PK[lane][t];
       xq = s0 * xq + cj * S.PQ[lane][t];
@@ -295,8 +367,10 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
 #pragma unroll
     for (int t = 0; t < LM; ++t) {
       const float bt = S.beta[t];
-      float w = bt * ((vt[t] - S.omega[t] * vbd) - (DELTA ? S.Gm[t][0] * x[t] : 0.f));
-      float ct = bt * (S.omega[t] - (DELTA ? S.Gm[t][0] * S.aK[t] : 0.f));
+      // (KDA: the decay to token t is inside the decayed keys already)
+      const float gt = DIAG ? 1.f : S.Gm[t][0];
+      float w = bt * ((vt[t] - S.omega[t] * vbd) - (DELTA ? gt * x[t] : 0.f));
+      float ct = bt * (S.omega[t] - (DELTA ? gt * S.aK[t] : 0.f));
       if constexpr (DELTA) {
 #pragma unroll
         for (int s = 0; s < t; ++s) {
@@ -333,17 +407,55 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     const float vbd = S.vb[d];
 #pragma unroll
     for (int t = 0; t < LM; ++t) {
-      float o = S.Gm[t][0] * fmaf(vbd, S.aQ[t], y[t]);
+      float o = (DIAG ? 1.f : S.Gm[t][0]) * fmaf(vbd, S.aQ[t], y[t]);
 #pragma unroll
       for (int s = 0; s <= t; ++s) o = fmaf(S.Aqk[t][s], S.W[s][d], o);
       if (t < L) reinterpret_cast<IT*>(A.o)[tok(t) * DV + d] = from_f32<IDT>(o);
     }
   }
-  const float gL = S.Gm[L - 1][0];
-  if (tid <= m - r) sc[tid] *= gL;  // slot 0 and the window columns held before the chunk
-  if (tid < L) {
-    sc[1 + m + tid - r] = S.Gm[L - 1][tid + 1];
-    sc[A.coef_off + m + tid - r] = S.c[tid];
+  if constexpr (DIAG) {
+    // channel d: the new columns stored against the channel scale after the chunk,
+    // Gamma P_{L-1}; where that falls below the floor, the channel is folded first (its scale
+    // into the stored columns and a_0, the scale back to 1) and the new columns are stored true
+    for (int dd = tid; dd < DK; dd += 256) {
+      const float g0 = sc[dd];
+      float P[LM];
+      float p = 1.f;
+#pragma unroll
+      for (int t = 0; t < LM; ++t) {
+        p *= S.Al[t][dd];
+        P[t] = p;
+      }
+      const float gfin = g0 * P[LM - 1];   // padding gates are 1
+      const bool fold = gfin < kChunkFoldFloor<FDT>;
+      float rest = 1.f;                    // Gamma(L-1, t): the gates after token t
+#pragma unroll
+      for (int t = LM - 1; t >= 0; --t) {
+        if (t < L) {
+          // the key from the input again: its LDS copy now holds the residuals
+          const float kv = to_f32<IDT>(reinterpret_cast<const IT*>(A.k)[tok(t) * DK + dd]);
+          const float x = fold ? kv * rest : kv / (g0 * P[t]);
+          Ub[static_cast<int64_t>(m + t) * DK + dd] = from_f32<FDT>(x);
+          rest *= S.Al[t][dd];
+        }
+      }
+      if (fold) {
+        for (int j = 0; j < m; ++j) {
+          FT* e = Ub + static_cast<int64_t>(j) * DK + dd;
+          *e = from_f32<FDT>(to_f32<FDT>(*e) * gfin);
+        }
+        A.a[unit * DK + dd] = S.a0[dd] * gfin;
+      }
+      sc[dd] = fold ? 1.f : gfin;
+    }
+    if (tid < L) sc[A.coef_off + m + tid - r] = S.c[tid];
+  } else {
+    const float gL = S.Gm[L - 1][0];
+    if (tid <= m - r) sc[tid] *= gL;  // slot 0 and the window columns held before the chunk
+    if (tid < L) {
+      sc[1 + m + tid - r] = S.Gm[L - 1][tid + 1];
+      sc[A.coef_off + m + tid - r] = S.c[tid];
+    }
   }
   if (tid == 0) sc[A.m_off] = __uint_as_float(static_cast<uint32_t>(m + L));
 }
@@ -351,33 +463,33 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
 namespace {
 using ChunkFn = void (*)(const StepArgs);
 
-template <int DK, int DV, bool DELTA, int LM>
+template <int DK, int DV, bool DELTA, bool DIAG, int LM>
 ChunkFn pick_chunk_dt(int fdt, int idt) {
   if (idt == SEED_BF16) {
     switch (fdt) {
-      case SEED_F32: return k_decode_chunk<DK, DV, DELTA, 0, 1, LM>;
-      case SEED_BF16: return k_decode_chunk<DK, DV, DELTA, 1, 1, LM>;
-      case SEED_F16: return k_decode_chunk<DK, DV, DELTA, 2, 1, LM>;
+      case SEED_F32: return k_decode_chunk<DK, DV, DELTA, DIAG, 0, 1, LM>;
+      case SEED_BF16: return k_decode_chunk<DK, DV, DELTA, DIAG, 1, 1, LM>;
+      case SEED_F16: return k_decode_chunk<DK, DV, DELTA, DIAG, 2, 1, LM>;
       default: return nullptr;
     }
   }
   if (idt == SEED_F32) {
     switch (fdt) {
-      case SEED_F32: return k_decode_chunk<DK, DV, DELTA, 0, 0, LM>;
-      case SEED_BF16: return k_decode_chunk<DK, DV, DELTA, 1, 0, LM>;
+      case SEED_F32: return k_decode_chunk<DK, DV, DELTA, DIAG, 0, 0, LM>;
+      case SEED_BF16: return k_decode_chunk<DK, DV, DELTA, DIAG, 1, 0, LM>;
       default: return nullptr;
     }
   }
   return nullptr;
 }
 
-template <bool DELTA, int LM>
+template <bool DELTA, bool DIAG, int LM>
 ChunkFn pick_chunk_dims(const seed_shape& sh) {
   const int f = sh.factor_dtype, i = sh.io_dtype;
-  if (sh.d_k == 128 && sh.d_v == 128) return pick_chunk_dt<128, 128, DELTA, LM>(f, i);
-  if (sh.d_k == 128 && sh.d_v == 64) return pick_chunk_dt<128, 64, DELTA, LM>(f, i);
-  if (sh.d_k == 64 && sh.d_v == 128) return pick_chunk_dt<64, 128, DELTA, LM>(f, i);
-  if (sh.d_k == 64 && sh.d_v == 64) return pick_chunk_dt<64, 64, DELTA, LM>(f, i);
+  if (sh.d_k == 128 && sh.d_v == 128) return pick_chunk_dt<128, 128, DELTA, DIAG, LM>(f, i);
+  if (sh.d_k == 128 && sh.d_v == 64) return pick_chunk_dt<128, 64, DELTA, DIAG, LM>(f, i);
+  if (sh.d_k == 64 && sh.d_v == 128) return pick_chunk_dt<64, 128, DELTA, DIAG, LM>(f, i);
+  if (sh.d_k == 64 && sh.d_v == 64) return pick_chunk_dt<64, 64, DELTA, DIAG, LM>(f, i);
   return nullptr;
 }
 
@@ -385,19 +497,26 @@ template <int LM>
 ChunkFn pick_chunk_kind(const seed_shape& sh) {
   if (sh.rank + sh.period > kColsMax) return nullptr;
   if (sh.rounding != SEED_ROUND_NEAREST) return nullptr;
-  if (sh.kind == SEED_GDN) return pick_chunk_dims<true, LM>(sh);
-  if (sh.kind == SEED_MAMBA2) return pick_chunk_dims<false, LM>(sh);
-  return nullptr;  // KDA's per-channel gate: not on this path
+  if (sh.kind == SEED_GDN) return pick_chunk_dims<true, false, LM>(sh);
+  if (sh.kind == SEED_MAMBA2) return pick_chunk_dims<false, false, LM>(sh);
+  return nullptr;
 }
 
 ChunkFn pick_chunk(const seed_shape& sh, int len) {
+  // KDA stages its gates and decayed keys as well: 16 tokens per call fit the LDS
+  if (sh.kind == SEED_KDA) {
+    if (len > kChunkMaxDiag || sh.rank + sh.period > kColsMax || sh.rounding != SEED_ROUND_NEAREST) return nullptr;
+    return pick_chunk_dims<true, true, 16>(sh);
+  }
   return len <= 16 ? pick_chunk_kind<16>(sh) : pick_chunk_kind<32>(sh);
 }
 }  // namespace
 
 int32_t chunk_max_tokens() { return kChunkMax; }
 
-bool chunk_supported(const seed_shape& sh) { return pick_chunk(sh, kChunkMax) != nullptr; }
+bool chunk_supported(const seed_shape& sh) { return pick_chunk(sh, 1) != nullptr; }
+
+bool chunk_supported_len(const seed_shape& sh, int32_t len) { return pick_chunk(sh, len) != nullptr; }
 
 hipError_t launch_decode_chunk(const seed_shape& sh, const StepArgs& a, hipStream_t s) {
   ChunkFn fn = pick_chunk(sh, a.len);

@@ -152,8 +152,8 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert chunk(sh, 15, 4) == rrs.SEED_ERR_ARG          # m < r
     assert chunk(sh, 30, 3) == rrs.SEED_ERR_ARG          # 30 + 3 > r + T
     assert chunk(sh, 16, 4, q=_Fake(0)) == rrs.SEED_ERR_ARG
-    kda = rrs.make_shape(rrs.SEED_KDA, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16)
-    assert chunk(kda, 16, 4) == rrs.SEED_ERR_UNSUPPORTED
+    kda = rrs.make_shape(rrs.SEED_KDA, 4, 2, 128, 128, 16, 32, rrs.SEED_BF16)
+    assert chunk(kda, 16, 17) == rrs.SEED_ERR_UNSUPPORTED   # KDA: up to 16 tokens per call
     srd = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16,
                          rounding=rrs.SEED_ROUND_STOCHASTIC)
     assert chunk(srd, 16, 4) == rrs.SEED_ERR_UNSUPPORTED

@@ -115,6 +115,10 @@ CASES = {
     "gdn64:bf16": (synth.GDN, 64, 64, synth.BF16, synth.BF16),
     "mamba2:bf16": (synth.MAMBA2, 128, 64, synth.BF16, synth.BF16),
     "mamba2:fp32": (synth.MAMBA2, 128, 64, synth.F32, synth.F32),
+    "kda:bf16": (synth.KDA, 128, 128, synth.BF16, synth.BF16),
+    "kda:fp16": (synth.KDA, 128, 128, synth.F16, synth.BF16),
+    "kda:fp32": (synth.KDA, 128, 128, synth.F32, synth.F32),
+    "kda64:bf16": (synth.KDA, 64, 128, synth.BF16, synth.BF16),
 }
 
 
@@ -194,3 +198,26 @@ def test_full_size_chunk_sampled():
     eS, eo = check_chunk(rrs, torch, w, sh, st, w.rank, L, d, vbar, hc, units)
     print(f"[chunk] full size L={L}: S {eS:.2e} o {eo:.2e}", flush=True)
     assert eS <= tolerance(w) and eo <= out_tolerance(w)
+
+
+@pytest.mark.parametrize("fdt", [synth.BF16, synth.F16])
+def test_kda_chunk_folds_channels(fdt):
+    """KDA: channels whose scale falls below the floor within a chunk are folded into the
+    stored columns (here: half the channels forget at token 3, and a quarter decay by 0.05 per
+    token, 0.05^16 being below both floors), and the state stays the oracle's."""
+    w = synth.Workload("chunkkda", synth.KDA, 2, 3, 128, 128, 16, 16, 32, 24, fdt, synth.BF16)
+    rrs, torch, sh, hc, gen, vbar, st = _prefilled(w, seed=33)
+    L = 16
+    xs_gen = synth.rng(34)
+    d = _chunk_inputs(w, hc, xs_gen, L)
+    g = d["g"].clone()
+    g[:, 3, :, :64] = 0.0
+    g[:, :, :, 96:] = 0.05
+    d["g"] = g.contiguous()
+    eS, eo = check_chunk(rrs, torch, w, sh, st, w.rank, L, d, vbar, hc, list(range(w.units)))
+    scales = st.scale[:, :w.d_k].cpu()
+    print(f"[chunk] kda fold {fdt}: S {eS:.2e} o {eo:.2e}; channels at scale 1: "
+          f"{int((scales == 1.0).sum())} of {scales.numel()}", flush=True)
+    assert eS <= tolerance(w) and eo <= out_tolerance(w)
+    assert torch.all(scales[:, :64] == 1.0) and torch.all(scales[:, 96:] == 1.0)
+    assert torch.all(torch.isfinite(st.U.float()))
