@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--workload", default="gdn-stack36")
     ap.add_argument("--factor-dtype", choices=["fp32", "bf16", "fp16"], default=None,
                     help="factor storage other than the workload's own (fp16: with bf16 inputs)")
+    ap.add_argument("--no-diagnostics", action="store_true",
+                    help="skip everything after the timed steps except the dense baseline (the "
+                         "energy, spectrum, chunked-update and overlapped-schedule measurements), "
+                         "so that a profile holds only the step's kernels and the baseline")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the overlapped-schedule measurement (decode and compression on "
                          "disjoint XCDs, compressions shifted per layer)")
@@ -347,27 +351,14 @@ def main():
         f"{t_cmp * 1e3:.1f} ms over {n_cmp_launch} launches")
 
     # ---- the state-energy diagnostic (not part of a step): one launch per layer ----------------
-    en_out = [torch.empty((U1, 3), dtype=torch.float32, device=dev) for _ in range(L)]
-    for l in range(L):
-        rrs.seed_state_energy(sh_l[l], states[l], vbars[l], out=en_out[l])
-    e_a, e_b = ev(), ev()
-    torch.cuda.synchronize()
-    e_a.record()
-    for l in range(L):
-        rrs.seed_state_energy(sh_l[l], states[l], vbars[l], out=en_out[l])
-    e_b.record()
-    torch.cuda.synchronize()
-    t_en = e_a.elapsed_time(e_b) / 1e3
+    diag = not args.no_diagnostics
     m_now = int(rrs.column_counts(sh_l[0], states[0])[0])
-    f_b = 2 if w.factor_dtype else 4
-    en_bytes = N * (f_b * (w.d_k + w.d_v) * m_now + 4 * w.d_k + 4 * rrs.seed_scale_len(sh) + 12)
-    sink_share = float(sum(e[:, 1].sum() for e in en_out) / sum(e[:, 0].sum() for e in en_out))
-    log(f"[bench] energy diagnostic: {t_en * 1e3:.2f} ms over the stack at m = {m_now} "
-        f"({en_bytes / t_en / 1e9:.0f} GB/s); sink share of the energy {sink_share:.3f}")
-
+    energy = None
+    if diag:
+        energy = energy_diagnostic(rrs, torch, w, sh, sh_l, states, vbars, U1, L, N, m_now, dev, ev, log)
     # ---- the content spectrum (not part of a step): one launch per layer ------------------------
     spectrum = None
-    if w.factor_dtype != rrs.SEED_F32 and w.rank <= 32:
+    if diag and w.factor_dtype != rrs.SEED_F32 and w.rank <= 32:
         sp_out = [torch.empty((U1, rrs.SEED_SPECTRUM_LEN), dtype=torch.float32, device=dev) for _ in range(L)]
         for l in range(L):
             rrs.seed_state_spectrum(sh_l[l], states[l], out=sp_out[l])
@@ -389,13 +380,13 @@ def main():
     # ---- the chunked update (not part of a step): len tokens per unit in one launch, on a copy
     # of layer 0's state, against len decode launches -----------------------------------------
     chunk = None
-    if w.kind != rrs.SEED_KDA and args.rounding == "nearest":
+    if diag and args.rounding == "nearest":
         chunk = {}
         st_c = rrs.State(*[t.clone() for t in states[0].tensors()])
         m0 = int(rrs.column_counts(sh_l[0], st_c)[0])
         io_t = {rrs.SEED_BF16: torch.bfloat16, rrs.SEED_F32: torch.float32}[w.io_dtype]
         Bq, Hq = w.batch, w.heads
-        for Lc in (16, 32):
+        for Lc in ((16,) if w.kind == rrs.SEED_KDA else (16, 32)):   # KDA: 16 tokens per call
             if m0 + Lc > w.rank + T:
                 continue
             gq = torch.Generator(device=dev).manual_seed(Lc)
@@ -407,7 +398,8 @@ def main():
             v_c = torch.randn(Bq, Lc, Hq, w.d_v, device=dev, generator=gq).to(io_t)
             q_c, k_c = q_c.to(io_t), k_c.to(io_t)
             b_c = torch.rand(Bq, Lc, Hq, device=dev, generator=gq)
-            g_c = 0.9 + 0.1 * torch.rand(Bq, Lc, Hq, device=dev, generator=gq)
+            g_shape = (Bq, Lc, Hq, w.d_k) if w.kind == rrs.SEED_KDA else (Bq, Lc, Hq)
+            g_c = 0.9 + 0.1 * torch.rand(*g_shape, device=dev, generator=gq)
             o_c = torch.empty(Bq, Lc, Hq, w.d_v, dtype=io_t, device=dev)
             rrs.seed_decode_chunk(sh_l[0], st_c, m0, Lc, q_c, k_c, v_c, b_c, g_c, vbars[0], o_c)
             c_ev = [(ev(), ev()) for _ in range(5)]
@@ -427,7 +419,7 @@ def main():
         del st_c
 
     # ---- the overlapped schedule (reported beside the lockstep step) ---------------------------
-    overlapped = None if args.no_overlap else run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T,
+    overlapped = None if (args.no_overlap or not diag) else run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T,
                                                             P, ev, log)
 
     # ---- dense-state baseline ----------------------------------------------------------------
@@ -516,13 +508,34 @@ def main():
                              "decode_only": dense_step_ms / dec_step_ms,
                              "state_byte_ratio_target": state_ratio},
         "setup_s": {"prefill_end_compression": t_from_dense},
-        "energy_diagnostic": {"ms_per_stack": t_en * 1e3, "columns": m_now, "gbs": en_bytes / t_en / 1e9,
-                              "sink_share": sink_share},
+        "energy_diagnostic": energy,
         "overlapped_schedule": overlapped,
         "spectrum_diagnostic": spectrum,
         "chunked_update": chunk,
     }
     print(json.dumps(res), flush=True)
+
+
+def energy_diagnostic(rrs, torch, w, sh, sh_l, states, vbars, U1, L, N, m_now, dev, ev, log):
+    """seed_state_energy over the stack (one launch per layer), timed; the pooled sink share."""
+    en_out = [torch.empty((U1, 3), dtype=torch.float32, device=dev) for _ in range(L)]
+    for l in range(L):
+        rrs.seed_state_energy(sh_l[l], states[l], vbars[l], out=en_out[l])
+    e_a, e_b = ev(), ev()
+    torch.cuda.synchronize()
+    e_a.record()
+    for l in range(L):
+        rrs.seed_state_energy(sh_l[l], states[l], vbars[l], out=en_out[l])
+    e_b.record()
+    torch.cuda.synchronize()
+    t_en = e_a.elapsed_time(e_b) / 1e3
+    f_b = 2 if w.factor_dtype else 4
+    en_bytes = N * (f_b * (w.d_k + w.d_v) * m_now + 4 * w.d_k + 4 * rrs.seed_scale_len(sh) + 12)
+    sink_share = float(sum(e[:, 1].sum() for e in en_out) / sum(e[:, 0].sum() for e in en_out))
+    log(f"[bench] energy diagnostic: {t_en * 1e3:.2f} ms over the stack at m = {m_now} "
+        f"({en_bytes / t_en / 1e9:.0f} GB/s); sink share of the energy {sink_share:.3f}")
+    return {"ms_per_stack": t_en * 1e3, "columns": m_now, "gbs": en_bytes / t_en / 1e9,
+            "sink_share": sink_share}
 
 
 def _partition_streams(torch, split):
