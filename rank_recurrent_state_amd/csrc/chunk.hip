@@ -23,8 +23,9 @@
 // inputs, so every loop runs to LM without a test, and only the stores look at L.
 //   staging      keys and queries of the chunk in LDS as fp32 (row stride d_k + 4: the
 //                pair products below read rows t and s in one access without bank conflicts);
-//   U pass       thread (j, w) holds column j of U and forms U~_j . kappa_t and U~_j . q_t for
-//                the tokens t = w, w + 4, ... (the key and query rows are LDS broadcasts);
+//   U pass       U~^T kappa and U~^T q by MFMA 32x32x2 (fp32): one 32-column, 32-token tile
+//                per wave; each lane's row of U is loaded at the start of the kernel (its
+//                latency overlaps the staging), the key and query rows come from LDS;
 //   pair terms   kappa_t . kappa_s and q_t . kappa_s over the lower triangle, and the decay
 //                products Gamma(t, s) by running products;
 //   V pass       thread d of the first half owns value channel d: V (U~^T kappa) in registers,
@@ -94,6 +95,20 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
   // row of token t in the [batch][L][heads] layout of the chunk's inputs and outputs
   auto tok = [&](int t) { return (bq * L + t) * H + hd; };
+
+  // ---- the U pass's column loads go out first: their latency overlaps the staging -------------
+  // Wave wv takes column block jt = wv % 2; lane (c, h) loads row 32 jt + c of U: the whole row
+  // for 16-bit factors, its first half for fp32 factors (the second half follows later).
+  const int ujt = wv & 1;
+  const int uj = 32 * ujt + (lane & 31);
+  const bool ujok = uj < m;
+  const uint4* __restrict__ urow = reinterpret_cast<const uint4*>(Ub + static_cast<int64_t>(ujok ? uj : 0) * DK);
+  constexpr int UW = DK / 8;   // 16-byte words held: DK 16-bit elements, or DK / 2 fp32 ones
+  uint4 uraw[UW];
+  if (32 * ujt < m) {  // uniform
+#pragma unroll
+    for (int i = 0; i < UW; ++i) uraw[i] = urow[i];
+  }
 
   // ---- staging (padding tokens: zero inputs, zero pair terms) ---------------------------------
   for (int i = tid; i < LM * (DK / 4); i += 256) {
@@ -174,46 +189,56 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     else return &S.Q[t][0];
   };
   {
-    const int j = lane;  // column of U; tokens wv, wv + 4, ...
-    constexpr int TPW = LM / 4;
-    float pk[TPW], pq[TPW];
+    // U pass by MFMA 32x32x2 (fp32): wave wv forms the 32 x 32 tile of column block jt = wv % 2
+    // and keys (wv < 2) or queries of (U^T K)[j][t] = sum_d U[j][d] K[t][d]. Lane (c, h) feeds
+    // A = U[32 jt + c][d] and B = K[c][d] for d = 2 s + h: its column's elements from the
+    // words loaded above, its key row's from LDS; tokens past L and columns past m are zero.
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    const bool isq = wv >= 2;
+    if (32 * ujt < m) {  // uniform
+      const int c = lane & 31, h = lane >> 5;
+      const float* __restrict__ brow = c < LM ? (isq ? qrow(c) : krow(c)) : nullptr;
+      uint4 uraw2[FDT == 0 ? UW : 1];   // fp32 factors: the row's second half
+      if constexpr (FDT == 0) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) { pk[i] = 0.f; pq[i] = 0.f; }
-    if (j < m) {
-      const FT* __restrict__ up = Ub + static_cast<int64_t>(j) * DK;
-      // the column in batches of 32 elements, all of a batch's loads in flight at once
-#pragma unroll 1
-      for (int d0 = 0; d0 < DK; d0 += 32) {
-        float u[4][8];
+        for (int i = 0; i < UW; ++i) uraw2[i] = urow[UW + i];
+      }
+      auto word = [](const uint4& q, int k) { return k == 0 ? q.x : (k == 1 ? q.y : (k == 2 ? q.z : q.w)); };
+      f32x16 acc;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) load_f32<FDT, 8>(up + d0 + 8 * c, u[c]);
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int d = d0 + 8 * c;
+      for (int d8 = 0; d8 < DK; d8 += 8) {
 #pragma unroll
-          for (int i = 0; i < TPW; ++i) {
-            const int t = wv + 4 * i;
-            const float4 k0 = *reinterpret_cast<const float4*>(krow(t) + d);
-            const float4 k1 = *reinterpret_cast<const float4*>(krow(t) + d + 4);
-            const float4 q0 = *reinterpret_cast<const float4*>(qrow(t) + d);
-            const float4 q1 = *reinterpret_cast<const float4*>(qrow(t) + d + 4);
-            const float* uc = u[c];
-            pk[i] += uc[0] * k0.x + uc[1] * k0.y + uc[2] * k0.z + uc[3] * k0.w +
-                     uc[4] * k1.x + uc[5] * k1.y + uc[6] * k1.z + uc[7] * k1.w;
-            pq[i] += uc[0] * q0.x + uc[1] * q0.y + uc[2] * q0.z + uc[3] * q0.w +
-                     uc[4] * q1.x + uc[5] * q1.y + uc[6] * q1.z + uc[7] * q1.w;
+        for (int e = 0; e < 4; ++e) {
+          float av;
+          if constexpr (FDT == 0) {
+            const int i = d8 + 2 * e;                          // even: i and i + 1 share a word
+            const uint4& q = i < DK / 2 ? uraw[i / 4] : uraw2[(i - DK / 2) / 4];
+            av = __uint_as_float(h ? word(q, i % 4 + 1) : word(q, i % 4));
+          } else {
+            const uint32_t w = word(uraw[d8 / 8], e);
+            av = h ? hi16<FDT>(w) : lo16<FDT>(w);
           }
-          __builtin_amdgcn_sched_barrier(0);  // the key and query reads of one slice at a time
+          av = ujok ? av : 0.f;
+          const float bv = brow != nullptr ? brow[d8 + 2 * e + h] : 0.f;
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
         }
       }
-      // true columns: slot 0 scales the r columns kept by the last compression, slot 1 + i
-      // window column r + i
-      const float s = DIAG ? 1.f : sc[j < r ? 0 : 1 + j - r];
+      // acc[v] is the tile's entry (row 8 (v / 4) + 4 h + v % 4, column c): column j of U,
+      // token c
+      if (c < LM) {
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int t = wv + 4 * i;
-        S.PK[j][t] = s * pk[i];
-        S.PQ[j][t] = s * pq[i];
+        for (int v = 0; v < 16; ++v) {
+          const int jj = 32 * ujt + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (jj < m) {
+            // true columns: slot 0 scales the r columns kept by the last compression, slot 1 + i
+            // window column r + i (KDA: the channel scales are in the keys)
+            const float sj = DIAG ? 1.f : sc[jj < r ? 0 : 1 + jj - r];
+            if (isq) S.PQ[jj][c] = sj * acc[v];
+            else S.PK[jj][c] = sj * acc[v];
+          }
+        }
       }
     }
   }
@@ -318,18 +343,22 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   __syncthreads();
 
   // ---- V pass: W and c by forward substitution (first half), V (U~^T q) (second half) ---------
-  // Each half reads its channel of the m stored V columns, sixteen loads in flight at a time.
+  // Each half reads its channel of the m stored V columns, sixteen loads ahead of their use.
   const int d = tid < DV ? tid : tid - DV;
   auto v_times = [&](const float (*P)[LM], float (&acc)[LM]) {
 #pragma unroll
     for (int t = 0; t < LM; ++t) acc[t] = 0.f;
-#pragma unroll 1
-    for (int j0 = 0; j0 < m; j0 += 16) {
-      // sixteen columns' loads in flight at once (a column past m reads column m - 1; its row of
-      // P is zero)
-      float vj[16];
+    // sixteen columns at a time, the next sixteen columns' loads in flight meanwhile (a column
+    // past m reads column m - 1; its row of P is zero)
+    auto vload = [&](int j0, float (&vj)[16]) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) vj[e] = to_f32<FDT>(Vb[static_cast<int64_t>(j0 + e < m ? j0 + e : m - 1) * DV + d]);
+    };
+    float vj[16], vn[16];
+    vload(0, vj);
+#pragma unroll 1
+    for (int j0 = 0; j0 < m; j0 += 16) {
+      vload(j0 + 16, vn);   // unconditional (clamped), so that no branch waits on it
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
 #pragma unroll
@@ -343,6 +372,8 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
         // one row of P at a time (hoisted, the rows' reads would take 512 registers)
         __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vj[e] = vn[e];
     }
   };
   float y[LM];
