@@ -574,6 +574,11 @@ def run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T, P, ev, log
     T steps at r + T columns. Returns ms per step and head-steps/s, or None."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         return None
+    if L < 8:
+        # one layer (or a few) leaves nothing to overlap with: the layer's own next decode
+        # launch waits for its compression, on half the chip
+        log("[bench] overlapped schedule: needs a stack of layers, skipped")
+        return None
     streams = _partition_streams(torch, split)
     if streams is None:
         log("[bench] overlapped schedule: CU-masked streams not available, skipped")

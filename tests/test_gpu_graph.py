@@ -77,3 +77,62 @@ def test_graph_replay_matches_eager(kind, fdt):
         torch.cuda.synchronize()
         for te, tg in zip(eager.tensors(), graph.tensors()):
             assert torch.equal(te, tg), f"replay {rep}: compressed state differs"
+
+
+@pytest.mark.parametrize("kind", [synth.GDN, synth.KDA])
+def test_graph_replay_chunk_and_spectrum(kind):
+    """The chunked update and the spectrum diagnostic captured in a graph: each replay, from a
+    fresh copy of the same state, equals the eager call bit for bit (eager work in between)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_recurrent_state_amd as rrs
+
+    w = synth.Workload("graphchunk", kind, 2, 3, 128, 128, 16, 16, 32, 24, synth.BF16, synth.BF16)
+    sh = shape_of(w)
+    n, r, L = w.units, w.rank, 12
+    hc = synth.head_consts(w, 41)
+    gen = synth.rng(41)
+    vbar = torch.tensor(hc.vbar, dtype=torch.float32, device="cuda")
+    S = torch.zeros((n, w.d_k, w.d_v), dtype=torch.float32, device="cuda")
+    o1 = torch.empty((n, w.d_v), dtype=torch.bfloat16, device="cuda")
+    for _ in range(w.prefill):
+        d = to_device_inputs(synth.step_inputs(w, hc, gen, n), w.io_dtype)
+        rrs.seed_dense_decode_step(sh, S, d["q"], d["k"], d["v"], d["beta"], d["g"], o1)
+    base = rrs.State.empty(sh)
+    rrs.seed_state_from_dense(sh, S, vbar, base)
+    B, H = w.batch, w.heads
+    gshape = (B, L, H, w.d_k) if kind == synth.KDA else (B, L, H)
+    q = torch.nn.functional.normalize(torch.randn(B, L, H, w.d_k, device="cuda"), dim=-1).bfloat16()
+    k = torch.nn.functional.normalize(torch.randn(B, L, H, w.d_k, device="cuda"), dim=-1).bfloat16()
+    v = torch.randn(B, L, H, w.d_v, device="cuda").bfloat16()
+    beta = torch.rand(B, L, H, device="cuda")
+    g = 0.9 + 0.1 * torch.rand(*gshape, device="cuda")
+
+    def run(st, o, spec):
+        rrs.seed_decode_chunk(sh, st, r, L, q, k, v, beta, g, vbar, o)
+        rrs.seed_state_spectrum(sh, st, out=spec)
+
+    eager = rrs.State(*[t.clone() for t in base.tensors()])
+    o_e = torch.empty((B, L, H, w.d_v), dtype=torch.bfloat16, device="cuda")
+    sp_e = torch.empty((n, rrs.SEED_SPECTRUM_LEN), dtype=torch.float32, device="cuda")
+    run(eager, o_e, sp_e)
+    work = rrs.State(*[t.clone() for t in base.tensors()])
+    o_g = torch.empty_like(o_e)
+    sp_g = torch.empty_like(sp_e)
+    run(work, o_g, sp_g)                 # first launches eagerly
+    torch.cuda.synchronize()
+    g_ = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_):
+        run(work, o_g, sp_g)
+    for rep in range(3):
+        for x, y in zip(work.tensors(), base.tensors()):
+            x.copy_(y)
+        o_g.zero_()
+        sp_g.zero_()
+        torch.cuda.synchronize()
+        g_.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), rep
+        assert torch.equal(sp_g, sp_e), rep
+        for x, y in zip(work.tensors(), eager.tensors()):
+            assert torch.equal(x, y), rep
