@@ -246,6 +246,20 @@ int seed_decode_chunk(const seed_shape *shape, const seed_state *state, int32_t 
                       const void *q, const void *k, const void *v, const float *beta,
                       const float *g, const float *vbar, void *o, void *stream);
 
+/*
+ * The chunked update for a ragged batch: every unit takes its own column count m from its
+ * state, as seed_decode_step_ragged does, and runs the chunk of seed_decode_chunk from it when
+ *   - active is NULL or active[u] != 0 (active: uint8 [units], device memory), and
+ *   - rank <= m and m + len <= rank + period (the chunk fits the unit's free slots).
+ * Any other unit is left untouched and its rows of o are not written. len <= period, else
+ * SEED_ERR_ARG. Arguments otherwise as for seed_decode_chunk. Source: the chunk of
+ * seed_decode_chunk; requests of different lengths in one batch (continuous batching).
+ */
+int seed_decode_chunk_ragged(const seed_shape *shape, const seed_state *state, const uint8_t *active,
+                             int32_t len, const void *q, const void *k, const void *v,
+                             const float *beta, const float *g, const float *vbar, void *o,
+                             void *stream);
+
 /* The largest len seed_decode_chunk takes. */
 int32_t seed_chunk_max_tokens(void);
 

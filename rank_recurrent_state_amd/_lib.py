@@ -23,7 +23,8 @@ EXPORTS = [
     "seed_state_bytes", "seed_scale_len", "seed_workspace_bytes", "seed_state_from_dense",
     "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
     "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_decode_chunk",
-    "seed_chunk_max_tokens", "seed_state_spectrum", "seed_status_string", "seed_version",
+    "seed_chunk_max_tokens", "seed_decode_chunk_ragged", "seed_state_spectrum", "seed_status_string",
+    "seed_version",
 ]
 
 SEED_SPECTRUM_LEN = 33
@@ -78,6 +79,7 @@ def _load():
         "seed_decode_chunk": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P,
                                              P, P]),
         "seed_chunk_max_tokens": (ctypes.c_int32, []),
+        "seed_decode_chunk_ragged": (ctypes.c_int, [Sp, Stp, P, ctypes.c_int32, P, P, P, P, P, P, P, P]),
         "seed_state_spectrum": (ctypes.c_int, [Sp, Stp, P, P]),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "seed_version": (ctypes.c_char_p, []),
@@ -268,12 +270,7 @@ def seed_chunk_max_tokens() -> int:
     return int(LIB.seed_chunk_max_tokens())
 
 
-def seed_decode_chunk(shape: seed_shape, state, m: int, length: int, q, k, v, beta, g, vbar, o,
-                      stream=None) -> None:
-    """`length` tokens of every unit in one call: q, k [batch, length, heads, d_k], v and o
-    [batch, length, heads, d_v], beta [batch, length, heads] and g [batch, length, heads]
-    (KDA: [batch, length, heads, d_k]), float32."""
-    _expect_state(shape, state)
+def _expect_chunk_io(shape, length, q, k, v, beta, g, o):
     n = shape.units * length
     _expect("q", q, n * shape.d_k, shape.io_dtype)
     _expect("k", k, n * shape.d_k, shape.io_dtype)
@@ -281,6 +278,33 @@ def seed_decode_chunk(shape: seed_shape, state, m: int, length: int, q, k, v, be
     _expect("beta", beta, n, SEED_F32)
     _expect("g", g, n * (shape.d_k if shape.kind == SEED_KDA else 1), SEED_F32)
     _expect("o", o, n * shape.d_v, shape.io_dtype)
+
+
+def seed_decode_chunk_ragged(shape: seed_shape, state, length: int, q, k, v, beta, g, vbar, o,
+                             active=None, stream=None) -> None:
+    """The chunk of seed_decode_chunk for every unit from its own column count (kept in the
+    state); active (uint8 [units] on the device, or None for all) masks units out, and units
+    without room for the chunk are skipped."""
+    import torch
+    _expect_state(shape, state)
+    _expect_chunk_io(shape, length, q, k, v, beta, g, o)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    if active is not None and hasattr(active, "is_cuda"):
+        _expect("active", active, shape.units)
+        if active.dtype != torch.uint8:
+            raise ValueError(f"active: expected dtype torch.uint8, got {active.dtype}")
+    _check("seed_decode_chunk_ragged", LIB.seed_decode_chunk_ragged(
+        ctypes.byref(shape), _state_c(state), _ptr(active), length, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+        _ptr(g), _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_decode_chunk(shape: seed_shape, state, m: int, length: int, q, k, v, beta, g, vbar, o,
+                      stream=None) -> None:
+    """`length` tokens of every unit in one call: q, k [batch, length, heads, d_k], v and o
+    [batch, length, heads, d_v], beta [batch, length, heads] and g [batch, length, heads]
+    (KDA: [batch, length, heads, d_k]), float32."""
+    _expect_state(shape, state)
+    _expect_chunk_io(shape, length, q, k, v, beta, g, o)
     _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
     _check("seed_decode_chunk", LIB.seed_decode_chunk(
         ctypes.byref(shape), _state_c(state), m, length, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),

@@ -134,6 +134,28 @@ int compress_call(const seed_shape* sh, const seed_state* st, int32_t m, bool ra
   return hip_status(seed::launch_compress(*sh, a, static_cast<hipStream_t>(stream)));
 }
 
+int chunk_call(const seed_shape* sh, const seed_state* st, int32_t m, const uint8_t* active, bool ragged,
+               int32_t len, const void* q, const void* k, const void* v, const float* beta, const float* g,
+               const float* vbar, void* o, void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st) || !q || !k || !v || !beta || !g || !vbar || !o) return SEED_ERR_ARG;
+  if (len < 1 || len > seed::chunk_max_tokens()) return SEED_ERR_ARG;
+  if (!ragged && (m < sh->rank || m + len > sh->rank + sh->period)) return SEED_ERR_ARG;
+  if (len > sh->period) return SEED_ERR_ARG;
+  if (!seed::chunk_supported_len(*sh, len)) return SEED_ERR_UNSUPPORTED;
+  seed::StepArgs a = step_args(sh, st, m, active, ragged);
+  a.len = len;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.vbar = vbar;
+  a.o = o;
+  return hip_status(seed::launch_decode_chunk(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,25 +206,17 @@ int seed_decode_step_ragged(const seed_shape* sh, const seed_state* st, const ui
   return decode_call(sh, st, 0, active, true, q, k, v, beta, g, vbar, o, stream);
 }
 
+
 int seed_decode_chunk(const seed_shape* sh, const seed_state* st, int32_t m, int32_t len, const void* q,
                       const void* k, const void* v, const float* beta, const float* g, const float* vbar,
                       void* o, void* stream) {
-  const int c = check_shape(sh);
-  if (c != SEED_OK) return c;
-  if (!state_ok(st) || !q || !k || !v || !beta || !g || !vbar || !o) return SEED_ERR_ARG;
-  if (len < 1 || len > seed::chunk_max_tokens()) return SEED_ERR_ARG;
-  if (m < sh->rank || m + len > sh->rank + sh->period) return SEED_ERR_ARG;
-  if (!seed::chunk_supported_len(*sh, len)) return SEED_ERR_UNSUPPORTED;
-  seed::StepArgs a = step_args(sh, st, m, nullptr, false);
-  a.len = len;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.beta = beta;
-  a.g = g;
-  a.vbar = vbar;
-  a.o = o;
-  return hip_status(seed::launch_decode_chunk(*sh, a, static_cast<hipStream_t>(stream)));
+  return chunk_call(sh, st, m, nullptr, false, len, q, k, v, beta, g, vbar, o, stream);
+}
+
+int seed_decode_chunk_ragged(const seed_shape* sh, const seed_state* st, const uint8_t* active, int32_t len,
+                             const void* q, const void* k, const void* v, const float* beta, const float* g,
+                             const float* vbar, void* o, void* stream) {
+  return chunk_call(sh, st, 0, active, true, len, q, k, v, beta, g, vbar, o, stream);
 }
 
 int32_t seed_chunk_max_tokens(void) { return seed::chunk_max_tokens(); }

@@ -89,8 +89,15 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   const int H = A.heads;
   const int64_t bq = unit / H;
   const int hd = static_cast<int>(unit - bq * H);
-  const int L = A.len, m = A.m, r = A.rank, C = A.slots;
+  const int L = A.len, r = A.rank, C = A.slots;
   float* __restrict__ sc = A.scale + unit * A.scale_len;
+  int m = A.m;
+  if (A.ragged) {
+    // every unit from its own column count; units masked out, or without room for the chunk,
+    // are left untouched (their rows of o are not written)
+    m = static_cast<int>(__float_as_uint(sc[A.m_off]));
+    if ((A.active != nullptr && A.active[unit] == 0) || m < r || m + L > C) return;
+  }
   FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(C) * DK;
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
   // row of token t in the [batch][L][heads] layout of the chunk's inputs and outputs

@@ -157,5 +157,9 @@ def test_invalid_arguments_are_rejected_on_the_host():
     srd = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16,
                          rounding=rrs.SEED_ROUND_STOCHASTIC)
     assert chunk(srd, 16, 4) == rrs.SEED_ERR_UNSUPPORTED
+    # ragged chunk: len > period cannot fit any unit
+    with pytest.raises(rrs.SeedError) as e:
+        rrs.seed_decode_chunk_ragged(sh, st, 17, f, f, f, f, f, f, f, stream=0)
+    assert e.value.status == rrs.SEED_ERR_ARG
     for code in (0, -1, -2, -3, -4, 5):
         assert isinstance(rrs.seed_status_string(code), str)

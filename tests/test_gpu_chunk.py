@@ -221,3 +221,52 @@ def test_kda_chunk_folds_channels(fdt):
     assert eS <= tolerance(w) and eo <= out_tolerance(w)
     assert torch.all(scales[:, :64] == 1.0) and torch.all(scales[:, 96:] == 1.0)
     assert torch.all(torch.isfinite(st.U.float()))
+
+
+def test_ragged_chunk():
+    """Units at different column counts take a chunk each from their own count; a masked unit
+    and units without room are left bit for bit as they were, their rows of o unwritten."""
+    w = synth.Workload("chunkrag", synth.GDN, 4, 2, 128, 128, 16, 16, 32, 24, synth.BF16, synth.BF16)
+    rrs, torch, sh, hc, gen, vbar, st = _prefilled(w, seed=61)
+    n, H = w.units, w.heads
+    o1 = torch.empty((n, w.d_v), dtype=torch.bfloat16, device="cuda")
+    # request b takes 3 b decode steps first: counts 16, 19, 22, 25
+    for t in range(9):
+        dx = to_device_inputs(synth.step_inputs(w, hc, gen, n), synth.BF16)
+        act = torch.tensor([1 if (u // H) * 3 > t else 0 for u in range(n)], dtype=torch.uint8, device="cuda")
+        rrs.seed_decode_step_ragged(sh, st, dx["q"], dx["k"], dx["v"], dx["beta"], dx["g"], vbar, o1, active=act)
+    m0 = rrs.column_counts(sh, st).numpy()
+    L = 8                                           # 25 + 8 > 32: request 3 has no room
+    active = torch.ones(n, dtype=torch.uint8, device="cuda")
+    active[0] = 0                                   # and unit 0 is masked out
+    d = _chunk_inputs(w, hc, gen, L)
+    units = list(range(n))
+    pre = host_state(sh, st, units, m0)
+    before = [t.clone() for t in st.tensors()]
+    o = torch.full((w.batch, L, H, w.d_v), float("nan"), dtype=torch.bfloat16, device="cuda")
+    rrs.seed_decode_chunk_ragged(sh, st, L, d["q"], d["k"], d["v"], d["beta"], d["g"], vbar, o, active=active)
+    torch.cuda.synchronize()
+    m1 = rrs.column_counts(sh, st).numpy()
+    toks = _host_tokens(d, w, L, units)
+    og = o.double().cpu().numpy()
+    for u in units:
+        b, hh = divmod(u, H)
+        runs = u != 0 and m0[u] + L <= w.rank + w.period
+        if not runs:
+            assert m1[u] == m0[u]
+            for x, y in zip(before, st.tensors()):
+                assert torch.equal(x[u], y[u]), u
+            assert np.all(np.isnan(og[b, :, hh])), u
+            continue
+        assert m1[u] == m0[u] + L
+        post = host_state(sh, st, [u], m0[u] + L)[0]
+        vb = hc.vbar[hh]
+        a1, U1, V1, outs = orc.factored_chunk(w.kind, *pre[u], vb, toks[u])
+        S1 = orc.reconstruct(a1, vb, U1, V1)
+        eS = relF(orc.reconstruct(post[0], vb, post[1], post[2]), S1)
+        assert eS <= tolerance(w), (u, eS)
+        a_t, U_t, V_t = pre[u]
+        for t in range(L):
+            x = toks[u][t]
+            a_t, U_t, V_t, o_t = orc.factored_step(w.kind, a_t, U_t, V_t, vb, x["q"], x["k"], x["v"], x["beta"], x["g"])
+            assert rel_out(og[b, t, hh], o_t, orc.reconstruct(a_t, vb, U_t, V_t), x["q"]) <= out_tolerance(w)
