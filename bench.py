@@ -63,6 +63,9 @@ def parse():
                     help="skip everything after the timed steps except the dense baseline (the "
                          "energy, spectrum, chunked-update and overlapped-schedule measurements), "
                          "so that a profile holds only the step's kernels and the baseline")
+    ap.add_argument("--overlap-split", type=int, default=4,
+                    help="XCDs (of 8) that run the decode in the overlapped schedule; the "
+                         "compressions run on the others")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the overlapped-schedule measurement (decode and compression on "
                          "disjoint XCDs, compressions shifted per layer)")
@@ -420,7 +423,7 @@ def main():
 
     # ---- the overlapped schedule (reported beside the lockstep step) ---------------------------
     overlapped = None if (args.no_overlap or not diag) else run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T,
-                                                            P, ev, log)
+                                                            P, ev, log, split=args.overlap_split)
 
     # ---- dense-state baseline ----------------------------------------------------------------
     KD = args.dense_steps
