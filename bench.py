@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--overlap-split", type=int, default=4,
                     help="XCDs (of 8) that run the decode in the overlapped schedule; the "
                          "compressions run on the others")
+    ap.add_argument("--compress-scan", action="store_true",
+                    help="with --staggered: compress with seed_compress_ragged (a wave per unit of "
+                         "the stack) instead of listing the units that fill (seed_compress_units)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="skip the overlapped-schedule measurement (decode and compression on "
                          "disjoint XCDs, compressions shifted per layer)")
@@ -642,8 +645,8 @@ def run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vb
                   U1, L, T, P, nwin, Wu, K):
     """Ragged serving: request b of every layer holds r + (b mod T) columns when the timed steps
     start, so that every step fills, and compresses, the units of one T-th of the requests. A
-    step is one ragged decode launch per layer and one compression launch over the stack that
-    compresses exactly the full units. Whole-job throughput only: the per-step compressions sit
+    step is one ragged decode launch per layer and one compression launch for exactly the units
+    that filled (listed; or, with --compress-scan, a launch over the stack that the others leave). Whole-job throughput only: the per-step compressions sit
     in the same graph as the decode launches."""
     dev = torch.device("cuda", 0)
     phase = (torch.arange(U1, device=dev) // w.heads) % T
@@ -659,6 +662,14 @@ def run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vb
     counts = rrs.column_counts(sh_all, state_all)
     assert int(counts.min()) == w.rank and int(counts.max()) == w.rank + T - 1, "stagger"
 
+    # the units that fill on step j of a window: request b holds r + (b + j) mod T columns
+    # before it, so phase T - 1 - j fills (every layer's copy of those requests). The serving
+    # loop knows its requests' lengths, so it lists them; --compress-scan starts a wave for
+    # every unit of the stack instead and lets the others leave (seed_compress_ragged).
+    ustack = torch.arange(N, device=dev, dtype=torch.int64)
+    uphase = ((ustack % U1) // w.heads) % T
+    full_lists = [ustack[uphase == (T - 1 - j) % T].to(torch.int32).contiguous() for j in range(T)]
+
     def enqueue_steps(wi):
         for j in range(T):
             xl = pool[wi * T + j]
@@ -666,7 +677,10 @@ def run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vb
                 x = xl[l]
                 rrs.seed_decode_step_ragged(sh_l[l], states[l], x["q"], x["k"], x["v"], x["beta"],
                                             x["g"], vbars[l], o[l])
-            rrs.seed_compress_ragged(sh_all, state_all, w.rank + T)
+            if args.compress_scan:
+                rrs.seed_compress_ragged(sh_all, state_all, w.rank + T)
+            else:
+                rrs.seed_compress_units(sh_all, state_all, full_lists[j])
 
     for i in range(max(1, Wu // T)):
         enqueue_steps(i % nwin)

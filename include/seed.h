@@ -216,6 +216,19 @@ int seed_decode_step_ragged(const seed_shape *shape, const seed_state *state,
 int seed_state_spectrum(const seed_shape *shape, const seed_state *state, float *out, void *stream);
 
 /*
+ * Compression of listed units: units[0 .. count-1] (int32, device memory) name the units to
+ * compress, each at its own column count m (taken from the state), as seed_compress does for
+ * one unit; a listed unit with m <= rank, or an index outside [0, units), is skipped. One
+ * wavefront (or workgroup) is launched per listed unit, so a serving loop that knows which
+ * requests filled their slots this step compresses only those (seed_compress_ragged instead
+ * starts one per unit of the batch and lets the others leave). A unit listed twice races with
+ * itself: list each at most once. count = 0 does nothing. ws as for seed_compress.
+ * Source: as seed_compress; compress-when-full serving of requests of different lengths.
+ */
+int seed_compress_units(const seed_shape *shape, const seed_state *state, const int32_t *units,
+                        int32_t count, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Chunked update: len consecutive tokens of every unit in one call.
  * It appends the len columns and writes the len read-outs that len calls of seed_decode_step
  * would give for the same inputs (equal in exact arithmetic; fp32 arithmetic in another order).

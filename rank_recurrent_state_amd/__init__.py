@@ -19,7 +19,7 @@ _NAMES = {
     "column_counts", "seed_compress", "seed_compress_ragged", "seed_decode_step",
     "seed_decode_step_ragged", "seed_dense_decode_step", "seed_from_dense_iterations",
     "seed_state_energy", "seed_decode_chunk", "seed_chunk_max_tokens", "seed_state_spectrum",
-    "seed_decode_chunk_ragged",
+    "seed_decode_chunk_ragged", "seed_compress_units",
     "SEED_SPECTRUM_LEN",
     "seed_scale_len", "seed_shape", "seed_state", "seed_state_bytes", "seed_state_from_dense",
     "seed_status_string", "seed_version", "seed_workspace_bytes",

@@ -23,8 +23,8 @@ EXPORTS = [
     "seed_state_bytes", "seed_scale_len", "seed_workspace_bytes", "seed_state_from_dense",
     "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
     "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_decode_chunk",
-    "seed_chunk_max_tokens", "seed_decode_chunk_ragged", "seed_state_spectrum", "seed_status_string",
-    "seed_version",
+    "seed_chunk_max_tokens", "seed_decode_chunk_ragged", "seed_state_spectrum", "seed_compress_units",
+    "seed_status_string", "seed_version",
 ]
 
 SEED_SPECTRUM_LEN = 33
@@ -79,6 +79,7 @@ def _load():
         "seed_decode_chunk": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P,
                                              P, P]),
         "seed_chunk_max_tokens": (ctypes.c_int32, []),
+        "seed_compress_units": (ctypes.c_int, [Sp, Stp, P, ctypes.c_int32, P, ctypes.c_size_t, P]),
         "seed_decode_chunk_ragged": (ctypes.c_int, [Sp, Stp, P, ctypes.c_int32, P, P, P, P, P, P, P, P]),
         "seed_state_spectrum": (ctypes.c_int, [Sp, Stp, P, P]),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -309,6 +310,23 @@ def seed_decode_chunk(shape: seed_shape, state, m: int, length: int, q, k, v, be
     _check("seed_decode_chunk", LIB.seed_decode_chunk(
         ctypes.byref(shape), _state_c(state), m, length, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
         _ptr(g), _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_compress_units(shape: seed_shape, state, units, ws=None, stream=None) -> None:
+    """Compress the listed units (int32 device tensor of unit indices, each listed once), each
+    at its own column count."""
+    import torch
+    _expect_state(shape, state)
+    count = 0
+    if units is not None and hasattr(units, "is_cuda"):
+        if not units.is_cuda or not units.is_contiguous() or units.dtype != torch.int32:
+            raise ValueError("units: expected a contiguous int32 device tensor")
+        count = units.numel()
+    elif units is not None:
+        raise ValueError("units: expected a torch tensor")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("seed_compress_units", LIB.seed_compress_units(
+        ctypes.byref(shape), _state_c(state), _ptr(units), count, _ptr(ws), ws_bytes, _stream_ptr(stream)))
 
 
 def seed_compress_ragged(shape: seed_shape, state, min_m: int, ws=None, stream=None) -> None:

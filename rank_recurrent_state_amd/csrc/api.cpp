@@ -226,6 +226,22 @@ int seed_compress_ragged(const seed_shape* sh, const seed_state* st, int32_t min
   return compress_call(sh, st, min_m, true, ws, ws_bytes, stream);
 }
 
+int seed_compress_units(const seed_shape* sh, const seed_state* st, const int32_t* units, int32_t count,
+                        void* ws, size_t ws_bytes, void* stream) {
+  const int c = check_shape(sh);
+  if (c != SEED_OK) return c;
+  if (!state_ok(st) || count < 0 || (count > 0 && !units)) return SEED_ERR_ARG;
+  if (ws_bytes < seed_workspace_bytes(sh, SEED_OP_COMPRESS)) return SEED_ERR_WORKSPACE;
+  (void)ws;
+  if (!seed::compress_supported(*sh)) return SEED_ERR_UNSUPPORTED;
+  if (count == 0) return SEED_OK;
+  seed::CompressArgs a = compress_args(sh, st, sh->rank + 1);
+  a.ragged = 1;  // each listed unit at its own column count, when it holds columns beyond r
+  a.list = units;
+  a.list_len = count;
+  return hip_status(seed::launch_compress(*sh, a, static_cast<hipStream_t>(stream)));
+}
+
 int seed_compress(const seed_shape* sh, const seed_state* st, int32_t m, void* ws, size_t ws_bytes,
                   void* stream) {
   return compress_call(sh, st, m, false, ws, ws_bytes, stream);

@@ -403,7 +403,11 @@ __global__ __launch_bounds__(256) void k_compress(const CompressArgs A) {
   Core<CT>& S = *reinterpret_cast<Core<CT>*>(lds4);
   float* gam = reinterpret_cast<float*>(reinterpret_cast<char*>(lds4) + sizeof(Core<CT>));
   const int t = threadIdx.x;
-  const int64_t unit = blockIdx.x;
+  int64_t unit = blockIdx.x;
+  if (A.list != nullptr) {   // list mode: the unit this block compresses (an index out of range: none)
+    unit = A.list[blockIdx.x];
+    if (unit < 0 || unit >= A.units) return;
+  }
   const int r = A.rank, C = A.slots;
   float* __restrict__ sc = A.scale + unit * A.scale_len;
   int m = A.m;
@@ -885,7 +889,7 @@ hipError_t launch_compress(const seed_shape& sh, const CompressArgs& a, hipStrea
   size_t lds = 0;
   KFn fn = pick_compress(sh, &lds);
   if (!fn) return hipErrorInvalidValue;
-  return launch_big_lds(fn, lds, a.units, a, s);
+  return launch_big_lds(fn, lds, compress_blocks(a), a, s);
 }
 
 hipError_t launch_from_dense(const seed_shape& sh, const CompressArgs& a, hipStream_t s) {

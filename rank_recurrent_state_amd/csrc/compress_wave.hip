@@ -427,7 +427,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   const int lane = threadIdx.x;
   const int h = lane >> 5, c32 = lane & 31;
   const int row = N == 64 ? lane : c32;  // the core row this lane holds
-  const int64_t unit = blockIdx.x;
+  int64_t unit = blockIdx.x;
+  if (A.list != nullptr) {   // list mode: the unit this block compresses (an index out of range: none)
+    unit = A.list[blockIdx.x];
+    if (unit < 0 || unit >= A.units) return;
+  }
   const int r = A.rank, C = A.slots;
   float* __restrict__ sc = A.scale + unit * A.scale_len;
   int m = A.m;
@@ -1255,7 +1259,7 @@ hipError_t launch_compress_wave(const seed_shape& sh, const CompressArgs& a, hip
   WaveFn fn = pick_compress_wave(sh);
   *used = fn != nullptr;
   if (!fn) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(a.units)), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(compress_blocks(a))), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

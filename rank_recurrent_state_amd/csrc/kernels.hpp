@@ -69,7 +69,12 @@ struct CompressArgs {
   const float* vbar;  // from_dense only
   int32_t iters;      // from_dense only: subspace iterations (128 x 128 states)
   float* spectrum;    // spectrum mode only ([units][33]): the state is read, not written
+  const int32_t* list;  // list mode: block b compresses unit list[b] (ragged semantics); nullptr: block b is unit b
+  int32_t list_len;     // list mode: the number of blocks
 };
+
+// Blocks of a compression launch: one per listed unit, or one per unit.
+inline int64_t compress_blocks(const CompressArgs& a) { return a.list != nullptr ? a.list_len : a.units; }
 
 struct EnergyArgs {
   int64_t units;

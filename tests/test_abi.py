@@ -157,6 +157,11 @@ def test_invalid_arguments_are_rejected_on_the_host():
     srd = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16,
                          rounding=rrs.SEED_ROUND_STOCHASTIC)
     assert chunk(srd, 16, 4) == rrs.SEED_ERR_UNSUPPORTED
+    # listed compression: a negative count is an argument error, an empty list does nothing
+    assert rrs.LIB.seed_compress_units(ctypes.byref(sh), ctypes.byref(st.c), None, -1,
+                                       None, 0, None) == rrs.SEED_ERR_ARG
+    assert rrs.LIB.seed_compress_units(ctypes.byref(sh), ctypes.byref(st.c), None, 0,
+                                       None, 0, None) == rrs.SEED_OK
     # ragged chunk: len > period cannot fit any unit
     with pytest.raises(rrs.SeedError) as e:
         rrs.seed_decode_chunk_ragged(sh, st, 17, f, f, f, f, f, f, f, stream=0)

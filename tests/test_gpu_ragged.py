@@ -174,3 +174,53 @@ def test_uniform_calls_keep_the_counts():
         m += 1
     rrs.seed_compress(sh, st, m)
     assert np.all(rrs.column_counts(sh, st).numpy() == r)
+
+
+def test_compress_units_matches_ragged_scan():
+    """seed_compress_units over the units that are full gives, bit for bit, what
+    seed_compress_ragged gives (the same kernel per unit); units not listed, or listed with
+    m <= r, are left as they were."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_recurrent_state_amd as rrs
+    from gpu_util import to_device_inputs
+    w = synth.Workload("units", synth.GDN, 4, 3, 128, 128, 8, 8, 16, 16, synth.BF16, synth.BF16)
+    sh = rrs.make_shape(w.kind, w.batch, w.heads, 128, 128, 8, 8, synth.BF16, synth.BF16)
+    hc = synth.head_consts(w, 5)
+    gen = synth.rng(5)
+    n, H = w.units, w.heads
+    vbar = torch.tensor(hc.vbar, dtype=torch.float32, device="cuda")
+    S = torch.zeros((n, 128, 128), dtype=torch.float32, device="cuda")
+    o = torch.empty((n, 128), dtype=torch.bfloat16, device="cuda")
+    for _ in range(w.prefill):
+        dx = to_device_inputs(synth.step_inputs(w, hc, gen, n), synth.BF16)
+        rrs.seed_dense_decode_step(sh, S, dx["q"], dx["k"], dx["v"], dx["beta"], dx["g"], o)
+    st = rrs.State.empty(sh)
+    rrs.seed_state_from_dense(sh, S, vbar, st)
+    # request b takes 8 - 2 b steps: counts 16 (full), 14, 12, 10
+    for t in range(8):
+        dx = to_device_inputs(synth.step_inputs(w, hc, gen, n), synth.BF16)
+        act = torch.tensor([1 if t < 8 - 2 * (u // H) else 0 for u in range(n)], dtype=torch.uint8, device="cuda")
+        rrs.seed_decode_step_ragged(sh, st, dx["q"], dx["k"], dx["v"], dx["beta"], dx["g"], vbar, o, active=act)
+    m = rrs.column_counts(sh, st)
+    assert sorted(set(m.tolist())) == [10, 12, 14, 16]
+    a = rrs.State(*[t.clone() for t in st.tensors()])
+    b = rrs.State(*[t.clone() for t in st.tensors()])
+    rrs.seed_compress_ragged(sh, a, 16)                      # the full ones
+    full = torch.nonzero(m == 16).flatten().to(torch.int32).cuda()
+    rrs.seed_compress_units(sh, b, full)
+    torch.cuda.synchronize()
+    for x, y in zip(a.tensors(), b.tensors()):
+        assert torch.equal(x, y)
+    # every unit listed: each at its own count (all hold columns beyond r)
+    c = rrs.State(*[t.clone() for t in st.tensors()])
+    rrs.seed_compress_units(sh, c, torch.arange(n, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(rrs.column_counts(sh, c) == 8)
+    # a second call: every count is r now, so nothing changes
+    d = rrs.State(*[t.clone() for t in c.tensors()])
+    rrs.seed_compress_units(sh, d, torch.arange(n, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for x, y in zip(c.tensors(), d.tensors()):
+        assert torch.equal(x, y)
