@@ -418,6 +418,13 @@ __device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float
 
 }  // namespace cw
 
+// The draws of one group of eight elements, as a call: inlined sixteen times per factor it
+// pushed the stochastic-rounding kernel past the instruction cache.
+__device__ __noinline__ uint4 sr_group_call(uint32_t rng_key, uint32_t site, int slot, int64_t unit,
+                                            uint32_t window, int elem) {
+  return sr_group(rng_key, site, 0u, slot, unit, window, elem);
+}
+
 template <int DK, int DV, bool DIAG, int N, int FDT, bool SR>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 : 3))) void k_compress_wave(const CompressArgs A) {
   using namespace cw;
@@ -943,7 +950,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int d0 = NV * (8 * (j >> 2) + 4 * h + (j & 3));
-      if (sr && j % (8 / NV) == 0) dr = sr_group(A.rng_key, kSiteCompressV, 0u, c32, unit, window, d0);
+      if constexpr (SR) {
+        if (j % (8 / NV) == 0) dr = sr_group_call(A.rng_key, kSiteCompressV, c32, unit, window, d0);
+      }
 #pragma unroll
       for (int e = 0; e < NV / 2; ++e) {
         const float x0 = vt[2 * e][j], x1 = vt[2 * e + 1][j];
@@ -1049,7 +1058,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     for (int j = 0; j < 16; ++j) {
       const int i = 8 * (j >> 2) + 4 * h + (j & 3);
       const int d0 = NU * i;
-      if (sr && j % (8 / NU) == 0) dr = sr_group(A.rng_key, kSiteCompressU, 0u, c32, unit, window, d0);
+      if constexpr (SR) {
+        if (j % (8 / NU) == 0) dr = sr_group_call(A.rng_key, kSiteCompressU, c32, unit, window, d0);
+      }
       float g[NU];
 #pragma unroll
       for (int I = 0; I < NU; ++I) g[I] = 1.f;
