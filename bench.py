@@ -544,91 +544,34 @@ def energy_diagnostic(rrs, torch, w, sh, sh_l, states, vbars, U1, L, N, m_now, d
             "sink_share": sink_share}
 
 
-def _partition_streams(torch, split):
-    """Two streams on disjoint sets of XCDs (CU masks of whole 32-CU blocks; masks that split an
-    XCD were refused by the runtime here): the decode on the first `split` XCDs, the compression
-    on the rest. None when the runtime does not provide them."""
-    import ctypes
-    try:
-        hip = ctypes.CDLL("libamdhip64.so")
-    except OSError:
-        return None
-    ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    words = (ncu + 31) // 32
-    out = []
-    for pick in (lambda i: i // 32 < split, lambda i: i // 32 >= split):
-        mask = (ctypes.c_uint32 * words)()
-        for i in range(ncu):
-            if pick(i):
-                mask[i // 32] |= 1 << (i % 32)
-        h = ctypes.c_void_p()
-        if hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), mask) != 0:
-            return None
-        out.append(torch.cuda.ExternalStream(h.value))
-    return out
-
-
 def run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T, P, ev, log, steps=64, split=4):
-    """The same work as the lockstep step, with the compressions overlapped with the decode.
-
-    Decode is bound by HBM bandwidth, compression by vector arithmetic, so they can share the
-    chip: the decode launches go to a stream on half of the XCDs, each layer's compression to a
-    stream on the other half. Layer l's compression window is shifted by l mod T steps, so that
-    every step compresses one or two layers instead of every layer compressing on the same step.
-    Layer l's compression waits for its T-th decode launch (an event), and its next decode
-    launch waits for the compression. Every layer still decodes every step and compresses every
-    T steps at r + T columns. Returns ms per step and head-steps/s, or None."""
-    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
-        return None
+    """The same work as the lockstep step, with the compressions overlapped with the decode
+    (rank_recurrent_state_amd.OverlappedStack): decode launches on a stream over `split` XCDs,
+    each layer's compression on a stream over the others, the layers' windows shifted by l mod T
+    steps. Every layer still decodes every step and compresses every T steps at r + T columns.
+    Returns ms per step and head-steps/s, or None."""
     if L < 8:
         # one layer (or a few) leaves nothing to overlap with: the layer's own next decode
         # launch waits for its compression, on half the chip
         log("[bench] overlapped schedule: needs a stack of layers, skipped")
         return None
-    streams = _partition_streams(torch, split)
+    streams = rrs.partition_streams(split)
     if streams is None:
         log("[bench] overlapped schedule: CU-masked streams not available, skipped")
         return None
-    sA, sB = streams
+    stack = rrs.OverlappedStack(sh_l, states, *streams)
     cur = torch.cuda.current_stream()
-    # layer l's window starts at step l mod T: layers that share a start (l and l + T) are T
-    # launches apart in the step, so the first compression is done before the second starts
-    phase = [l % T for l in range(L)]
-    pending = [None] * L
-
-    def run(s0, n):
-        for s in range(s0, s0 + n):
-            xl = pool[s % P]
-            for l in range(L):
-                m = w.rank + (s - phase[l]) % T
-                if pending[l] is not None:
-                    sA.wait_event(pending[l])
-                    pending[l] = None
-                x = xl[l]
-                rrs.seed_decode_step(sh_l[l], states[l], m, x["q"], x["k"], x["v"], x["beta"], x["g"],
-                                     vbars[l], o[l], stream=sA)
-                if m + 1 == w.rank + T:
-                    e = torch.cuda.Event()
-                    e.record(sA)
-                    sB.wait_event(e)
-                    rrs.seed_compress(sh_l[l], states[l], w.rank + T, stream=sB)
-                    ec = torch.cuda.Event()
-                    ec.record(sB)
-                    pending[l] = ec
-
-    sA.wait_stream(cur)
-    sB.wait_stream(cur)
-    run(0, T)                      # warmup: brings every layer onto its shifted window
-    e0, e1 = ev(), ev()
-    cur.wait_stream(sA)
-    cur.wait_stream(sB)
+    stack.start()
+    for s in range(T):               # warmup: brings every layer onto its shifted window
+        stack.step(pool[s % P], vbars, o)
+    stack.finish()
     torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
     e0.record(cur)
-    sA.wait_stream(cur)
-    sB.wait_stream(cur)
-    run(T, steps)
-    cur.wait_stream(sA)
-    cur.wait_stream(sB)
+    stack.start()
+    for s in range(T, T + steps):
+        stack.step(pool[s % P], vbars, o)
+    stack.finish()
     e1.record(cur)
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / 1e3

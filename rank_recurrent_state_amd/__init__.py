@@ -26,10 +26,15 @@ _NAMES = {
 }
 
 
+_OVERLAP = {"OverlappedStack", "partition_streams"}
+
+
 def __getattr__(name):
     if name in _NAMES:
         return getattr(importlib.import_module("._lib", __name__), name)
+    if name in _OVERLAP:
+        return getattr(importlib.import_module(".overlap", __name__), name)
     raise AttributeError(name)
 
 
-__all__ = sorted(_NAMES)
+__all__ = sorted(_NAMES | _OVERLAP)
