@@ -251,7 +251,9 @@ int seed_compress_units(const seed_shape *shape, const seed_state *state, const 
  *          coefficients; the scales held before take the product of all len gates; the column
  *          count becomes m + len. KDA: a channel whose scale would fall below the floor of
  *          seed_decode_step is folded into the stored columns and a as there.
- * SEED_ERR_UNSUPPORTED for stochastic rounding.
+ * Stochastic rounding takes the draws the decode steps would take for the same stores (site,
+ * slot m + t, unit, window count, element; a KDA fold: site 6 with aux = m, the count before the
+ * chunk).
  * Source: picx.dev summary, "Exact Update (Lemma 2)" applied token after token, and
  * "Theoretical and Practical Implications", Lemma 1 (each part follows the head's recurrence).
  */

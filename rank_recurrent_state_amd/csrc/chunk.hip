@@ -102,6 +102,20 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(C) * DV;
   // row of token t in the [batch][L][heads] layout of the chunk's inputs and outputs
   auto tok = [&](int t) { return (bq * L + t) * H + hd; };
+  // factor stores: nearest, or stochastic with the draws the decode steps would take for the
+  // same columns (site, slot, unit, compression window, element)
+  const bool sr = FDT != 0 && A.rounding != 0;
+  const uint32_t window = sr ? __float_as_uint(sc[A.win_off]) : 0u;
+  auto put = [&](FT* dst, float x, uint32_t site, uint32_t aux, int slot, int elem) {
+    if constexpr (FDT != 0) {
+      if (sr) {
+        const uint4 dr = sr_group(A.rng_key, site, aux, slot, unit, window, elem);
+        *dst = round_sr<FDT>(x, draw16(dr, elem & 7));
+        return;
+      }
+    }
+    *dst = from_f32<FDT>(x);
+  };
 
   // ---- the U pass's column loads go out first: their latency overlaps the staging -------------
   // Wave wv takes column block jt = wv % 2; lane (c, h) loads row 32 jt + c of U: the whole row
@@ -182,7 +196,12 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
       const int t = i / (DK / 4), d = 4 * (i - t * (DK / 4));
       const float4 x4 = *reinterpret_cast<const float4*>(&S.K[t][d]);
       const float x[4] = {x4.x, x4.y, x4.z, x4.w};
-      store_f32<FDT, 4>(Ub + static_cast<int64_t>(m + t) * DK + d, x);
+      if (sr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put(Ub + static_cast<int64_t>(m + t) * DK + d + e, x[e], kSiteDecodeU, 0u, m + t, d + e);
+      } else {
+        store_f32<FDT, 4>(Ub + static_cast<int64_t>(m + t) * DK + d, x);
+      }
     }
   }
   // the keys and queries the U pass uses: as given (the slot scales apply per column), or KDA's
@@ -428,7 +447,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
 #pragma unroll
     for (int t = 0; t < LM; ++t) {
       S.W[t][d] = fmaf(cc[t], vbd, x[t]);
-      if (t < L) Vb[static_cast<int64_t>(m + t) * DV + d] = from_f32<FDT>(x[t]);
+      if (t < L) put(Vb + static_cast<int64_t>(m + t) * DV + d, x[t], kSiteDecodeV, 0u, m + t, d);
     }
     if (tid == 0) {
 #pragma unroll
@@ -473,14 +492,14 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
           // the key from the input again: its LDS copy now holds the residuals
           const float kv = to_f32<IDT>(reinterpret_cast<const IT*>(A.k)[tok(t) * DK + dd]);
           const float x = fold ? kv * rest : kv / (g0 * P[t]);
-          Ub[static_cast<int64_t>(m + t) * DK + dd] = from_f32<FDT>(x);
+          put(Ub + static_cast<int64_t>(m + t) * DK + dd, x, kSiteDecodeU, 0u, m + t, dd);
           rest *= S.Al[t][dd];
         }
       }
       if (fold) {
         for (int j = 0; j < m; ++j) {
           FT* e = Ub + static_cast<int64_t>(j) * DK + dd;
-          *e = from_f32<FDT>(to_f32<FDT>(*e) * gfin);
+          put(e, to_f32<FDT>(*e) * gfin, kSiteFoldU, static_cast<uint32_t>(m), j, dd);
         }
         A.a[unit * DK + dd] = S.a0[dd] * gfin;
       }
@@ -534,7 +553,6 @@ ChunkFn pick_chunk_dims(const seed_shape& sh) {
 template <int LM>
 ChunkFn pick_chunk_kind(const seed_shape& sh) {
   if (sh.rank + sh.period > kColsMax) return nullptr;
-  if (sh.rounding != SEED_ROUND_NEAREST) return nullptr;
   if (sh.kind == SEED_GDN) return pick_chunk_dims<true, false, LM>(sh);
   if (sh.kind == SEED_MAMBA2) return pick_chunk_dims<false, false, LM>(sh);
   return nullptr;
@@ -543,7 +561,7 @@ ChunkFn pick_chunk_kind(const seed_shape& sh) {
 ChunkFn pick_chunk(const seed_shape& sh, int len) {
   // KDA stages its gates and decayed keys as well: 16 tokens per call fit the LDS
   if (sh.kind == SEED_KDA) {
-    if (len > kChunkMaxDiag || sh.rank + sh.period > kColsMax || sh.rounding != SEED_ROUND_NEAREST) return nullptr;
+    if (len > kChunkMaxDiag || sh.rank + sh.period > kColsMax) return nullptr;
     return pick_chunk_dims<true, true, 16>(sh);
   }
   return len <= 16 ? pick_chunk_kind<16>(sh) : pick_chunk_kind<32>(sh);

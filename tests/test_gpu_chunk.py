@@ -270,3 +270,29 @@ def test_ragged_chunk():
             x = toks[u][t]
             a_t, U_t, V_t, o_t = orc.factored_step(w.kind, a_t, U_t, V_t, vb, x["q"], x["k"], x["v"], x["beta"], x["g"])
             assert rel_out(og[b, t, hh], o_t, orc.reconstruct(a_t, vb, U_t, V_t), x["q"]) <= out_tolerance(w)
+
+
+@pytest.mark.parametrize("kind,fdt", [(synth.GDN, synth.BF16), (synth.KDA, synth.F16), (synth.MAMBA2, synth.BF16)])
+def test_chunk_stochastic_rounding(kind, fdt):
+    """Stochastically rounded chunk stores stay within the format's tolerance of the oracle
+    (KDA with channels that fold), and the draws follow the key."""
+    import rank_recurrent_state_amd as rrs_mod
+    dv = 64 if kind == synth.MAMBA2 else 128
+    w = synth.Workload("chunksr", kind, 2, 3, 128, dv, 16, 16, 32, 24, fdt, synth.BF16)
+    rrs, torch, _, hc, gen, vbar, st0 = _prefilled(w, seed=71)
+    results = []
+    for key in (5, 5, 6):
+        sh = rrs_mod.make_shape(kind, w.batch, w.heads, 128, dv, 16, 16, fdt, synth.BF16,
+                                rounding=rrs_mod.SEED_ROUND_STOCHASTIC, rng_key=key)
+        st = rrs.State(*[t.clone() for t in st0.tensors()])
+        d = _chunk_inputs(w, hc, synth.rng(72), 12)
+        if kind == synth.KDA:
+            g = d["g"].clone()
+            g[:, 4, :, :32] = 0.0
+            d["g"] = g.contiguous()
+        eS, eo = check_chunk(rrs, torch, w, sh, st, w.rank, 12, d, vbar, hc, list(range(w.units)))
+        print(f"[chunk] sr {kind} {fdt} key {key}: S {eS:.2e} o {eo:.2e}", flush=True)
+        assert eS <= tolerance(w) and eo <= out_tolerance(w)
+        results.append([t.clone() for t in st.tensors()])
+    assert all(torch.equal(x, y) for x, y in zip(results[0], results[1]))
+    assert not torch.equal(results[0][2], results[2][2])          # V differs under another key
