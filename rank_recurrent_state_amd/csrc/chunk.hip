@@ -21,8 +21,10 @@
 // Design (gfx950): one 256-thread workgroup per unit; the scalar-decay kinds (GDN, Mamba-2).
 // The token count is padded to LM = 16 or 32 (a compiled width): the padding tokens have zero
 // inputs, so every loop runs to LM without a test, and only the stores look at L.
-//   staging      keys and queries of the chunk in LDS as fp32 (row stride d_k + 4: the
-//                pair products below read rows t and s in one access without bank conflicts);
+//   staging      keys and queries of the chunk in LDS (bf16 as given for bf16 inputs, else
+//                fp32; rows padded by 16 bytes, so that the pair products below read rows t and
+//                s without bank conflicts); they share their LDS with the residuals W, which
+//                are written only after their last read;
 //   U pass       U~^T kappa and U~^T q by MFMA 32x32x2 (fp32): one 32-column, 32-token tile
 //                per wave; each lane's row of U is loaded at the start of the kernel (its
 //                latency overlaps the staging), the key and query rows come from LDS;
@@ -47,13 +49,34 @@ constexpr int kChunkMax = 32;      // tokens per call
 constexpr int kChunkMaxDiag = 16;  // tokens per call, KDA
 constexpr int kColsMax = 64;   // column slots per unit
 
-template <int DK, int DV, int LM, bool DIAG>
+// The chunk's keys and queries in LDS: as given (bf16) when the inputs are bf16, so that a
+// 32-token chunk leaves room for three workgroups per CU; fp32 for fp32 inputs and for KDA,
+// whose decayed copies are formed from them. Rows are padded by 16 bytes.
+template <int IDT, bool DIAG> struct KqStore { using T = float; static constexpr int PAD = 4; };
+template <> struct KqStore<1, false> { using T = uint16_t; static constexpr int PAD = 8; };
+
+__device__ __forceinline__ float kqf(float x) { return x; }
+__device__ __forceinline__ float kqf(uint16_t x) { return bf16_to_f32(x); }
+
+// four consecutive elements of a key or query row as fp32
+__device__ __forceinline__ float4 kq4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 kq4(const uint16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xffff0000u));
+}
+
+template <int DK, int DV, int LM, bool DIAG, int IDT>
 struct ChunkSmem {
+  using KQ = typename KqStore<IDT, DIAG>::T;
+  static constexpr int KP = KqStore<IDT, DIAG>::PAD;
   union {
-    alignas(16) float K[LM][DK + 4];  // the chunk's keys (until the pair terms are done)
+    struct {
+      alignas(16) KQ K[LM][DK + KP];  // the chunk's keys and queries (until the pair terms are done)
+      alignas(16) KQ Q[LM][DK + KP];
+    } kq;
     alignas(16) float W[LM][DV];      // then the chunk's residuals delta_t = w_t + c_t vbar
   };
-  alignas(16) float Q[LM][DK + 4];
   alignas(16) float PK[kColsMax][LM];  // U~^T kappa_t (row j: column j of U)
   alignas(16) float PQ[kColsMax][LM];  // U~^T q_t
   float Gm[LM][LM + 1];                // Gm[t][s + 1] = Gamma(t, s), s = -1 .. t
@@ -82,7 +105,8 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   static_assert(!DIAG || DELTA, "the diagonal gate comes with the delta rule (KDA)");
   using FT = stor_t<FDT>;
   using IT = stor_t<IDT>;
-  __shared__ ChunkSmem<DK, DV, LM, DIAG> S;
+  __shared__ ChunkSmem<DK, DV, LM, DIAG, IDT> S;
+  using KQ = typename ChunkSmem<DK, DV, LM, DIAG, IDT>::KQ;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int64_t unit = blockIdx.x;
@@ -134,13 +158,24 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   // ---- staging (padding tokens: zero inputs, zero pair terms) ---------------------------------
   for (int i = tid; i < LM * (DK / 4); i += 256) {
     const int t = i / (DK / 4), d = 4 * (i - t * (DK / 4));
-    float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < L) {
-      load_f32<IDT, 4>(reinterpret_cast<const IT*>(A.k) + tok(t) * DK + d, x);
-      load_f32<IDT, 4>(reinterpret_cast<const IT*>(A.q) + tok(t) * DK + d, y);
+    if constexpr (sizeof(KQ) == 2) {
+      // the inputs' bf16 bits as they are
+      uint2 x = make_uint2(0u, 0u), y = make_uint2(0u, 0u);
+      if (t < L) {
+        x = *reinterpret_cast<const uint2*>(reinterpret_cast<const IT*>(A.k) + tok(t) * DK + d);
+        y = *reinterpret_cast<const uint2*>(reinterpret_cast<const IT*>(A.q) + tok(t) * DK + d);
+      }
+      *reinterpret_cast<uint2*>(&S.kq.K[t][d]) = x;
+      *reinterpret_cast<uint2*>(&S.kq.Q[t][d]) = y;
+    } else {
+      float x[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+      if (t < L) {
+        load_f32<IDT, 4>(reinterpret_cast<const IT*>(A.k) + tok(t) * DK + d, x);
+        load_f32<IDT, 4>(reinterpret_cast<const IT*>(A.q) + tok(t) * DK + d, y);
+      }
+      *reinterpret_cast<float4*>(&S.kq.K[t][d]) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(&S.kq.Q[t][d]) = make_float4(y[0], y[1], y[2], y[3]);
     }
-    *reinterpret_cast<float4*>(&S.K[t][d]) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(&S.Q[t][d]) = make_float4(y[0], y[1], y[2], y[3]);
   }
   for (int i = tid; i < kColsMax * LM; i += 256) {
     (&S.PK[0][0])[i] = 0.f;
@@ -177,8 +212,8 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
       float p = sc[dd];
       for (int t = 0; t < LM; ++t) {
         p *= S.Al[t][dd];
-        S.Kh[t][dd] = p * S.K[t][dd];
-        S.Qh[t][dd] = p * S.Q[t][dd];
+        S.Kh[t][dd] = p * kqf(S.kq.K[t][dd]);
+        S.Qh[t][dd] = p * kqf(S.kq.Q[t][dd]);
       }
     }
     __syncthreads();
@@ -194,7 +229,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     }
     for (int i = tid; i < L * (DK / 4); i += 256) {
       const int t = i / (DK / 4), d = 4 * (i - t * (DK / 4));
-      const float4 x4 = *reinterpret_cast<const float4*>(&S.K[t][d]);
+      const float4 x4 = kq4(&S.kq.K[t][d]);
       const float x[4] = {x4.x, x4.y, x4.z, x4.w};
       if (sr) {
 #pragma unroll
@@ -206,13 +241,13 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   }
   // the keys and queries the U pass uses: as given (the slot scales apply per column), or KDA's
   // decayed ones
-  auto krow = [&](int t) -> const float* {
-    if constexpr (DIAG) return &S.Kh[t][0];
-    else return &S.K[t][0];
+  auto krow = [&](int t) {
+    if constexpr (DIAG) return static_cast<const float*>(&S.Kh[t][0]);
+    else return static_cast<const KQ*>(&S.kq.K[t][0]);
   };
-  auto qrow = [&](int t) -> const float* {
-    if constexpr (DIAG) return &S.Qh[t][0];
-    else return &S.Q[t][0];
+  auto qrow = [&](int t) {
+    if constexpr (DIAG) return static_cast<const float*>(&S.Qh[t][0]);
+    else return static_cast<const KQ*>(&S.kq.Q[t][0]);
   };
   {
     // U pass by MFMA 32x32x2 (fp32): wave wv forms the 32 x 32 tile of column block jt = wv % 2
@@ -223,7 +258,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     const bool isq = wv >= 2;
     if (32 * ujt < m) {  // uniform
       const int c = lane & 31, h = lane >> 5;
-      const float* __restrict__ brow = c < LM ? (isq ? qrow(c) : krow(c)) : nullptr;
+      const auto brow = c < LM ? (isq ? qrow(c) : krow(c)) : nullptr;
       uint4 uraw2[FDT == 0 ? UW : 1];   // fp32 factors: the row's second half
       if constexpr (FDT == 0) {
 #pragma unroll
@@ -247,7 +282,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
             av = h ? hi16<FDT>(w) : lo16<FDT>(w);
           }
           av = ujok ? av : 0.f;
-          const float bv = brow != nullptr ? brow[d8 + 2 * e + h] : 0.f;
+          const float bv = brow != nullptr ? kqf(brow[d8 + 2 * e + h]) : 0.f;
           acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
         }
       }
@@ -304,7 +339,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
 #pragma unroll
       for (int e = 0; e < NA; ++e) {
         G[e] = 1.f;
-        ks[e] = S.K[s][NA * lane + e];
+        ks[e] = kqf(S.kq.K[s][NA * lane + e]);
       }
       for (int t = s; t < L; ++t) {
         float kk = 0.f, qk = 0.f;
@@ -312,8 +347,8 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
         for (int e = 0; e < NA; ++e) {
           if (t > s) G[e] *= S.Al[t][NA * lane + e];
           const float gk = G[e] * ks[e];
-          kk = fmaf(S.K[t][NA * lane + e], gk, kk);
-          qk = fmaf(S.Q[t][NA * lane + e], gk, qk);
+          kk = fmaf(kqf(S.kq.K[t][NA * lane + e]), gk, kk);
+          qk = fmaf(kqf(S.kq.Q[t][NA * lane + e]), gk, qk);
         }
         kk = wave_sum(kk);
         qk = wave_sum(qk);
@@ -333,9 +368,9 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     float kk = 0.f, qk = 0.f;
 #pragma unroll 4
     for (int d = 0; d < DK; d += 4) {
-      const float4 ks = *reinterpret_cast<const float4*>(&S.K[s][d]);
-      const float4 kt = *reinterpret_cast<const float4*>(&S.K[t][d]);
-      const float4 qt = *reinterpret_cast<const float4*>(&S.Q[t][d]);
+      const float4 ks = kq4(&S.kq.K[s][d]);
+      const float4 kt = kq4(&S.kq.K[t][d]);
+      const float4 qt = kq4(&S.kq.Q[t][d]);
       kk += kt.x * ks.x + kt.y * ks.y + kt.z * ks.z + kt.w * ks.w;
       qk += qt.x * ks.x + qt.y * ks.y + qt.z * ks.z + qt.w * ks.w;
     }
@@ -353,8 +388,8 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
       float xk = 0.f, xq = 0.f;
 #pragma unroll
       for (int e = 0; e < NA; ++e) {
-        xk += S.a0[NA * lane + e] * krow(t)[NA * lane + e];
-        xq += S.a0[NA * lane + e] * qrow(t)[NA * lane + e];
+        xk += S.a0[NA * lane + e] * kqf(krow(t)[NA * lane + e]);
+        xq += S.a0[NA * lane + e] * kqf(qrow(t)[NA * lane + e]);
       }
       xk = s0 * xk + cj * S.PK[lane][t];
       xq = s0 * xq + cj * S.PQ[lane][t];
