@@ -79,17 +79,17 @@ struct ChunkSmem {
   };
   alignas(16) float PK[kColsMax][LM];  // U~^T kappa_t (row j: column j of U)
   alignas(16) float PQ[kColsMax][LM];  // U~^T q_t
-  float Gm[LM][LM + 1];                // Gm[t][s + 1] = Gamma(t, s), s = -1 .. t
+  float Gm[DIAG ? 1 : LM][LM + 1];     // Gm[t][s + 1] = Gamma(t, s), s = -1 .. t (scalar decay)
   float Akk[LM][LM + 1];               // A[t][s] = beta_t Gamma(t, s) kappa_t . kappa_s, s < t
   float Aqk[LM][LM + 1];               // Gamma(t, s) q_t . kappa_s, s <= t
   float vb[DV];
   float a0[DK];
   float g[LM], beta[LM], omega[LM], aK[LM], aQ[LM], c[LM];
-  // KDA only: the gates, and the keys and queries decayed to the chunk's start and through the
-  // state's own channel scales (Gamma P_t kappa_t, Gamma P_t q_t)
+  // KDA only: the gates, and each token's decay from the state held before the chunk through
+  // the state's own channel scales, Gamma P_t (the decayed keys and queries are this times the
+  // keys and queries)
   float Al[DIAG ? LM : 1][DIAG ? DK : 1];
-  alignas(16) float Kh[DIAG ? LM : 1][DIAG ? DK + 4 : 4];
-  alignas(16) float Qh[DIAG ? LM : 1][DIAG ? DK + 4 : 4];
+  float Pg[DIAG ? LM : 1][DIAG ? DK + 1 : 1];
 };
 
 // KDA: a channel whose scale would fall below this is folded into the stored columns (as in the
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
   for (int i = tid; i < LM * (LM + 1); i += 256) {
     (&S.Akk[0][0])[i] = 0.f;
     (&S.Aqk[0][0])[i] = 0.f;
-    (&S.Gm[0][0])[i] = 0.f;
+    if constexpr (!DIAG) (&S.Gm[0][0])[i] = 0.f;
   }
   for (int i = tid; i < DV; i += 256) S.vb[i] = A.vbar[static_cast<int64_t>(hd) * DV + i];
   for (int i = tid; i < DK; i += 256) S.a0[i] = A.a[unit * DK + i];
@@ -206,14 +206,13 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
 
   // ---- decay products, the new U columns, U~^T kappa and U~^T q, the value split ----------------
   if constexpr (DIAG) {
-    // channel d: P_t = prod_{u <= t} alpha_u (running), the true-state keys and queries
-    // Gamma P_t kappa_t, Gamma P_t q_t for the terms of the state held before the chunk
+    // channel d: Gamma P_t with P_t = prod_{u <= t} alpha_u (running), the decay of the
+    // terms of the state held before the chunk
     for (int dd = tid; dd < DK; dd += 256) {
       float p = sc[dd];
       for (int t = 0; t < LM; ++t) {
         p *= S.Al[t][dd];
-        S.Kh[t][dd] = p * kqf(S.kq.K[t][dd]);
-        S.Qh[t][dd] = p * kqf(S.kq.Q[t][dd]);
+        S.Pg[t][dd] = p;
       }
     }
     __syncthreads();
@@ -240,14 +239,14 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     }
   }
   // the keys and queries the U pass uses: as given (the slot scales apply per column), or KDA's
-  // decayed ones
-  auto krow = [&](int t) {
-    if constexpr (DIAG) return static_cast<const float*>(&S.Kh[t][0]);
-    else return static_cast<const KQ*>(&S.kq.K[t][0]);
+  // decayed ones, Gamma P_t kappa_t and Gamma P_t q_t
+  auto kval = [&](int t, int d) {
+    if constexpr (DIAG) return S.Pg[t][d] * kqf(S.kq.K[t][d]);
+    else return kqf(S.kq.K[t][d]);
   };
-  auto qrow = [&](int t) {
-    if constexpr (DIAG) return static_cast<const float*>(&S.Qh[t][0]);
-    else return static_cast<const KQ*>(&S.kq.Q[t][0]);
+  auto qval = [&](int t, int d) {
+    if constexpr (DIAG) return S.Pg[t][d] * kqf(S.kq.Q[t][d]);
+    else return kqf(S.kq.Q[t][d]);
   };
   {
     // U pass by MFMA 32x32x2 (fp32): wave wv forms the 32 x 32 tile of column block jt = wv % 2
@@ -258,7 +257,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
     const bool isq = wv >= 2;
     if (32 * ujt < m) {  // uniform
       const int c = lane & 31, h = lane >> 5;
-      const auto brow = c < LM ? (isq ? qrow(c) : krow(c)) : nullptr;
+      const bool cok = c < LM;
       uint4 uraw2[FDT == 0 ? UW : 1];   // fp32 factors: the row's second half
       if constexpr (FDT == 0) {
 #pragma unroll
@@ -282,7 +281,7 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
             av = h ? hi16<FDT>(w) : lo16<FDT>(w);
           }
           av = ujok ? av : 0.f;
-          const float bv = brow != nullptr ? kqf(brow[d8 + 2 * e + h]) : 0.f;
+          const float bv = cok ? (isq ? qval(c, d8 + 2 * e + h) : kval(c, d8 + 2 * e + h)) : 0.f;
           acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
         }
       }
@@ -388,8 +387,8 @@ __global__ __launch_bounds__(256) void k_decode_chunk(const StepArgs A) {
       float xk = 0.f, xq = 0.f;
 #pragma unroll
       for (int e = 0; e < NA; ++e) {
-        xk += S.a0[NA * lane + e] * kqf(krow(t)[NA * lane + e]);
-        xq += S.a0[NA * lane + e] * kqf(qrow(t)[NA * lane + e]);
+        xk += S.a0[NA * lane + e] * kval(t, NA * lane + e);
+        xq += S.a0[NA * lane + e] * qval(t, NA * lane + e);
       }
       xk = s0 * xk + cj * S.PK[lane][t];
       xq = s0 * xq + cj * S.PQ[lane][t];
