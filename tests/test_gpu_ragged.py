@@ -176,31 +176,33 @@ def test_uniform_calls_keep_the_counts():
     assert np.all(rrs.column_counts(sh, st).numpy() == r)
 
 
-def test_compress_units_matches_ragged_scan():
+@pytest.mark.parametrize("fdt", [synth.BF16, synth.F32])
+def test_compress_units_matches_ragged_scan(fdt):
     """seed_compress_units over the units that are full gives, bit for bit, what
-    seed_compress_ragged gives (the same kernel per unit); units not listed, or listed with
-    m <= r, are left as they were."""
+    seed_compress_ragged gives (the same kernel per unit: the one-wave kernel for bf16 factors,
+    the workgroup kernel for fp32); units not listed, or listed with m <= r, are left as they
+    were."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import rank_recurrent_state_amd as rrs
     from gpu_util import to_device_inputs
-    w = synth.Workload("units", synth.GDN, 4, 3, 128, 128, 8, 8, 16, 16, synth.BF16, synth.BF16)
-    sh = rrs.make_shape(w.kind, w.batch, w.heads, 128, 128, 8, 8, synth.BF16, synth.BF16)
+    w = synth.Workload("units", synth.GDN, 4, 3, 128, 128, 8, 8, 16, 16, fdt, fdt)
+    sh = rrs.make_shape(w.kind, w.batch, w.heads, 128, 128, 8, 8, fdt, fdt)
     hc = synth.head_consts(w, 5)
     gen = synth.rng(5)
     n, H = w.units, w.heads
     vbar = torch.tensor(hc.vbar, dtype=torch.float32, device="cuda")
     S = torch.zeros((n, 128, 128), dtype=torch.float32, device="cuda")
-    o = torch.empty((n, 128), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((n, 128), dtype=torch.bfloat16 if fdt else torch.float32, device="cuda")
     for _ in range(w.prefill):
-        dx = to_device_inputs(synth.step_inputs(w, hc, gen, n), synth.BF16)
+        dx = to_device_inputs(synth.step_inputs(w, hc, gen, n), fdt)
         rrs.seed_dense_decode_step(sh, S, dx["q"], dx["k"], dx["v"], dx["beta"], dx["g"], o)
     st = rrs.State.empty(sh)
     rrs.seed_state_from_dense(sh, S, vbar, st)
     # request b takes 8 - 2 b steps: counts 16 (full), 14, 12, 10
     for t in range(8):
-        dx = to_device_inputs(synth.step_inputs(w, hc, gen, n), synth.BF16)
+        dx = to_device_inputs(synth.step_inputs(w, hc, gen, n), fdt)
         act = torch.tensor([1 if t < 8 - 2 * (u // H) else 0 for u in range(n)], dtype=torch.uint8, device="cuda")
         rrs.seed_decode_step_ragged(sh, st, dx["q"], dx["k"], dx["v"], dx["beta"], dx["g"], vbar, o, active=act)
     m = rrs.column_counts(sh, st)
