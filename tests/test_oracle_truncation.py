@@ -153,3 +153,18 @@ def test_from_dense_full_rank_is_exact():
         a, U, V, err = orc.from_dense(S, vbar, min(dk, dv))
         np.testing.assert_allclose(orc.reconstruct(a, vbar, U, V), S, atol=1e-12)
         assert err < 1e-12
+
+
+def test_singular_values_and_gap_of_a_known_spectrum():
+    """A matrix built as P diag(s) Q^T with orthogonal P, Q has singular values s (sorted,
+    non-negative, sign-free), and its relative gap at rank r is (s_r - s_{r+1}) / s_1."""
+    rng = np.random.default_rng(7)
+    s = np.array([5.0, -3.0, 2.0, 0.5])          # a negative entry flips one column's sign
+    P, _ = np.linalg.qr(rng.standard_normal((6, 6)))
+    Q, _ = np.linalg.qr(rng.standard_normal((4, 4)))
+    C = P[:, :4] @ np.diag(s) @ Q.T
+    got = orc.singular_values(C)
+    assert np.allclose(got, [5.0, 3.0, 2.0, 0.5], atol=1e-12)
+    assert orc.relative_gap(C, 2) == pytest.approx((3.0 - 2.0) / 5.0, abs=1e-12)
+    assert orc.relative_gap(C, 4) == 1.0            # rank <= r
+    assert orc.relative_gap(np.zeros((3, 3)), 1) == 1.0
