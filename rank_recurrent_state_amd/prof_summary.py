@@ -6,7 +6,10 @@
     python -m rank_recurrent_state_amd.prof_summary pmc FETCH_DIR WRITE_DIR [--copy-bytes B]
         per-kernel average FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two
         `rocprofv3 --pmc ... --output-format csv` runs, scaled to bytes by what the same counters
-        read for the calibration copy of B bytes (the largest copy kernel in the run).
+        read for the calibration copy of B bytes (the largest copy kernel in the run);
+    python -m rank_recurrent_state_amd.prof_summary counters DIR
+        per-kernel dispatch count and average value per dispatch of every counter in a
+        `rocprofv3 --pmc ... --output-format csv -d DIR` run.
 
 Only reads the CSV files rocprofv3 wrote; prints plain text.
 """
@@ -95,6 +98,19 @@ def pmc(fetch_dir: str, write_dir: str, copy_bytes: int) -> None:
         print(f"{max(len(fv), len(wv)):7d} {fa:12.1f} {wa:12.1f} {rb:14.0f} {wb:14.0f}  {short(name)}")
 
 
+def counters(d: str) -> None:
+    rows = _rows(d, "counter_collection.csv")
+    names = sorted({_col(r, "Counter_Name", "counter_name") for r in rows})
+    agg = {n: _pmc(d, n) for n in names}
+    kernels = sorted({k for a in agg.values() for k in a},
+                     key=lambda k: -max(sum(a.get(k, [0])) for a in agg.values()))
+    print(f"{'calls':>7} " + " ".join(f"{n:>20}" for n in names) + "  kernel")
+    for k in kernels:
+        calls = max(len(a.get(k, [])) for a in agg.values())
+        vals = [(sum(a[k]) / len(a[k])) if a.get(k) else float("nan") for a in agg.values()]
+        print(f"{calls:7d} " + " ".join(f"{v:20.1f}" for v in vals) + f"  {short(k)}")
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -104,9 +120,13 @@ def main(argv=None) -> None:
     p.add_argument("fetch_dir")
     p.add_argument("write_dir")
     p.add_argument("--copy-bytes", type=int, default=1 << 30)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         trace(a.dir)
+    elif a.cmd == "counters":
+        counters(a.dir)
     else:
         pmc(a.fetch_dir, a.write_dir, a.copy_bytes)
 
