@@ -15,12 +15,17 @@ steps after --warmup untimed ones, bracketed by torch.cuda.synchronize(); inputs
 in HBM (a pool of --pool steps of seeded inputs, cycled).
 
 Algorithmic bytes per unit-step of the decode at m columns (what the method must move):
-  read the sink a_0 (4 d_k) and its m - r window coefficients (4 (m - r)), U and V
-  (f (d_k + d_v) m), q, k, v (e (2 d_k + d_v)), beta and g (4 + 4 or 4 d_k); write the new
-  coefficient (4), the new column pair (f (d_k + d_v)) and o (e d_v). f = factor bytes,
-  e = activation bytes. The lazy decay scales and vbar are not credited. The sink is lazy: a
-  step adds a multiple of its key to a, and the key is the column it appends to U, so a step
-  stores that multiple and a is rebuilt only at compression.
+  read the sink a (4 d_k), U and V (f (d_k + d_v) m), q, k, v (e (2 d_k + d_v)), beta and g
+  (4 + 4 or 4 d_k); write a (4 d_k), the new column pair (f (d_k + d_v)) and o (e d_v).
+  f = factor bytes, e = activation bytes; the lazy decay scales and vbar are not credited.
+  The roofline fraction is taken on these bytes. The kernel's own accounting is reported
+  beside it: the sink is lazy (a step adds a multiple of its key to a, and the key is the
+  column it appends to U, so a step stores that multiple and a is rebuilt only at
+  compression), so it reads a_0 and the window's m - r coefficients and writes one float in
+  place of a.
+Timing: whole compression windows (T decode steps of every layer, then the compression),
+at least five of them whatever --steps asks; the median and the spread over the windows are
+reported beside the total.
 Dense step per unit: 8 d_k d_v (fp32 state read and written) + inputs + o.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -44,6 +49,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_gdn-stack36_hbm_traffic.txt")
 DECODE_SOURCES = ("rank_recurrent_state_amd/csrc/decode.hip", "rank_recurrent_state_amd/csrc/common.hpp",
                   "rank_recurrent_state_amd/csrc/kernels.hpp")
+MIN_WINDOWS = 5
 METRIC = "factored decode head-steps/s + achieved HBM GB/s (% roofline) vs dense-state kernel"
 
 
@@ -126,6 +132,18 @@ def decode_bytes(w, m: int) -> int:
             + 4 + gb + 4 + f * (w.d_k + w.d_v) + e * w.d_v)
 
 
+def decode_bytes_alg(w, m: int) -> int:
+    """The algorithmic bytes of one unit-step as the hot-path table defines them: read a (4 d_k),
+    U and V (f (d_k + d_v) m), q, k, v and beta, g; write a (4 d_k), the new column pair and o.
+    The lazy sink moves fewer bytes than this (it writes one coefficient instead of a, and
+    reads the window's coefficients), so the fraction on these bytes is the one reported."""
+    f = 2 if w.factor_dtype else 4
+    e = 2 if w.io_dtype else 4
+    gb = 4 * w.d_k if w.kind == 1 else 4
+    return (4 * w.d_k + f * (w.d_k + w.d_v) * m + e * (2 * w.d_k + w.d_v) + 4 + gb
+            + 4 * w.d_k + f * (w.d_k + w.d_v) + e * w.d_v)
+
+
 def compress_bytes(w, m: int) -> int:
     f = 2 if w.factor_dtype else 4
     return f * (w.d_k + w.d_v) * (m + w.rank)
@@ -135,6 +153,26 @@ def dense_bytes(w) -> int:
     e = 2 if w.io_dtype else 4
     gb = 4 * w.d_k if w.kind == 1 else 4
     return 8 * w.d_k * w.d_v + e * (2 * w.d_k + w.d_v) + 4 + gb + e * w.d_v
+
+
+def host_cpu() -> dict:
+    """The host's CPU model, its logical CPU count, and the share this process may use: the CPUs
+    in its affinity mask, at most 16 (the host cores allotted to one GPU)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cpus = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = cpus
+    return {"model": model, "cpus": cpus, "share": max(1, min(16, avail))}
 
 
 def cpu_worker(job):
@@ -241,10 +279,10 @@ def main():
     log(f"[bench] prefill-end compression done in {t_from_dense:.1f} s")
 
     T = w.period
-    K = -(-args.steps // T) * T          # whole compression windows
+    K = max(-(-args.steps // T), MIN_WINDOWS) * T   # whole compression windows, at least five
     Wu = -(-args.warmup // T) * T
     if K != args.steps or Wu != args.warmup:
-        log(f"[bench] steps/warmup rounded up to whole windows of T={T}: {K}/{Wu}")
+        log(f"[bench] steps/warmup rounded up to whole windows of T={T} (at least {MIN_WINDOWS} timed): {K}/{Wu}")
     nwin = max(1, min(args.pool // T, (Wu + K) // T))
     P = nwin * T
     pool = []
@@ -346,7 +384,18 @@ def main():
     t_cmp = sum(b_.elapsed_time(c_) for _, b_, c_ in evs) / 1e3
     n_dec_launch = K * L
     n_cmp_launch = nw * cmp_calls
-    dec_bytes = nw * L * U1 * sum(decode_bytes(w, w.rank + j) for j in range(T))
+    dec_bytes = nw * L * U1 * sum(decode_bytes_alg(w, w.rank + j) for j in range(T))
+    dec_bytes_own = nw * L * U1 * sum(decode_bytes(w, w.rank + j) for j in range(T))
+    win_ms = sorted(a_.elapsed_time(c_) / T for a_, _, c_ in evs)        # ms per step, per window
+    win_dec_us = sorted(a_.elapsed_time(b_) * 1e3 / (T * L) for a_, b_, _ in evs)
+    win_cmp_ms = sorted(b_.elapsed_time(c_) for _, b_, c_ in evs)
+    median = lambda xs: (xs[(len(xs) - 1) // 2] + xs[len(xs) // 2]) / 2  # noqa: E731
+    windows = {"count": nw, "steps_each": T,
+               "ms_per_step": {"median": median(win_ms), "min": win_ms[0], "max": win_ms[-1]},
+               "decode_us_per_launch": {"median": median(win_dec_us), "min": win_dec_us[0],
+                                        "max": win_dec_us[-1]},
+               "compress_ms_per_window": {"median": median(win_cmp_ms), "min": win_cmp_ms[0],
+                                          "max": win_cmp_ms[-1]}}
     cmp_bytes = nw * N * compress_bytes(w, w.rank + T)
     head_steps = N * K
     value = head_steps / t_total
@@ -355,6 +404,10 @@ def main():
     log(f"[bench] timed {K} steps: {t_total * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms); decode "
         f"{t_dec * 1e3:.1f} ms over {n_dec_launch} launches ({dec_gbs:.0f} GB/s), compress "
         f"{t_cmp * 1e3:.1f} ms over {n_cmp_launch} launches")
+    log(f"[bench] {nw} windows: {windows['ms_per_step']['median']:.3f} ms per step median "
+        f"({win_ms[0]:.3f} .. {win_ms[-1]:.3f}); decode {windows['decode_us_per_launch']['median']:.2f} us "
+        f"per launch median ({win_dec_us[0]:.2f} .. {win_dec_us[-1]:.2f}); compression "
+        f"{windows['compress_ms_per_window']['median']:.2f} ms per window median")
 
     # ---- the state-energy diagnostic (not part of a step): one launch per layer ----------------
     diag = not args.no_diagnostics
@@ -456,7 +509,8 @@ def main():
         import multiprocessing as mp
 
         ah, Uh, Vh, xs_h, vb_h, ns = cpu_job
-        cores = min(16, os.cpu_count() or 1)
+        host = host_cpu()
+        cores = host["share"]
         states_h = [(ah[u], Uh[u].T.copy(), Vh[u].T.copy()) for u in range(ns)]
         inputs_h = [[{k: x[k][u] for k in x} for x in xs_h] for u in range(ns)]
         heads = [vb_h[u // U1][u % w.heads] for u in range(ns)]
@@ -467,7 +521,7 @@ def main():
             cpu_secs = pool_.map(cpu_worker, shards)
         c_wall = time.perf_counter() - c0
         cpu = {"value": ns * w.period / c_wall, "unit": "head-steps/s", "cores": cores,
-               "kind": "oracle",
+               "kind": "oracle", "host_cpus": host["cpus"], "cpu_model": host["model"],
                "sample": f"{ns} units (layers 0..{-(-ns // U1) - 1}) x one compression window ({w.period} decode "
                          f"steps + 1 compression), fp64 NumPy oracle, {sum(cpu_secs):.1f} s of "
                          f"CPU work on {cores} processes"}
@@ -501,7 +555,10 @@ def main():
                                  if args.factor_dtype is None and args.rounding == "nearest" else None),
                      "kernel": "k_decode (factored read-out + update)",
                      "bytes_per_launch": dec_bytes / n_dec_launch,
-                     "avg_launch_us": avg_launch_us},
+                     "avg_launch_us": avg_launch_us,
+                     "lazy_sink_bytes_per_launch": dec_bytes_own / n_dec_launch,
+                     "frac_on_lazy_sink_bytes": dec_bytes_own / t_dec / 1e9 / HBM_PEAK_GBS},
+        "windows": windows,
         "cpu_baseline": cpu,
         "decode_only": {"head_steps_per_s": head_steps / t_dec, "ms_per_step": dec_step_ms,
                         "gbs": dec_gbs},
@@ -555,10 +612,22 @@ def run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T, P, ev, log
         # launch waits for its compression, on half the chip
         log("[bench] overlapped schedule: needs a stack of layers, skipped")
         return None
+    if rrs.under_profiler():
+        log("[bench] overlapped schedule: not run under the profiler (a profiled run of it crashed, "
+            "cause not shown), skipped")
+        return None
     streams = rrs.partition_streams(split)
     if streams is None:
         log("[bench] overlapped schedule: CU-masked streams not available, skipped")
         return None
+    try:
+        return _run_overlapped(rrs, torch, sh_l, states, pool, vbars, o, T, P, ev, log, steps, split, streams)
+    finally:
+        for st in streams:
+            st.close()
+
+
+def _run_overlapped(rrs, torch, sh_l, states, pool, vbars, o, T, P, ev, log, steps, split, streams):
     stack = rrs.OverlappedStack(sh_l, states, *streams)
     cur = torch.cuda.current_stream()
     stack.start()

@@ -331,6 +331,24 @@ int seed_dense_decode_step(const seed_shape *shape, float *S, const void *q, con
                            const void *v, const float *beta, const float *g, void *o,
                            void *stream);
 
+/*
+ * Streams restricted to a set of compute units, for schedules that run the HBM-bound decode and
+ * the arithmetic-bound compression side by side on disjoint parts of the chip. These are the
+ * library's own HIP runtime calls, so the stream belongs to the runtime that launches the
+ * kernels.
+ *   cu_mask     mask_words (1 .. 64) words; bit i of word w selects compute unit 32 w + i; at
+ *               least one bit set. The runtime may refuse masks it cannot honour (on MI355X,
+ *               masks that split an XCD's block of 32 compute units were refused).
+ *   *stream     receives the new hipStream_t (NULL on failure). It has the default priority.
+ * Returns SEED_ERR_ARG for a null pointer, an empty mask or a bad word count, SEED_ERR_HIP when
+ * the runtime refuses. The caller owns the stream and releases it with seed_stream_destroy
+ * after the work queued on it has finished.
+ */
+int seed_stream_create_cu_masked(uint32_t mask_words, const uint32_t *cu_mask, void **stream);
+
+/* Destroys a stream made by seed_stream_create_cu_masked (SEED_ERR_ARG for NULL). */
+int seed_stream_destroy(void *stream);
+
 /* Static text for a status code. */
 const char *seed_status_string(int status);
 

@@ -24,7 +24,7 @@ EXPORTS = [
     "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
     "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_decode_chunk",
     "seed_chunk_max_tokens", "seed_decode_chunk_ragged", "seed_state_spectrum", "seed_compress_units",
-    "seed_status_string", "seed_version",
+    "seed_stream_create_cu_masked", "seed_stream_destroy", "seed_status_string", "seed_version",
 ]
 
 SEED_SPECTRUM_LEN = 33
@@ -57,10 +57,30 @@ class SeedError(RuntimeError):
         self.status = status
 
 
+def hip_runtimes_mapped() -> list:
+    """Paths of the HIP runtime libraries (libamdhip64) mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and "libamdhip64" in os.path.basename(parts[-1]):
+                    found.add(os.path.realpath(parts[-1]))
+    except OSError:
+        pass
+    return sorted(found)
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m rank_recurrent_state_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
+    # libseed binds to whichever HIP runtime the process already holds (torch's, when torch is
+    # imported first). Two copies would give two sets of streams and device state, and a
+    # stream of one handed to the other: refuse that outright.
+    rts = hip_runtimes_mapped()
+    if len(rts) > 1:
+        raise ImportError(f"more than one HIP runtime is mapped into this process: {rts}")
     P = ctypes.c_void_p
     Sp = ctypes.POINTER(seed_shape)
     Stp = ctypes.POINTER(seed_state)
@@ -82,6 +102,8 @@ def _load():
         "seed_compress_units": (ctypes.c_int, [Sp, Stp, P, ctypes.c_int32, P, ctypes.c_size_t, P]),
         "seed_decode_chunk_ragged": (ctypes.c_int, [Sp, Stp, P, ctypes.c_int32, P, P, P, P, P, P, P, P]),
         "seed_state_spectrum": (ctypes.c_int, [Sp, Stp, P, P]),
+        "seed_stream_create_cu_masked": (ctypes.c_int, [ctypes.c_uint32, P, ctypes.POINTER(ctypes.c_void_p)]),
+        "seed_stream_destroy": (ctypes.c_int, [P]),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "seed_version": (ctypes.c_char_p, []),
     }
@@ -215,6 +237,41 @@ def _expect_io(shape, q, k, v, beta, g, o):
     _expect("beta", beta, n, SEED_F32)
     _expect("g", g, n * (shape.d_k if shape.kind == SEED_KDA else 1), SEED_F32)
     _expect("o", o, n * shape.d_v, shape.io_dtype)
+
+
+class CUMaskedStream:
+    """A HIP stream restricted to a set of compute units, made and destroyed by libseed (so it
+    belongs to the runtime that launches the kernels). `.torch` is a torch ExternalStream view of
+    it for use with torch's stream and event API; close() (or the context manager) destroys the
+    stream after synchronising it."""
+
+    def __init__(self, cu_mask_words):
+        words = list(cu_mask_words)
+        arr = (ctypes.c_uint32 * len(words))(*words)
+        h = ctypes.c_void_p()
+        _check("seed_stream_create_cu_masked", LIB.seed_stream_create_cu_masked(len(words), arr, ctypes.byref(h)))
+        self.handle = h.value
+        import torch
+        self.torch = torch.cuda.ExternalStream(self.handle)
+
+    def close(self):
+        if self.handle:
+            self.torch.synchronize()
+            _check("seed_stream_destroy", LIB.seed_stream_destroy(ctypes.c_void_p(self.handle)))
+            self.handle = None
+            self.torch = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def seed_state_from_dense(shape: seed_shape, S, vbar, state, ws=None, stream=None) -> None:

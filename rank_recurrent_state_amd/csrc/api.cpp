@@ -298,6 +298,26 @@ int seed_dense_decode_step(const seed_shape* sh, float* S, const void* q, const 
   return hip_status(seed::launch_dense(*sh, a, static_cast<hipStream_t>(stream)));
 }
 
+int seed_stream_create_cu_masked(uint32_t mask_words, const uint32_t* cu_mask, void** stream) {
+  if (!stream || !cu_mask || mask_words == 0 || mask_words > 64) return SEED_ERR_ARG;
+  *stream = nullptr;
+  uint32_t any = 0;
+  for (uint32_t i = 0; i < mask_words; ++i) any |= cu_mask[i];
+  if (any == 0) return SEED_ERR_ARG;
+  hipStream_t s = nullptr;
+  if (hipExtStreamCreateWithCUMask(&s, mask_words, cu_mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return SEED_ERR_HIP;
+  }
+  *stream = s;
+  return SEED_OK;
+}
+
+int seed_stream_destroy(void* stream) {
+  if (!stream) return SEED_ERR_ARG;
+  return hip_status(hipStreamDestroy(static_cast<hipStream_t>(stream)));
+}
+
 const char* seed_status_string(int status) {
   switch (status) {
     case SEED_OK: return "ok";

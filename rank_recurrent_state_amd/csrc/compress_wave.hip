@@ -57,6 +57,15 @@ constexpr int kGrid = 128;      // points of the shared Sturm grid (two per lane
 constexpr int NSEC = 7;         // 5-section steps after the 128-point grid (129 * 5^7 ~ 1e7)
 constexpr float kPivTol = 1e-7f;
 constexpr float kReduceFloor = 1e-30f;  // squared column norm below which no reflector is built
+// Eigenvalues of the core below kEigFloor times the largest give zero columns. The fp32 core
+// resolves no finer: B carries fp32 rounding of about 1e-7 of its norm, and the Sturm search
+// stops at about 1e-7 of its Gershgorin range. Below that, the computed eigenvalue can sit far
+// above the direction's true Rayleigh quotient, and the computed vector keeps rounding-level
+// components along the dominant directions; V' = V L y lambda^(-1/4) then points mostly along
+// a dominant direction, and U' = M V' / sigma adds that direction a second time (seen on
+// Mamba-2 states whose column decays span 16 orders of magnitude). Dropping them costs at most
+// r * kEigFloor of the content's energy.
+constexpr float kEigFloor = 1e-6f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
@@ -723,6 +732,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     return;
   }
 
+  // eigenvalue floor: eigenvalues below the core's resolution give zero columns. They are the
+  // trailing ones (lane c32 holds the c32-th largest), so the live ones are the first rl.
+  const float lmax = uni(wmax(c32 < rr ? lam : 0.f));
+  const bool live = c32 < rr && lam > lmax * kEigFloor;
+  const int rl = __builtin_popcountll(__ballot(live && h == 0));
+
   // ---- eigenvectors of the tridiagonal: twisted factorisation per eigenvalue ------------------
   // Both lanes of a pair compute vector c32; lane half h keeps entries 2 s + h in Y[s]. One
   // register array serves both sweeps: slot i holds e_i / D-_{i+1} (bottom-up pivots) for
@@ -794,7 +809,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     const bool ok = nn > 0.f && nn < FLT_MAX;
     const float inv = ok ? 1.f / sqrtf(nn) : 0.f;
 #pragma unroll
-    for (int s = 0; s < N / 2; ++s) Y[s] = ok ? Y[s] * inv : ((2 * s + h) == kb ? 1.f : 0.f);
+    for (int s = 0; s < N / 2; ++s) Y[s] = !live ? 0.f : (ok ? Y[s] * inv : ((2 * s + h) == kb ? 1.f : 0.f));
   }
 
   // ---- modified Gram-Schmidt across the rr vectors, two at a time (norms applied at the end) ---
@@ -803,8 +818,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   // 1 / sqrt(a); a later z with h1 = z . y_c, h2 = z . y_c+1 loses a2 = (h2 - mu h1) / nu^2
   // times y_c+1 and h1 / a - mu a2 times y_c.
   float ys = 1.f;
-  for (int c = 0; c < rr; c += 2) {
-    const bool pair = c + 1 < rr;  // uniform
+  // A vector that keeps less than kDep of its squared norm (1 after the twisted factorisation)
+  // once the earlier ones are taken out is a copy of them (two shifts inside one unresolved
+  // cluster give nearly the same vector): it is dropped, as dividing by its tiny residual would
+  // blow rounding noise up into every direction.
+  constexpr float kDep = 1e-4f;
+  for (int c = 0; c < rl; c += 2) {
+    const bool pair = c + 1 < rl;  // uniform
     float n4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < N / 2; ++s) n4[s & 3] += Y[s] * Y[s];
@@ -838,10 +858,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     const float a = bcast(nn, c);
     const float d = pair ? bcast(nn, c + 1) : 0.f;
     const float b = pair ? bcast(h1, c + 1) : 0.f;
-    const float ia = a > 0.f ? 1.f / a : 0.f;
+    const float ia = a > kDep ? 1.f / a : 0.f;
     const float mu = b * ia;
     const float nu2 = d - mu * b;
-    const float inu2 = pair && nu2 > 0.f ? 1.f / nu2 : 0.f;
+    const float inu2 = pair && nu2 > kDep ? 1.f / nu2 : 0.f;
     float f1 = 0.f, f2 = 0.f;
     if (c32 > c + 1 || (!pair && c32 > c)) {
       f2 = pair ? (h2 - mu * h1) * inu2 : 0.f;
@@ -851,12 +871,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     }
 #pragma unroll
     for (int s = 0; s < N / 2; ++s) Y[s] = fmaf(-f2, yb[s], fmaf(-f1, ya[s], Y[s]));
-    if (c32 == c) ys = a > 0.f ? 1.f / sqrtf(a) : 0.f;
-    if (pair && c32 == c + 1) ys = nu2 > 0.f ? 1.f / sqrtf(nu2) : 0.f;
+    if (c32 == c) ys = a > kDep ? 1.f / sqrtf(a) : 0.f;
+    if (pair && c32 == c + 1) ys = nu2 > kDep ? 1.f / sqrtf(nu2) : 0.f;
     wave_lds_sync();
   }
 #pragma unroll
-  for (int s = 0; s < N / 2; ++s) Y[s] = c32 < rr ? Y[s] * ys : 0.f;
+  for (int s = 0; s < N / 2; ++s) Y[s] = c32 < rl ? Y[s] * ys : 0.f;
 
   // ---- back-transformation Y <- H_0 H_1 ... H_{N-3} Y, two reflectors at a time --------------
   // H_{j-1} H_j Y = Y - t_j v_j g1 - t_{j-1} v_{j-1} (g0 - t_j kappa g1) with g1 = v_j^T Y,
@@ -901,9 +921,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     }
   }
 
-  // eigenvalue floor: tiny or negative eigenvalues give zero columns
-  const float lmax = uni(wmax(c32 < rr ? lam : 0.f));
-  const bool live = c32 < rr && lam > lmax * 1e-14f;
   const float q4 = live ? sqrtf(sqrtf(lam * bs)) : 1.f;   // of the unscaled eigenvalue
   const float qv = live ? 1.f / q4 : 0.f;          // lambda^(-1/4)
   const float ql = live ? 1.f / (q4 * q4) : 0.f;   // lambda^(-1/2)

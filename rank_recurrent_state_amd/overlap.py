@@ -11,39 +11,54 @@ Layer l decodes every step; it compresses when it holds r + T columns, except on
 start, where it compresses after T - (l mod T) steps instead, which shifts its window by l mod
 T steps. Every later window is a full one.
 
-The streams are HIP streams with CU masks (hipExtStreamCreateWithCUMask) of whole 32-CU blocks:
-masks that split an XCD were refused by the runtime on MI355X. Kernels run unchanged; only the
-launch order and the streams differ from a serial schedule of the same launches.
+The streams are HIP streams with CU masks of whole 32-CU blocks (masks that split an XCD were
+refused by the runtime on MI355X), made and destroyed by libseed itself, so that they belong to
+the runtime that launches the kernels. Kernels run unchanged; only the launch order and the
+streams differ from a serial schedule of the same launches.
+
+Profiled runs. The first profiled run of this schedule (rocprofv3 kernel trace) ended with a
+segmentation fault of the profiled process, and its cause has not been shown: under the
+profiler the process maps a second HSA runtime (the profiler's, beside the one bundled with
+torch), and the CU-masked queues are the one thing this schedule adds. Until a cause is shown,
+partition_streams refuses to run under the profiler.
 """
 from __future__ import annotations
 
-import ctypes
+import os
 
 from . import _lib
 
 
+def under_profiler() -> bool:
+    """Whether rocprofv3's tool library is loaded into this process (its preload or tool list)."""
+    env = os.environ.get("LD_PRELOAD", "") + ":" + os.environ.get("ROCP_TOOL_LIBRARIES", "")
+    return "rocprofiler-sdk" in env
+
+
 def partition_streams(split: int = 4):
-    """Two torch streams on disjoint XCDs: the first `split` 32-CU blocks and the rest. None
-    when the runtime does not provide CU-masked streams or the device is not 256 CUs."""
+    """Two CU-masked streams on disjoint XCDs: the first `split` 32-CU blocks and the rest, as
+    _lib.CUMaskedStream objects (the caller closes them). None when the device is not 256 CUs or
+    the runtime refuses the masks. Raises RuntimeError under the profiler (see above)."""
     import torch
+    if under_profiler():
+        raise RuntimeError("the CU-partitioned schedule is not run under rocprofv3 (a profiled run "
+                           "of it crashed, cause not shown)")
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     if ncu != 256 or not 0 < split < 8:
-        return None
-    try:
-        hip = ctypes.CDLL("libamdhip64.so")
-    except OSError:
         return None
     words = (ncu + 31) // 32
     out = []
     for pick in (lambda i: i // 32 < split, lambda i: i // 32 >= split):
-        mask = (ctypes.c_uint32 * words)()
+        mask = [0] * words
         for i in range(ncu):
             if pick(i):
                 mask[i // 32] |= 1 << (i % 32)
-        h = ctypes.c_void_p()
-        if hip.hipExtStreamCreateWithCUMask(ctypes.byref(h), ctypes.c_uint32(words), mask) != 0:
+        try:
+            out.append(_lib.CUMaskedStream(mask))
+        except _lib.SeedError:
+            for st in out:
+                st.close()
             return None
-        out.append(torch.cuda.ExternalStream(h.value))
     return out
 
 
@@ -55,7 +70,9 @@ class OverlappedStack:
     def __init__(self, shapes, states, decode_stream, compress_stream):
         import torch
         self.shapes, self.states = list(shapes), list(states)
-        self.sA, self.sB = decode_stream, compress_stream
+        # CU-masked streams from partition_streams are used through their torch view
+        self.sA = getattr(decode_stream, "torch", decode_stream)
+        self.sB = getattr(compress_stream, "torch", compress_stream)
         r, T = self.shapes[0].rank, self.shapes[0].period
         self.r, self.T = r, T
         L = len(self.shapes)

@@ -111,19 +111,26 @@ def near_tie_threshold(code) -> float:
 def compare_compression(C_before, a, vbar, U_gpu, V_gpu, r, code, a_ref=None):
     """Compare a GPU compression with the oracle's exact truncation of the same content.
 
-    Returns (kind, err): kind "product" uses rel-Frobenius on S~; kind "optimal" (near ties)
-    checks the Eckart-Young optimality criterion and returns the excess ratio.
+    Returns (kind, err, raw, sink). kind "product" holds the reconstructed state S~ to the
+    oracle's by rel-Frobenius; kind "optimal" (near ties, where several truncations are correct)
+    checks the Eckart-Young optimality criterion instead (0 or inf). In both branches the sink is
+    compared as well: a compression never recomputes the split (Lemma 1), so the GPU's sink must
+    equal a_ref, the true sink before the call (for the prefill-end compression, the oracle's
+    S vbar / |vbar|^2); sink = |a - a_ref| / |a_ref|, and err is the larger of the two.
+    raw is the product error against the oracle's truncation whichever branch is taken.
     """
     Ur, Vr, _ = orc.compress(*C_before, r) if isinstance(C_before, tuple) else orc.truncate(C_before, r)
     C = C_before[0] @ C_before[1].T if isinstance(C_before, tuple) else C_before
-    a_ref = a if a_ref is None else a_ref
+    if a_ref is None:
+        raise ValueError("compare_compression needs the reference sink a_ref")
     S_ref = orc.reconstruct(a_ref, vbar, Ur, Vr)
     S_gpu = orc.reconstruct(a, vbar, U_gpu, V_gpu)
+    sink = relF(a, a_ref)
     gap = orc.relative_gap(C, r)
     if gap < near_tie_threshold(code):
         ok = orc.truncation_is_optimal(C, U_gpu @ V_gpu.T, r, tolerance(code), abs_tol=tolerance(code) ** 2)
-        return "optimal", (0.0 if ok else float("inf")), relF(S_gpu, S_ref)
-    return "product", relF(S_gpu, S_ref), relF(S_gpu, S_ref)
+        return "optimal", max(0.0 if ok else float("inf"), sink), relF(S_gpu, S_ref), sink
+    return "product", max(relF(S_gpu, S_ref), sink), relF(S_gpu, S_ref), sink
 
 
 def check_decode_call(rrs, sh, st, m, dx, vbar_dev, vbar_np, heads, units, o):
@@ -148,37 +155,43 @@ def check_decode_call(rrs, sh, st, m, dx, vbar_dev, vbar_np, heads, units, o):
 
 def check_compress_call(rrs, sh, st, m, vbar_np, heads, units, code):
     """One compression call on the GPU, compared with the oracle's exact truncation of the
-    same content on `units`. Returns (worst error per compare_compression, near-tie count)."""
+    same content on `units`. Returns (worst error per compare_compression, near-tie count);
+    check_compress_call.last_raw / .last_sink hold the worst product and sink errors."""
     pre = host_state(sh, st, units, m)
     rrs.seed_compress(sh, st, m)
     post = host_state(sh, st, units, sh.rank)
-    worst, ties, raw = 0.0, 0, 0.0
+    worst, ties, raw, sink = 0.0, 0, 0.0, 0.0
     for i, u in enumerate(units):
         vb = vbar_np[u % heads]
-        kind, err, rw = compare_compression((pre[i][1], pre[i][2]), post[i][0], vb, post[i][1],
-                                            post[i][2], sh.rank, code, a_ref=pre[i][0])
+        kind, err, rw, sk = compare_compression((pre[i][1], pre[i][2]), post[i][0], vb, post[i][1],
+                                                post[i][2], sh.rank, code, a_ref=pre[i][0])
         worst = max(worst, err)
         raw = max(raw, rw)
+        sink = max(sink, sk)
         ties += kind == "optimal"
     check_compress_call.last_raw = raw
+    check_compress_call.last_sink = sink
     return worst, ties
 
 
 def check_from_dense_call(rrs, sh, S, vbar_dev, vbar_np, heads, units, code):
     """seed_state_from_dense on the GPU against the oracle's split + truncation of the same
-    dense states. Returns (state, worst error, near-tie count)."""
+    dense states. Returns (state, worst error, near-tie count); check_from_dense_call.last_sink
+    holds the worst sink error |a - S vbar / |vbar|^2| / |S vbar / |vbar|^2|."""
     import torch
     st = rrs.State.empty(sh)
     rrs.seed_state_from_dense(sh, S, vbar_dev, st)
     Sg = S.index_select(0, torch.as_tensor(list(units), device=S.device)).double().cpu().numpy()
     post = host_state(sh, st, units, sh.rank)
-    worst, ties = 0.0, 0
+    worst, ties, sink = 0.0, 0, 0.0
     for i, u in enumerate(units):
         vb = vbar_np[u % heads]
         a_o, _, _, _ = orc.from_dense(Sg[i], vb, sh.rank)
         _, C = orc.sink_split(Sg[i], vb)
-        kind, err, _ = compare_compression(C, post[i][0], vb, post[i][1], post[i][2], sh.rank, code,
-                                           a_ref=a_o)
+        kind, err, _, sk = compare_compression(C, post[i][0], vb, post[i][1], post[i][2], sh.rank, code,
+                                               a_ref=a_o)
         worst = max(worst, err)
+        sink = max(sink, sk)
         ties += kind == "optimal"
+    check_from_dense_call.last_sink = sink
     return st, worst, ties

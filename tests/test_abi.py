@@ -168,3 +168,25 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert e.value.status == rrs.SEED_ERR_ARG
     for code in (0, -1, -2, -3, -4, 5):
         assert isinstance(rrs.seed_status_string(code), str)
+
+
+def test_stream_helpers_reject_bad_arguments_on_the_host():
+    # validation happens before any HIP call: no GPU is needed for these
+    rrs = _lib()
+    lib = rrs.LIB
+    h = ctypes.c_void_p()
+    one = (ctypes.c_uint32 * 1)(1)
+    zero = (ctypes.c_uint32 * 1)(0)
+    assert lib.seed_stream_create_cu_masked(1, None, ctypes.byref(h)) == rrs.SEED_ERR_ARG
+    assert lib.seed_stream_create_cu_masked(0, one, ctypes.byref(h)) == rrs.SEED_ERR_ARG
+    assert lib.seed_stream_create_cu_masked(65, one, ctypes.byref(h)) == rrs.SEED_ERR_ARG
+    assert lib.seed_stream_create_cu_masked(1, zero, ctypes.byref(h)) == rrs.SEED_ERR_ARG
+    assert lib.seed_stream_create_cu_masked(1, one, None) == rrs.SEED_ERR_ARG
+    assert lib.seed_stream_destroy(None) == rrs.SEED_ERR_ARG
+
+
+def test_one_hip_runtime_is_mapped():
+    # libseed binds to the HIP runtime the process already holds; the binding refuses to load
+    # beside a second copy
+    rrs = _lib()
+    assert len(rrs.hip_runtimes_mapped()) <= 1

@@ -20,9 +20,19 @@ def test_overlapped_matches_serial():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import rank_recurrent_state_amd as rrs
+    if rrs.under_profiler():
+        pytest.skip("the CU-partitioned schedule is not run under the profiler")
     streams = rrs.partition_streams(4)
     if streams is None:
         pytest.skip("CU-masked streams not available")
+    try:
+        _run(rrs, torch, streams)
+    finally:
+        for st in streams:
+            st.close()
+
+
+def _run(rrs, torch, streams):
     L, B, H, r, T = 9, 2, 2, 8, 8
     w = synth.Workload("ovl", synth.GDN, B, H, 128, 128, r, T, 2 * T, 8, synth.BF16, synth.BF16)
     shapes = [rrs.make_shape(w.kind, B, H, 128, 128, r, T, synth.BF16, synth.BF16) for _ in range(L)]

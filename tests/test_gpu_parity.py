@@ -81,9 +81,9 @@ def run_parity(w: synth.Workload, seed: int, steps: int, check_units=None, repor
         vb = vbar_np[heads_of[i]]
         a_o, U_o, V_o, _ = orc.from_dense(Sg[i], vb, w.rank)
         _, C = orc.sink_split(Sg[i], vb)
-        kind, err, raw = compare_compression(C, post[i][0], vb, post[i][1], post[i][2], w.rank,
-                                             w.factor_dtype, a_ref=a_o)
-        rep["from_dense"].append((kind, err, raw))
+        kind, err, raw, sink = compare_compression(C, post[i][0], vb, post[i][1], post[i][2], w.rank,
+                                                   w.factor_dtype, a_ref=a_o)
+        rep["from_dense"].append((kind, err, raw, sink))
         rep["ties"] += kind == "optimal"
         assert err <= tol, f"from_dense unit {u}: {kind} {err}"
         free.append([a_o, U_o, V_o])
@@ -121,10 +121,10 @@ def run_parity(w: synth.Workload, seed: int, steps: int, check_units=None, repor
             post = host_state(sh, st, check, w.rank)
             for i, u in enumerate(check):
                 vb = vbar_np[heads_of[i]]
-                kind, err, raw = compare_compression((pre[i][1], pre[i][2]), post[i][0], vb,
-                                                     post[i][1], post[i][2], w.rank, w.factor_dtype,
-                                                     a_ref=pre[i][0])
-                rep["compress"].append((kind, err, raw))
+                kind, err, raw, sink = compare_compression((pre[i][1], pre[i][2]), post[i][0], vb,
+                                                           post[i][1], post[i][2], w.rank, w.factor_dtype,
+                                                           a_ref=pre[i][0])
+                rep["compress"].append((kind, err, raw, sink))
                 rep["ties"] += kind == "optimal"
                 assert err <= tol, f"compress after step {t} unit {u}: {kind} {err}"
                 if free_running:
@@ -140,8 +140,9 @@ def run_parity(w: synth.Workload, seed: int, steps: int, check_units=None, repor
 def _summary(name, rep):
     fd = max((e[2] for e in rep["from_dense"]), default=0.0)
     cp = max((e[2] for e in rep["compress"]), default=0.0)
+    sk = max((e[3] for e in rep["from_dense"] + rep["compress"]), default=0.0)
     print(f"\n[{name}] dense {rep['dense']:.2e} from_dense {fd:.2e} step S {rep['step_S']:.2e} "
-          f"o {rep['step_o']:.2e} compress {cp:.2e} free S {rep['free_S']:.2e} "
+          f"o {rep['step_o']:.2e} compress {cp:.2e} sink {sk:.2e} free S {rep['free_S']:.2e} "
           f"o {rep['free_o']:.2e} near-ties {rep['ties']}", flush=True)
 
 

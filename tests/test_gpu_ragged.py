@@ -106,9 +106,9 @@ def _compress_checked(rrs, torch, w, sh, hc, st, min_m):
         post = host_state(sh, st, full, sh.rank)
         for i, u in enumerate(full):
             vb = hc.vbar[u % w.heads]
-            kind, err, _ = compare_compression((pre[i][1], pre[i][2]), post[i][0], vb, post[i][1],
-                                               post[i][2], sh.rank, w.factor_dtype, a_ref=pre[i][0])
-            assert err <= tol, f"unit {u} compressed at m {m0[u]}: {kind} {err}"
+            kind, err, _, sink = compare_compression((pre[i][1], pre[i][2]), post[i][0], vb, post[i][1],
+                                                     post[i][2], sh.rank, w.factor_dtype, a_ref=pre[i][0])
+            assert err <= tol, f"unit {u} compressed at m {m0[u]}: {kind} {err} (sink {sink})"
     if rest:
         for a_, b_ in zip(keep, _snapshot(st, rest)):
             assert torch.equal(a_, b_)

@@ -98,3 +98,43 @@ def test_state_bytes_convention_is_discriminating(golden_dir):
     assert round(orc.state_bytes(n, dk, dv, R) / 1e6, 1) == at_r
     assert round(orc.state_bytes(n, dk, dv, R, bytes_per=2) / 1e6, 1) != at_r
     assert round((orc.state_bytes(n, dk, dv, R) + 4 * n * dv) / 1e6, 1) != at_r
+
+
+def test_corollary4_bound_worked_value():
+    # eps_bar / (1 - g_bar^W) at eps_bar = 1, g_bar = 1/2, W = 2 is 1 / (1 - 1/4) = 4/3, worked by
+    # hand; the looser forms eps_bar / (1 - g_bar) = 2 and eps_bar / (1 - g_bar)^W = 4 differ
+    assert orc.corollary4_bound(1.0, 0.5, 2) == pytest.approx(4.0 / 3.0, rel=1e-15)
+    assert orc.corollary4_bound(0.1, 0.9, 8) == pytest.approx(0.1 / (1.0 - 0.43046721), rel=1e-12)
+    assert orc.corollary4_bound(3.0, 0.0, 5) == pytest.approx(3.0, rel=1e-15)
+
+
+def test_corollary4_bound_is_attained_by_coherent_errors():
+    """A trajectory on which the bound is tight: every compression drops an error of the same
+    size along the same direction, and the exact state keeps accumulating it.
+
+    Mamba-2 head, d_k = 2, d_v = 3, vbar = e3 (so the content lives on e1, e2 and the sink stays
+    0), constant decay g, rank r = 1, compression every W = 2 steps. Each window writes e1 e1^T
+    (the large direction, always kept) and then b e2 e2^T (always dropped). After window k the
+    exact state's e2 e2^T coefficient is b (1 + g^2 + ... + g^(2(k-1))), the compressed state's 0,
+    and every compression error is b. So the distance after window k is
+    b (1 - g^(2k)) / (1 - g^2), which tends to eps_bar / (1 - g_bar^W) = b / (1 - g^2): the
+    geometric series of the decayed errors, summed here step by step by the oracle's own driver.
+    """
+    g, b, W, K = 0.5, 0.1, 2, 24
+    e1, e2, e3 = np.eye(3)
+    xs = []
+    for _ in range(K):
+        xs.append({"q": e1[:2], "k": e1[:2], "v": e1, "beta": 1.0, "g": g})
+        xs.append({"q": e1[:2], "k": e2[:2], "v": b * e2, "beta": 1.0, "g": g})
+    res = orc.run_compressed(orc.MAMBA2, np.zeros((2, 3)), e3, xs, r=1, T=W)
+    errs = res["errs"]
+    assert errs[0] == 0.0 and np.allclose(errs[1:], b, rtol=1e-12)
+    bound = orc.corollary4_bound(max(errs), max(res["g_bound"]), W)
+    dist = [np.linalg.norm(Sc - S) for Sc, S in zip(res["S_c"], res["S"])]
+    for k in range(1, K + 1):
+        expect = b * (1 - g ** (2 * k)) / (1 - g * g)
+        assert dist[2 * k - 1] == pytest.approx(expect, rel=1e-12)
+    assert max(dist) <= bound * (1 + 1e-12)
+    assert max(dist) >= bound * (1 - 1e-12)          # tight: the sup is the bound itself
+    # a bound with g_bar in place of g_bar^W would be loose by a factor 1 + g here
+    assert max(dist) / orc.corollary4_bound(max(errs), max(res["g_bound"]), 1) == pytest.approx(1 / (1 + g))
