@@ -477,6 +477,12 @@ def main():
                 f"launches)")
         del st_c
 
+    # ---- the head-normalisation epilogue (seed_decode_step_normed): T - 1 steps of layer 0's
+    # 4096 units from copies of its state, with and without the epilogue -------------------------
+    head_norm = None
+    if diag:
+        head_norm = head_norm_cost(rrs, torch, w, sh_l[0], states[0], pool, vbars[0], o[0], T, P, ev, log)
+
     # ---- the overlapped schedule (reported beside the lockstep step) ---------------------------
     overlapped = None if (args.no_overlap or not diag) else run_overlapped(rrs, torch, w, sh_l, states, pool, vbars, o, L, T,
                                                             P, ev, log, split=args.overlap_split)
@@ -575,8 +581,45 @@ def main():
         "overlapped_schedule": overlapped,
         "spectrum_diagnostic": spectrum,
         "chunked_update": chunk,
+        "head_norm_epilogue": head_norm,
     }
     print(json.dumps(res), flush=True)
+
+
+def head_norm_cost(rrs, torch, w, sh, state, pool, vbar, o, T, P, ev, log):
+    """Per-launch time of T - 1 decode steps of one layer with the head normalisation fused in
+    (gated after the norm), against the same steps without it, each on its own copy of the
+    layer's state. Returns the two averages, or None when the state is not at r columns."""
+    m0 = int(rrs.column_counts(sh, state)[0])
+    if m0 != w.rank:
+        return None
+    weight = torch.rand((w.heads, w.d_v), device=o.device) + 0.5
+    gate = torch.randn((sh.units, w.d_v), device=o.device).to(o.dtype)
+    res = {}
+    for name in ("plain", "normed"):
+        st = rrs.State(*[t.clone() for t in state.tensors()])
+        for rep in range(2):   # the second pass is timed (the first warms the instruction caches)
+            for t_, x_ in zip(st.tensors(), state.tensors()):
+                t_.copy_(x_)
+            a_, b_ = ev(), ev()
+            torch.cuda.synchronize()
+            a_.record()
+            for j in range(T - 1):
+                x = pool[j % P][0]
+                if name == "plain":
+                    rrs.seed_decode_step(sh, st, w.rank + j, x["q"], x["k"], x["v"], x["beta"], x["g"], vbar, o)
+                else:
+                    rrs.seed_decode_step_normed(sh, st, w.rank + j, x["q"], x["k"], x["v"], x["beta"], x["g"], vbar,
+                                                o, weight, gate=gate, eps=1e-6)
+            b_.record()
+            torch.cuda.synchronize()
+        res[name] = a_.elapsed_time(b_) * 1e3 / (T - 1)
+        del st
+    out = {"us_per_launch": res["normed"], "plain_us_per_launch": res["plain"],
+           "overhead": res["normed"] / res["plain"] - 1.0, "steps": T - 1, "gated": True}
+    log(f"[bench] head-norm epilogue: {res['normed']:.2f} us per launch against {res['plain']:.2f} us without "
+        f"({100 * out['overhead']:+.1f} %)")
+    return out
 
 
 def energy_diagnostic(rrs, torch, w, sh, sh_l, states, vbars, U1, L, N, m_now, dev, ev, log):

@@ -183,6 +183,41 @@ int seed_decode_step(const seed_shape *shape, const seed_state *state, int32_t m
                      const float *g, const float *vbar, void *o, void *stream);
 
 /*
+ * Head normalisation of the read-out, applied by the decode step before o is written. The sink
+ * part of the read-out, vbar (a^T q), is a bias along the head's fixed direction inside the
+ * norm, and its energy sets part of the gain 1 / rms the content receives (picx.dev summary,
+ * "Theoretical and Practical Implications", practical implications: the state sink acts as a
+ * bias and gain through the head's normalization). With x = o, or o * silu(gate) when
+ * gate_first:
+ *     o <- weight[h] * x / sqrt(mean over d_v of x^2 + eps)      (then * silu(gate) when a gate
+ *                                                                   is given and !gate_first)
+ * silu(z) = z / (1 + exp(-z)).
+ *   weight      float [heads][d_v] (required).
+ *   gate        [units][d_v] in io_dtype, or NULL for no gate.
+ *   eps         >= 0 and finite.
+ *   gate_first  0: gate after the norm (Gated DeltaNet / KDA output norm); 1: before it (the gated
+ *               norm of Mamba-2).
+ */
+typedef struct seed_head_norm {
+  const float *weight;
+  const void *gate;
+  float eps;
+  int32_t gate_first;
+} seed_head_norm;
+
+/*
+ * seed_decode_step with the head normalisation above fused into its epilogue: o receives the
+ * normalised read-out (the raw read-out is not stored). The state update is that of
+ * seed_decode_step. SEED_ERR_ARG for a NULL norm or weight, eps negative or not finite, or
+ * gate_first other than 0 or 1. It adds one wave reduction and the weight and gate loads per
+ * unit; the factors are read once, as without it.
+ */
+int seed_decode_step_normed(const seed_shape *shape, const seed_state *state, int32_t m,
+                            const void *q, const void *k, const void *v, const float *beta,
+                            const float *g, const float *vbar, const seed_head_norm *norm, void *o,
+                            void *stream);
+
+/*
  * The decode step for a ragged batch: every unit takes its own column count m from its state
  * (see the scale buffer above), as requests that joined at different times hold different
  * counts. A unit runs the step of seed_decode_step with that m, and its count goes one up, when
@@ -197,6 +232,12 @@ int seed_decode_step_ragged(const seed_shape *shape, const seed_state *state,
                             const uint8_t *active, const void *q, const void *k, const void *v,
                             const float *beta, const float *g, const float *vbar, void *o,
                             void *stream);
+
+/* seed_decode_step_ragged with the head normalisation of seed_decode_step_normed. */
+int seed_decode_step_ragged_normed(const seed_shape *shape, const seed_state *state,
+                                   const uint8_t *active, const void *q, const void *k, const void *v,
+                                   const float *beta, const float *g, const float *vbar,
+                                   const seed_head_norm *norm, void *o, void *stream);
 
 /* Floats per unit written by seed_state_spectrum. */
 #define SEED_SPECTRUM_LEN 33

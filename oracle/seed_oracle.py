@@ -47,7 +47,7 @@ __all__ = [
     "factored_step", "factored_chunk", "compress", "from_dense", "reconstruct", "decay_bound",
     "corollary4_bound", "run_dense", "run_factored", "run_compressed", "singular_values",
     "relative_gap", "truncation_is_optimal", "state_bytes", "dense_state_bytes", "state_energy",
-    "content_spectrum",
+    "content_spectrum", "silu", "head_norm",
 ]
 
 
@@ -344,3 +344,32 @@ def content_spectrum(U, V, k: int = 32):
     n = min(k, s.size)
     out[:n] = s[:n] ** 2
     return out, float(np.sum(C * C))
+
+
+def silu(z):
+    """z * sigmoid(z), the gate of a gated head normalisation."""
+    z = _f64(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def head_norm(o, weight, eps: float, gate=None, gate_first: bool = False):
+    """Per-head RMS normalisation of a read-out, with a weight and an optional gate.
+
+    picx.dev summary, "Theoretical and Practical Implications", practical implications: the
+    state sink acts as a bias and gain through the head's normalization. The pages do not print
+    the normalisation; this is the plain RMS form of the models named there (Gated DeltaNet,
+    Kimi Delta Attention and Mamba-2 heads normalise their d_v read-out by its root mean square
+    and a learned per-channel weight, optionally gated):
+        x = o, or o * silu(gate) when the gate comes first (Mamba-2's gated norm);
+        y = x / sqrt(mean(x^2) + eps) * weight, then * silu(gate) when the gate comes after.
+    With o = vbar (a^T q) + V (U^T q), the sink term is a fixed-direction bias inside the norm,
+    and its energy sets the gain 1 / rms that the content receives.
+    """
+    x = _f64(o)
+    if gate is not None and gate_first:
+        x = x * silu(gate)
+    rms = np.sqrt(np.mean(x * x) + float(eps))
+    y = x / rms * _f64(weight)
+    if gate is not None and not gate_first:
+        y = y * silu(gate)
+    return y

@@ -20,7 +20,8 @@ _NAMES = {
     "seed_decode_step_ragged", "seed_dense_decode_step", "seed_from_dense_iterations",
     "seed_state_energy", "seed_decode_chunk", "seed_chunk_max_tokens", "seed_state_spectrum",
     "seed_decode_chunk_ragged", "seed_compress_units",
-    "SEED_SPECTRUM_LEN", "CUMaskedStream", "hip_runtimes_mapped",
+    "SEED_SPECTRUM_LEN", "CUMaskedStream", "hip_runtimes_mapped", "seed_head_norm",
+    "seed_decode_step_normed", "seed_decode_step_ragged_normed",
     "seed_scale_len", "seed_shape", "seed_state", "seed_state_bytes", "seed_state_from_dense",
     "seed_status_string", "seed_version", "seed_workspace_bytes",
 }

@@ -24,7 +24,8 @@ EXPORTS = [
     "seed_from_dense_iterations", "seed_decode_step", "seed_decode_step_ragged", "seed_compress",
     "seed_compress_ragged", "seed_state_energy", "seed_dense_decode_step", "seed_decode_chunk",
     "seed_chunk_max_tokens", "seed_decode_chunk_ragged", "seed_state_spectrum", "seed_compress_units",
-    "seed_stream_create_cu_masked", "seed_stream_destroy", "seed_status_string", "seed_version",
+    "seed_stream_create_cu_masked", "seed_stream_destroy", "seed_decode_step_normed",
+    "seed_decode_step_ragged_normed", "seed_status_string", "seed_version",
 ]
 
 SEED_SPECTRUM_LEN = 33
@@ -44,6 +45,11 @@ class seed_shape(ctypes.Structure):
     @property
     def slots(self) -> int:
         return self.rank + self.period
+
+
+class seed_head_norm(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("gate_first", ctypes.c_int32)]
 
 
 class seed_state(ctypes.Structure):
@@ -104,6 +110,10 @@ def _load():
         "seed_state_spectrum": (ctypes.c_int, [Sp, Stp, P, P]),
         "seed_stream_create_cu_masked": (ctypes.c_int, [ctypes.c_uint32, P, ctypes.POINTER(ctypes.c_void_p)]),
         "seed_stream_destroy": (ctypes.c_int, [P]),
+        "seed_decode_step_normed": (ctypes.c_int, [Sp, Stp, ctypes.c_int32, P, P, P, P, P, P,
+                                                   ctypes.POINTER(seed_head_norm), P, P]),
+        "seed_decode_step_ragged_normed": (ctypes.c_int, [Sp, Stp, P, P, P, P, P, P, P,
+                                                          ctypes.POINTER(seed_head_norm), P, P]),
         "seed_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "seed_version": (ctypes.c_char_p, []),
     }
@@ -292,6 +302,44 @@ def seed_decode_step(shape: seed_shape, state, m: int, q, k, v, beta, g, vbar, o
     _check("seed_decode_step", LIB.seed_decode_step(
         ctypes.byref(shape), _state_c(state), m, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
         _ptr(vbar), _ptr(o), _stream_ptr(stream)))
+
+
+def _head_norm(shape, weight, gate, eps, gate_first):
+    _expect("norm weight", weight, shape.heads * shape.d_v, SEED_F32)
+    _expect("norm gate", gate, shape.units * shape.d_v, shape.io_dtype)
+    return seed_head_norm(None if weight is None else weight.data_ptr(),
+                          None if gate is None else gate.data_ptr(), float(eps), int(gate_first))
+
+
+def seed_decode_step_normed(shape: seed_shape, state, m: int, q, k, v, beta, g, vbar, o, weight,
+                            gate=None, eps: float = 1e-6, gate_first: bool = False, stream=None) -> None:
+    """seed_decode_step with the head normalisation fused into its epilogue: o receives
+    weight[h] * x / sqrt(mean(x^2) + eps) (times silu(gate) after, or x = o * silu(gate) first)."""
+    _expect_state(shape, state)
+    _expect_io(shape, q, k, v, beta, g, o)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    nrm = _head_norm(shape, weight, gate, eps, gate_first)
+    _check("seed_decode_step_normed", LIB.seed_decode_step_normed(
+        ctypes.byref(shape), _state_c(state), m, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+        _ptr(vbar), ctypes.byref(nrm), _ptr(o), _stream_ptr(stream)))
+
+
+def seed_decode_step_ragged_normed(shape: seed_shape, state, q, k, v, beta, g, vbar, o, weight,
+                                   gate=None, eps: float = 1e-6, gate_first: bool = False, active=None,
+                                   stream=None) -> None:
+    """seed_decode_step_ragged with the head normalisation of seed_decode_step_normed."""
+    import torch
+    _expect_state(shape, state)
+    _expect_io(shape, q, k, v, beta, g, o)
+    _expect("vbar", vbar, shape.heads * shape.d_v, SEED_F32)
+    if active is not None and hasattr(active, "is_cuda"):
+        _expect("active", active, shape.units)
+        if active.dtype != torch.uint8:
+            raise ValueError(f"active: expected dtype torch.uint8, got {active.dtype}")
+    nrm = _head_norm(shape, weight, gate, eps, gate_first)
+    _check("seed_decode_step_ragged_normed", LIB.seed_decode_step_ragged_normed(
+        ctypes.byref(shape), _state_c(state), _ptr(active), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+        _ptr(g), _ptr(vbar), ctypes.byref(nrm), _ptr(o), _stream_ptr(stream)))
 
 
 def seed_decode_step_ragged(shape: seed_shape, state, q, k, v, beta, g, vbar, o, active=None,

@@ -101,10 +101,14 @@ seed::StepArgs step_args(const seed_shape* sh, const seed_state* st, int32_t m, 
 
 int decode_call(const seed_shape* sh, const seed_state* st, int32_t m, const uint8_t* active, bool ragged,
                 const void* q, const void* k, const void* v, const float* beta, const float* g,
-                const float* vbar, void* o, void* stream) {
+                const float* vbar, void* o, void* stream, const seed_head_norm* norm = nullptr,
+                bool normed = false) {
   const int c = check_shape(sh);
   if (c != SEED_OK) return c;
   if (!state_ok(st) || !q || !k || !v || !beta || !g || !vbar || !o) return SEED_ERR_ARG;
+  if (normed && (!norm || !norm->weight || !(norm->eps >= 0.f) || !(norm->eps < 3.0e38f) ||
+                 (norm->gate_first != 0 && norm->gate_first != 1)))
+    return SEED_ERR_ARG;
   if (!ragged && (m < sh->rank || m >= sh->rank + sh->period)) return SEED_ERR_ARG;
   if (!seed::decode_supported(*sh)) return SEED_ERR_UNSUPPORTED;
   seed::StepArgs a = step_args(sh, st, m, active, ragged);
@@ -115,6 +119,12 @@ int decode_call(const seed_shape* sh, const seed_state* st, int32_t m, const uin
   a.g = g;
   a.vbar = vbar;
   a.o = o;
+  if (normed) {
+    a.norm_w = norm->weight;
+    a.norm_gate = norm->gate;
+    a.norm_eps = norm->eps;
+    a.norm_gate_first = norm->gate_first;
+  }
   return hip_status(seed::launch_decode(*sh, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -198,6 +208,19 @@ int seed_decode_step(const seed_shape* sh, const seed_state* st, int32_t m, cons
                      const void* k, const void* v, const float* beta, const float* g,
                      const float* vbar, void* o, void* stream) {
   return decode_call(sh, st, m, nullptr, false, q, k, v, beta, g, vbar, o, stream);
+}
+
+int seed_decode_step_normed(const seed_shape* sh, const seed_state* st, int32_t m, const void* q,
+                            const void* k, const void* v, const float* beta, const float* g,
+                            const float* vbar, const seed_head_norm* norm, void* o, void* stream) {
+  return decode_call(sh, st, m, nullptr, false, q, k, v, beta, g, vbar, o, stream, norm, true);
+}
+
+int seed_decode_step_ragged_normed(const seed_shape* sh, const seed_state* st, const uint8_t* active,
+                                   const void* q, const void* k, const void* v, const float* beta,
+                                   const float* g, const float* vbar, const seed_head_norm* norm, void* o,
+                                   void* stream) {
+  return decode_call(sh, st, 0, active, true, q, k, v, beta, g, vbar, o, stream, norm, true);
 }
 
 int seed_decode_step_ragged(const seed_shape* sh, const seed_state* st, const uint8_t* active,

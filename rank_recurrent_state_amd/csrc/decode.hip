@@ -20,7 +20,9 @@
 //   V pass: V x and V y accumulated per lane, then summed across column groups with
 //           transposed permlane swaps (every lane ends with a few elements of d_v).
 //   Epilogue: w = beta (eps - V x) (delta kinds) or beta eps (Mamba-2) becomes column m of V,
-//           the key becomes column m of U, and o = vbar (a+ . q) + V y + (kappa . q) w.
+//           the key becomes column m of U, and o = vbar (a+ . q) + V y + (kappa . q) w;
+//           optionally o is normalised in place (per-head RMS norm with weight and gate, one
+//           more wave sum: no further pass over the factors).
 // The sink is lazy as well. Lemma 2 adds a multiple of kappa to a at every step, and kappa is
 // the column the step appends to U, so the state keeps a_0 (the sink when the factors were last
 // compressed) and one coefficient c_j per window column: a = (decay of slot 0) a_0 + sum_j c_j
@@ -472,6 +474,12 @@ void k_decode(const StepArgs A) {
   float vv[NB], vb[NB];
   load_f32<IDT, NB>(reinterpret_cast<const IT*>(A.v) + unit * DV + ve, vv);
   load_f32<0, NB>(A.vbar + static_cast<int64_t>(head) * DV + ve, vb);
+  // the head normalisation's weight and gate (when fused in), here so that their latency hides
+  // behind the V pass
+  const bool normed = A.norm_w != nullptr, gated = normed && A.norm_gate != nullptr;
+  float nw[NB], gz[NB];
+  if (normed) load_f32<0, NB>(A.norm_w + static_cast<int64_t>(head) * DV + ve, nw);
+  if (gated) load_f32<IDT, NB>(reinterpret_cast<const IT*>(A.norm_gate) + unit * DV + ve, gz);
   if constexpr (SPLIT) {
     load_v();
     __builtin_amdgcn_sched_barrier(0);
@@ -540,6 +548,28 @@ void k_decode(const StepArgs A) {
   }
   store_factor<FDT, NB>(Vb + static_cast<int64_t>(m) * DV + ve, w, sr, A.rng_key, kSiteDecodeV, 0u, m, unit, window,
                         ve);
+  if (normed) {  // uniform: the head normalisation of the read-out
+    // The lanes hold distinct elements of o, so its mean square is one wave sum. The sink's
+    // share vbar (a+ . q) is inside the norm: a bias along vbar, and part of the gain 1 / rms.
+    if (gated) {
+#pragma unroll
+      for (int e = 0; e < NB; ++e) gz[e] = gz[e] / (1.f + __expf(-gz[e]));   // silu
+    }
+    const bool gfirst = gated && A.norm_gate_first != 0;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      if (gfirst) o[e] *= gz[e];
+      ss = fmaf(o[e], o[e], ss);
+    }
+    ss = wave_sum(ss);
+    const float rinv = __builtin_amdgcn_rsqf(ss * (1.f / DV) + A.norm_eps);
+#pragma unroll
+    for (int e = 0; e < NB; ++e) {
+      o[e] *= rinv * nw[e];
+      if (gated && !gfirst) o[e] *= gz[e];
+    }
+  }
   store_f32<IDT, NB>(reinterpret_cast<IT*>(A.o) + unit * DV + ve, o);
   if constexpr (DIAG && FDT != 0) {
     // KDA with stochastic rounding: the new U column kappa / Gamma, from the key read again and

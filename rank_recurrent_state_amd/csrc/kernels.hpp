@@ -35,6 +35,14 @@ struct StepArgs {
   const float* g;
   const float* vbar;
   void* o;
+  // head-normalisation epilogue of the read-out (decode step only): norm_w == nullptr leaves o
+  // as the read-out; otherwise o becomes norm_w[head] * x / sqrt(mean(x^2) + norm_eps), with x
+  // the read-out (times silu(norm_gate) first when norm_gate_first), times silu(norm_gate)
+  // after when a gate is given and !norm_gate_first
+  const float* norm_w;      // [heads][d_v]
+  const void* norm_gate;    // [units][d_v] in the io dtype, or nullptr
+  float norm_eps;
+  int32_t norm_gate_first;
 };
 
 struct DenseArgs {

@@ -190,3 +190,24 @@ def test_one_hip_runtime_is_mapped():
     # beside a second copy
     rrs = _lib()
     assert len(rrs.hip_runtimes_mapped()) <= 1
+
+
+def test_normed_step_rejects_bad_norm_on_the_host():
+    rrs = _lib()
+    f = _Fake()
+    st = _FakeState(rrs)
+    sh = rrs.make_shape(rrs.SEED_GDN, 4, 2, 128, 128, 16, 16, rrs.SEED_BF16)
+    lib = rrs.LIB
+    P = ctypes.c_void_p
+
+    def call(norm):
+        return lib.seed_decode_step_normed(ctypes.byref(sh), ctypes.byref(st.c), 16, P(8), P(8), P(8), P(8), P(8),
+                                           P(8), norm, P(8), None)
+
+    assert call(None) == rrs.SEED_ERR_ARG
+    assert call(ctypes.byref(rrs.seed_head_norm(None, None, 1e-6, 0))) == rrs.SEED_ERR_ARG
+    assert call(ctypes.byref(rrs.seed_head_norm(8, None, -1.0, 0))) == rrs.SEED_ERR_ARG
+    assert call(ctypes.byref(rrs.seed_head_norm(8, None, float("nan"), 0))) == rrs.SEED_ERR_ARG
+    assert call(ctypes.byref(rrs.seed_head_norm(8, None, float("inf"), 0))) == rrs.SEED_ERR_ARG
+    assert call(ctypes.byref(rrs.seed_head_norm(8, None, 1e-6, 2))) == rrs.SEED_ERR_ARG
+    _ = f
