@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--staggered", action="store_true",
                     help="requests at staggered column counts (request b at r + b mod T): ragged "
                          "decode steps, each followed by a compression of the units that filled")
+    ap.add_argument("--stagger-group", type=int, default=1024,
+                    help="with --staggered: full units per compression launch in the overlapped schedule")
     ap.add_argument("--pool", type=int, default=64, help="steps of resident inputs, cycled")
     ap.add_argument("--dense-steps", type=int, default=32, help="timed dense-baseline steps")
     ap.add_argument("--prefill", type=int, default=None, help="override the prefill length")
@@ -768,6 +770,10 @@ def run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vb
     step_ms = t_total / K * 1e3
     value = N * K / t_total
     log(f"[bench] staggered: {K} steps in {t_total * 1e3:.1f} ms ({step_ms:.3f} ms/step)")
+    overlapped = None
+    if L >= 8 and not args.no_overlap:
+        overlapped = run_staggered_overlapped(rrs, torch, w, sh_l, sh_all, states, state_all, pool, vbars, o, N, L,
+                                              T, P, K, args.overlap_split, args.stagger_group)
     res = {
         "metric": "factored decode head-steps/s (staggered requests, compression when full)",
         "value": value, "unit": "head-steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -777,8 +783,52 @@ def run_staggered(args, rrs, torch, w, sh_l, sh_all, states, state_all, pool, vb
                    "launch_units": U1, "layers": L, "prefill_tokens": prefill,
                    "rounding": args.rounding},
         "roofline": None, "cpu_baseline": None,
+        "overlapped_schedule": overlapped,
     }
     print(json.dumps(res), flush=True)
+
+
+def run_staggered_overlapped(rrs, torch, w, sh_l, sh_all, states, state_all, pool, vbars, o, N, L, T, P, K, split,
+                             group_units):
+    """The staggered steps with the compressions overlapped (rank_recurrent_state_amd.StaggeredStack):
+    ragged decode launches on `split` XCDs, each group of layers' filled units compressed on the
+    others as soon as the group has decoded. Eager launches, from the state the serial staggered
+    steps left. Returns ms per step, or None."""
+    if rrs.under_profiler():
+        log("[bench] overlapped staggered schedule: not run under the profiler, skipped")
+        return None
+    streams = rrs.partition_streams(split)
+    if streams is None:
+        log("[bench] overlapped staggered schedule: CU-masked streams not available, skipped")
+        return None
+    try:
+        stack = rrs.StaggeredStack(sh_all, state_all, sh_l, states, *streams, group_units=group_units)
+        cur = torch.cuda.current_stream()
+        stack.start()
+        for s_ in range(T):                  # warmup
+            stack.step(pool[s_ % P], vbars, o)
+        stack.finish()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        stack.start()
+        for s_ in range(K):
+            stack.step(pool[s_ % P], vbars, o)
+        stack.finish()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3
+        counts = rrs.column_counts(sh_all, state_all)
+        assert int(counts.min()) >= w.rank and int(counts.max()) <= w.rank + T - 1, "every full unit compressed"
+    finally:
+        for st in streams:
+            st.close()
+    res = {"ms_per_step": t / K * 1e3, "head_steps_per_s": N * K / t, "steps": K, "decode_xcds": split,
+           "compress_xcds": 8 - split, "layer_groups": len(stack.groups), "eager": True}
+    log(f"[bench] overlapped staggered schedule (decode on {split} XCDs, each group of {stack.groups[0][1]} layers' "
+        f"filled units compressed on the other {8 - split}): {res['ms_per_step']:.3f} ms per step, "
+        f"{res['head_steps_per_s'] / 1e6:.1f} M head-steps/s")
+    return res
 
 
 if __name__ == "__main__":

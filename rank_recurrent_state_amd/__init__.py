@@ -27,7 +27,7 @@ _NAMES = {
 }
 
 
-_OVERLAP = {"OverlappedStack", "partition_streams", "under_profiler"}
+_OVERLAP = {"OverlappedStack", "StaggeredStack", "partition_streams", "under_profiler"}
 
 
 def __getattr__(name):
