@@ -147,16 +147,18 @@ size_t seed_workspace_bytes(const seed_shape *shape, int32_t op);
  *          and zero columns where C has rank below r; scales reset to 1.
  *   ws     workspace of seed_workspace_bytes(shape, SEED_OP_FROM_DENSE) bytes (may be NULL
  *          when that is 0).
- * When min(d_k, d_v) <= 64 the truncation is exact up to fp32 rounding. For 128 x 128 states
- * the leading 64-dimensional right singular subspace is first found by block subspace
- * iteration on C^T C (fixed count, see seed_from_dense_iterations), then truncated exactly.
+ * When min(d_k, d_v) <= 64 the truncation is exact up to rounding (a factored core of the
+ * smaller side). For 128 x 128 states it is a one-sided Jacobi SVD of C in fp64: sweeps of plane
+ * rotations over all column pairs, stopping at the first sweep in which every pair is orthogonal
+ * to 1e-8 of the product of their lengths (at most seed_from_dense_iterations() sweeps).
  * Source: thelatestinai.com figures & tables, overview table (states leaving the prefill are
  * compressed to the sink plus rank-r factors); picx.dev summary, Lemma 1.
  */
 int seed_state_from_dense(const seed_shape *shape, const float *S, const float *vbar,
                           const seed_state *state, void *ws, size_t ws_bytes, void *stream);
 
-/* Subspace-iteration count used by seed_state_from_dense for 128 x 128 states. */
+/* The most one-sided Jacobi sweeps seed_state_from_dense runs on a 128 x 128 state (it stops at
+ * the first sweep that rotates no column pair). */
 int32_t seed_from_dense_iterations(void);
 
 /*

@@ -31,7 +31,6 @@
 // any output is written (the output overwrites the first r column slots in place).
 #include <float.h>
 
-#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -42,7 +41,8 @@ namespace seed {
 constexpr int MX = 64;       // maximum columns handled by the core (r + T <= 64)
 constexpr int LD = MX + 1;   // padded leading dimension of the m x m matrices
 constexpr int kMaxSweeps = 16;
-constexpr int kFromDenseIters = 6;    // subspace iterations for 128 x 128 dense states
+constexpr int kJacobiMaxSweeps = 30;  // one-sided Jacobi sweeps for 128 x 128 dense states, at most
+constexpr double kJacobiTol = 1e-8;   // a pair is rotated while |w_p . w_q| > kJacobiTol |w_p| |w_q|
 
 template <typename CT> struct Tol;
 template <> struct Tol<float> {
@@ -492,75 +492,21 @@ constexpr size_t compress_lds_bytes() {
 // content is put in factored form with m <= 64 columns, then the core truncates it exactly:
 //   DV <= 64:       U = C, V = I_DV          (m = DV, exact)
 //   DK <= 64 < DV:  U = I_DK, V = C^T        (m = DK, exact)
-//   DK = DV = 128:  U = C X, V = X with X = orth((C^T C)^q C^T Omega), Omega = [I_64; I_64]
-//                   (m = 64, q = kFromDenseIters block subspace iterations; fp32 core)
-// The exact cases read C back from the dense state for the reconstruction.
+// Both read C back from the dense state for the reconstruction. 128 x 128 states go to
+// k_from_dense_jacobi below.
 template <int DK, int DV, int FDT>
 struct FD {
   static constexpr bool UC = (DV <= 64);               // U = C, V = I
   static constexpr bool VC = (!UC && DK <= 64);        // U = I, V = C^T
-  static constexpr bool ITER = (!UC && !VC);
-  static constexpr int M = UC ? DV : (VC ? DK : 64);
-  using CT = typename std::conditional<ITER, float, core_t<FDT>>::type;
+  static_assert(UC || VC, "one side of at most 64");
+  static constexpr int M = UC ? DV : DK;
+  using CT = core_t<FDT>;
   static constexpr int LDC = DV + 1;                   // staged C rows
-  static constexpr int LDX = DV + 1;                   // X columns (ITER)
-  static constexpr int LDZ = DK + 1;                   // Z = C X columns (ITER)
   static constexpr size_t CORE = sizeof(Core<CT>);
   static constexpr size_t CST = sizeof(float) * DK * LDC;
   static constexpr size_t BIG = ((CORE > CST ? CORE : CST) + 15) / 16 * 16;
-  static constexpr size_t XB = ITER ? sizeof(float) * M * LDX : 0;
-  static constexpr size_t ZB = ITER ? sizeof(float) * M * LDZ : 0;
-  static constexpr size_t LDS = BIG + XB + ZB + sizeof(float) * (DK + DV + 4);
+  static constexpr size_t LDS = BIG + sizeof(float) * (DK + DV + 4);
 };
-
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  return v;
-}
-
-// Modified Gram-Schmidt, two passes, on M columns of length D at X + c * ld. Columns that
-// vanish (norm^2 <= 1e-30 of the largest) are set to zero. The 4 lanes of a quad share a
-// column, so the quad sums stay inside lanes that branch together.
-template <int D, int M>
-__device__ void mgs2(float* X, const int ld) {
-  const int t = threadIdx.x;
-  static_assert(M * 4 <= 256, "4 lanes per column");
-  const int c = t >> 2, part = t & 3;
-  float scale0 = 0.f;
-  {
-    float p = 0.f;
-    if (c < M) for (int j = part; j < D; j += 4) p += X[c * ld + j] * X[c * ld + j];
-    scale0 = quad_sum(p);
-  }
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int l = 0; l < M; ++l) {
-      if (c > l && c < M) {
-        float nl = 0.f, h = 0.f;
-        for (int j = part; j < D; j += 4) {
-          const float xl = X[l * ld + j];
-          nl += xl * xl;
-          h += X[c * ld + j] * xl;
-        }
-        nl = quad_sum(nl);
-        h = quad_sum(h);
-        if (nl > 0.f) {
-          const float f = h / nl;
-          for (int j = part; j < D; j += 4) X[c * ld + j] -= f * X[l * ld + j];
-        }
-      }
-      __syncthreads();
-    }
-  }
-  if (c < M) {
-    float p = 0.f;
-    for (int j = part; j < D; j += 4) p += X[c * ld + j] * X[c * ld + j];
-    p = quad_sum(p);
-    const float f = (p > 1e-30f * scale0 && p > 0.f) ? 1.f / sqrtf(p) : 0.f;
-    for (int j = part; j < D; j += 4) X[c * ld + j] *= f;
-  }
-  __syncthreads();
-}
 
 template <int DK, int DV, int FDT>
 __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
@@ -572,9 +518,7 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
   char* base = reinterpret_cast<char*>(lds4);
   Core<CT>& S = *reinterpret_cast<Core<CT>*>(base);
   float* Cst = reinterpret_cast<float*>(base);           // staged C rows (before the core)
-  float* X = reinterpret_cast<float*>(base + L::BIG);    // ITER: X columns
-  float* Z = reinterpret_cast<float*>(base + L::BIG + L::XB);  // ITER: Z = C X columns
-  float* sa = reinterpret_cast<float*>(base + L::BIG + L::XB + L::ZB);
+  float* sa = reinterpret_cast<float*>(base + L::BIG);
   float* svb = sa + DK;
   float* misc = svb + DV;
   static_assert(DK <= 256 && DV <= 256, "one thread per row");
@@ -617,34 +561,6 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
   }
   __syncthreads();
 
-  if constexpr (L::ITER) {
-    // X0 = C^T Omega, Omega = [I_64; I_64]; then q rounds of X <- orth(C^T (C X))
-    for (int idx = t; idx < M * DV; idx += 256) {
-      const int c = idx / DV, j = idx - c * DV;
-      X[c * L::LDX + j] = Cst[c * L::LDC + j] + Cst[(c + 64) * L::LDC + j];
-    }
-    __syncthreads();
-    mgs2<DV, M>(X, L::LDX);
-    for (int it = 0; it <= kFromDenseIters; ++it) {
-      for (int idx = t; idx < M * DK; idx += 256) {      // Z = C X
-        const int c = idx / DK, i = idx - c * DK;
-        float acc = 0.f;
-        for (int j = 0; j < DV; ++j) acc += Cst[i * L::LDC + j] * X[c * L::LDX + j];
-        Z[c * L::LDZ + i] = acc;
-      }
-      __syncthreads();
-      if (it == kFromDenseIters) break;                  // final Z = C X is the U factor
-      for (int idx = t; idx < M * DV; idx += 256) {      // X = C^T Z
-        const int c = idx / DV, j = idx - c * DV;
-        float acc = 0.f;
-        for (int i = 0; i < DK; ++i) acc += Cst[i * L::LDC + j] * Z[c * L::LDZ + i];
-        X[c * L::LDX + j] = acc;
-      }
-      __syncthreads();
-      mgs2<DV, M>(X, L::LDX);
-    }
-  }
-
   // Grams of the factored content, accumulated in registers, then written to the core
   // region once every thread is done with the staged C
   {
@@ -655,7 +571,7 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int f = 0; f < 4; ++f) au[e][f] = AccT(0);
-    // the non-identity Gram: U^T U (UC: C^T C over rows i; ITER: Z^T Z) or V^T V (VC: C C^T)
+    // the non-identity Gram: U^T U (UC: C^T C over rows i) or V^T V (VC: C C^T)
     if (4 * ta < M && 4 * tb < M) {
       if constexpr (L::UC) {
         for (int i = 0; i < DK; ++i) {
@@ -683,19 +599,6 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
 #pragma unroll
             for (int f = 0; f < 4; ++f) au[e][f] += x[e] * y[f];
         }
-      } else {
-        for (int i = 0; i < DK; ++i) {
-          AccT x[4], y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = (4 * ta + e < M) ? AccT(Z[(4 * ta + e) * L::LDZ + i]) : AccT(0);
-            y[e] = (4 * tb + e < M) ? AccT(Z[(4 * tb + e) * L::LDZ + i]) : AccT(0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int f = 0; f < 4; ++f) au[e][f] += x[e] * y[f];
-        }
       }
     }
     __syncthreads();  // the staged C is dead from here on: the core overwrites it
@@ -712,33 +615,6 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
             else { S.GA[a * LD + b] = g; S.GB[a * LD + b] = id; }
           }
         }
-    }
-    if constexpr (L::ITER) {
-      // G_V = X^T X (orthonormal up to rounding; computed rather than assumed)
-      __syncthreads();
-      if (4 * ta < M && 4 * tb < M) {
-        float av[4][4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int f = 0; f < 4; ++f) av[e][f] = 0.f;
-        for (int j = 0; j < DV; ++j) {
-          float x[4], y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[e] = X[(4 * ta + e) * L::LDX + j];
-            y[e] = X[(4 * tb + e) * L::LDX + j];
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int f = 0; f < 4; ++f) av[e][f] += x[e] * y[f];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int f = 0; f < 4; ++f) S.GB[(4 * ta + e) * LD + 4 * tb + f] = CT(av[e][f]);
-      }
     }
     if (t < MX) S.colsc[t] = CT(1);
     __syncthreads();
@@ -781,19 +657,182 @@ __global__ __launch_bounds__(256) void k_from_dense(const CompressArgs A) {
       for (int i = 0; i < DK; ++i) acc += CT(Sd[i * DV + j] - sa[i] * svb[j]) * S.GA[i * LD + c];
       Vb[static_cast<int64_t>(c) * DV + j] = round_store<FDT>(static_cast<float>(acc), RV, c, j);
     }
-  } else {
-    // U'[c][i] = sum_a Z[perm[a]][i] X_U[a][c]; V'[c][j] = sum_b X[b][j] X_V[b][c]
-    for (int c = t / DK; c < r; c += 256 / DK) {
-      const int i = t % DK;
-      CT acc = CT(0);
-      for (int a = 0; a < k; ++a) acc += CT(Z[S.perm[a] * L::LDZ + i]) * S.GB[a * LD + c];
-      Ub[static_cast<int64_t>(c) * DK + i] = round_store<FDT>(static_cast<float>(acc), RU, c, i);
+  }
+  // decay scales 1, sink coefficients 0, window count 0, m = r
+  float* __restrict__ sc = A.scale + unit * A.scale_len;
+  for (int i = t; i < A.scale_len; i += 256)
+    sc[i] = i < A.coef_off ? 1.f : (i == A.m_off ? __uint_as_float(static_cast<uint32_t>(r)) : 0.f);
+}
+
+
+// ---- prefill-end compression of 128 x 128 states: one-sided Jacobi SVD of the content ----------
+// The content C = S - a vbar^T (a as stored) is held in LDS in fp64 as its 128 columns w_j, one
+// per value channel. Sweeps of plane rotations over all column pairs orthogonalise them: with the
+// accumulated rotation J, C J = W, so C = sum_c w_c j_c^T with orthogonal w_c, and sigma_c =
+// |w_c| are the singular values. A sweep is 127 rounds of 64 disjoint pairs (the circle method:
+// position 127 stays, the others turn). A pair with a = |w_p|^2, b = |w_q|^2, g = w_p . w_q is
+// rotated while |g| > kJacobiTol sqrt(a b), by the angle that makes the two columns orthogonal;
+// columns below the noise floor (1e-28 of the content's energy) are left alone. The iteration stops
+// at the first sweep that rotates no pair, or after kJacobiMaxSweeps. The r longest columns give
+// U'_k = w_c / sqrt(sigma_c), and V'_k = j_c sqrt(sigma_c) = C^T w_c / sigma_c^(3/2) is formed from
+// the dense state itself, so J is never stored. There is no Gram (whose condition number is the
+// square of C's), no iteration count to guess, and the truncation is exact up to the stopping
+// tolerance and fp64 rounding.
+template <int FDT>
+struct FDJ {
+  static constexpr int D = 128;
+  static constexpr int LDW = D + 1;
+  static constexpr size_t LDS = sizeof(double) * (D * LDW + D + 8) + sizeof(float) * (2 * D + 4) +
+                                sizeof(int) * 64;
+};
+
+__device__ __forceinline__ double quad_sum_d(double v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  return v;
+}
+
+template <int FDT>
+__global__ __launch_bounds__(256) void k_from_dense_jacobi(const CompressArgs A) {
+  using FT = stor_t<FDT>;
+  constexpr int D = FDJ<FDT>::D;
+  constexpr int LDW = FDJ<FDT>::LDW;
+  extern __shared__ float4 lds4[];
+  double* W = reinterpret_cast<double*>(lds4);   // column c at W + c * LDW
+  double* sig = W + D * LDW;                      // [D] column lengths
+  double* red = sig + D;                          // [8] reduction scratch
+  float* sa = reinterpret_cast<float*>(red + 8);  // [D] the sink a
+  float* svb = sa + D;                            // [D] vbar
+  float* misc = svb + D;                          // [4]
+  int* sel = reinterpret_cast<int*>(misc + 4);    // [64] the kept columns, longest first
+
+  const int t = threadIdx.x;
+  const int64_t unit = blockIdx.x;
+  const int head = static_cast<int>(unit % A.heads);
+  const int r = A.rank, Cs = A.slots;
+  const float* __restrict__ Sd = A.S + unit * D * D;
+  FT* __restrict__ Ub = reinterpret_cast<FT*>(A.U) + unit * static_cast<int64_t>(Cs) * D;
+  FT* __restrict__ Vb = reinterpret_cast<FT*>(A.V) + unit * static_cast<int64_t>(Cs) * D;
+
+  // sink split: a = S vbar / |vbar|^2 (stored in fp32), C = S - a vbar^T
+  for (int j = t; j < D; j += 256) svb[j] = A.vbar[static_cast<int64_t>(head) * D + j];
+  __syncthreads();
+  if (t < kWave) {
+    float p = 0.f;
+    for (int j = t; j < D; j += kWave) p += svb[j] * svb[j];
+    p = group_sum<64>(p);
+    if (t == 0) misc[0] = p;
+  }
+  __syncthreads();
+  const float inv = misc[0] > 0.f ? 1.f / misc[0] : 0.f;
+  if (t < D) {
+    float p = 0.f;
+    for (int j = 0; j < D; ++j) p += Sd[t * D + j] * svb[j];
+    const float ai = p * inv;
+    sa[t] = ai;
+    A.a[unit * D + t] = ai;
+  }
+  __syncthreads();
+  double e = 0.0;
+  for (int idx = t; idx < D * D; idx += 256) {
+    const int i = idx / D, j = idx - i * D;
+    const double c = static_cast<double>(Sd[idx]) - static_cast<double>(sa[i]) * static_cast<double>(svb[j]);
+    W[j * LDW + i] = c;
+    e += c * c;
+  }
+  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off);
+  if ((t & (kWave - 1)) == 0) red[t >> 6] = e;
+  __syncthreads();
+  const double floor = 1e-28 * (red[0] + red[1] + red[2] + red[3]);
+
+  // sweeps; the 4 lanes of a pair hold rows part + 4 k of its two columns
+  const int pr = t >> 2, part = t & 3;
+  for (int sweep = 0; sweep < kJacobiMaxSweeps; ++sweep) {
+    int rot = 0;
+    for (int k = 0; k < D - 1; ++k) {
+      const int p = pr == 0 ? D - 1 : (k + pr) % (D - 1);
+      const int q = pr == 0 ? k : (k - pr + (D - 1)) % (D - 1);
+      double* wp = W + p * LDW + part;
+      double* wq = W + q * LDW + part;
+      double x[D / 4], y[D / 4];
+      double a = 0.0, b = 0.0, g = 0.0;
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) {
+        x[i] = wp[4 * i];
+        y[i] = wq[4 * i];
+        a = fma(x[i], x[i], a);
+        b = fma(y[i], y[i], b);
+        g = fma(x[i], y[i], g);
+      }
+      a = quad_sum_d(a);
+      b = quad_sum_d(b);
+      g = quad_sum_d(g);
+      // the four lanes of a pair hold the same sums, so they take the same branch
+      if (a > floor && b > floor && fabs(g) > kJacobiTol * sqrt(a) * sqrt(b)) {
+        const double zeta = (b - a) / (2.0 * g);
+        const double tn = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+        const double c = 1.0 / sqrt(1.0 + tn * tn), s = c * tn;
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) {
+          wp[4 * i] = c * x[i] - s * y[i];
+          wq[4 * i] = s * x[i] + c * y[i];
+        }
+        rot = 1;
+      }
+      __syncthreads();
     }
-    for (int c = t / DV; c < r; c += 256 / DV) {
-      const int j = t % DV;
-      CT acc = CT(0);
-      for (int b = 0; b < M; ++b) acc += CT(X[b * L::LDX + j]) * S.GA[b * LD + c];
-      Vb[static_cast<int64_t>(c) * DV + j] = round_store<FDT>(static_cast<float>(acc), RV, c, j);
+    if (!__syncthreads_or(rot)) break;
+  }
+
+  // singular values and the r longest columns
+  if (t < D) {
+    double n2 = 0.0;
+    for (int i = 0; i < D; ++i) n2 = fma(W[t * LDW + i], W[t * LDW + i], n2);
+    sig[t] = sqrt(n2);
+  }
+  __syncthreads();
+  if (t < D) {
+    const double st = sig[t];
+    int rank = 0;
+    for (int c = 0; c < D; ++c) rank += (sig[c] > st) || (sig[c] == st && c < t);
+    if (rank < r) sel[rank] = t;
+  }
+  __syncthreads();
+  const double smax = sig[sel[0]];
+  const double sfloor = 1e-13 * smax;
+  const Rounding RU{A.rounding != 0, A.rng_key, kSiteFromDenseU, unit, 0u};
+  const Rounding RV{A.rounding != 0, A.rng_key, kSiteFromDenseV, unit, 0u};
+  // U'_k = w_c / sqrt(sigma_c) (zero past the content's rank)
+  for (int idx = t; idx < r * D; idx += 256) {
+    const int kk = idx / D, i = idx - kk * D;
+    const int c = sel[kk];
+    const double sc = sig[c];
+    const double v = sc > sfloor ? W[c * LDW + i] / sqrt(sc) : 0.0;
+    Ub[static_cast<int64_t>(kk) * D + i] = round_store<FDT>(static_cast<float>(v), RU, kk, i);
+  }
+  // V'_k = C^T w_c / sigma_c^(3/2): thread j (value channel) of half h takes k = h, h + 2, ...
+  {
+    const int j = t & (D - 1), h = t >> 7;
+    double acc[32];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) acc[q] = 0.0;
+    const double vj = static_cast<double>(svb[j]);
+    for (int i = 0; i < D; ++i) {
+      const double cij = static_cast<double>(Sd[i * D + j]) - static_cast<double>(sa[i]) * vj;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const int kk = h + 2 * q;
+        if (kk < r) acc[q] = fma(cij, W[sel[kk] * LDW + i], acc[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const int kk = h + 2 * q;
+      if (kk < r) {
+        const double sc = sig[sel[kk]];
+        const double v = sc > sfloor ? acc[q] / (sc * sqrt(sc)) : 0.0;
+        Vb[static_cast<int64_t>(kk) * D + j] = round_store<FDT>(static_cast<float>(v), RV, kk, j);
+      }
     }
   }
   // decay scales 1, sink coefficients 0, window count 0, m = r
@@ -837,31 +876,24 @@ KFn pick_f(int dt, size_t* lds) {
   return k_from_dense<DK, DV, 0>;
 }
 KFn pick_from_dense(const seed_shape& sh, size_t* lds) {
-  if (sh.d_k == 128 && sh.d_v == 128) return pick_f<128, 128>(sh.factor_dtype, lds);
+  if (sh.d_k == 128 && sh.d_v == 128) {
+    if (sh.factor_dtype == SEED_BF16) { *lds = FDJ<1>::LDS; return k_from_dense_jacobi<1>; }
+    if (sh.factor_dtype == SEED_F16) { *lds = FDJ<2>::LDS; return k_from_dense_jacobi<2>; }
+    *lds = FDJ<0>::LDS;
+    return k_from_dense_jacobi<0>;
+  }
   if (sh.d_k == 128 && sh.d_v == 64) return pick_f<128, 64>(sh.factor_dtype, lds);
   if (sh.d_k == 64 && sh.d_v == 128) return pick_f<64, 128>(sh.factor_dtype, lds);
   if (sh.d_k == 64 && sh.d_v == 64) return pick_f<64, 64>(sh.factor_dtype, lds);
   return nullptr;
 }
 
-// The dynamic-LDS limit is raised once per kernel and device (the first launch), so that
-// later launches, including those recorded into a HIP graph, issue nothing but the launch.
+// The dynamic-LDS limit of a kernel that takes more than 64 KB is set before each of its
+// launches (a host-side attribute of the kernel on the current device: no stream work, and no
+// state kept by the library).
 hipError_t raise_lds_limit(KFn fn, size_t lds) {
-  struct Entry { KFn fn; int dev; };
-  static Entry done[64];
-  static int n_done = 0;
-  static std::mutex mu;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < n_done; ++i)
-    if (done[i].fn == fn && done[i].dev == dev) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  if (n_done < 64) done[n_done++] = Entry{fn, dev};
-  return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(lds));
 }
 
 hipError_t launch_big_lds(KFn fn, size_t lds, int64_t units, const CompressArgs& a, hipStream_t s) {
@@ -872,9 +904,8 @@ hipError_t launch_big_lds(KFn fn, size_t lds, int64_t units, const CompressArgs&
 }
 }  // namespace
 
-static_assert(FD<128, 128, 0>::LDS <= 160 * 1024 && FD<128, 64, 0>::LDS <= 160 * 1024 &&
-              FD<64, 128, 0>::LDS <= 160 * 1024 && FD<64, 64, 0>::LDS <= 160 * 1024 &&
-              FD<128, 128, 1>::LDS <= 160 * 1024, "from_dense LDS budget");
+static_assert(FD<128, 64, 0>::LDS <= 160 * 1024 && FD<64, 128, 0>::LDS <= 160 * 1024 &&
+              FD<64, 64, 0>::LDS <= 160 * 1024 && FDJ<0>::LDS <= 160 * 1024, "from_dense LDS budget");
 static_assert(compress_lds_bytes<128, 0>() <= 160 * 1024, "compress LDS budget");
 
 bool compress_supported(const seed_shape& sh) {
@@ -899,6 +930,6 @@ hipError_t launch_from_dense(const seed_shape& sh, const CompressArgs& a, hipStr
   return launch_big_lds(fn, lds, a.units, a, s);
 }
 
-int32_t from_dense_iterations() { return kFromDenseIters; }
+int32_t from_dense_iterations() { return kJacobiMaxSweeps; }
 
 }  // namespace seed
