@@ -605,12 +605,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   }
 
   // ---- Householder tridiagonalisation, the reflectors kept in the registers they zero ---------
-  // From step 16 qt on, v and w vanish on rows (and registers) below 16 qt, so block qt of
-  // the steps works on registers 16 qt.. only.
+  // From step 8 qt on, v and w vanish on rows (and registers) below 8 qt, so block qt of the
+  // steps works on registers 8 qt.. only.
 #pragma unroll
-  for (int qt = 0; qt < N / 16; ++qt) {
-    const int c0 = 4 * qt;                       // first float4 block of registers touched
-    for (int j = 16 * qt; j < (qt == N / 16 - 1 ? N - 2 : 16 * qt + 16); ++j) {
+  for (int qt = 0; qt < N / 8; ++qt) {
+    const int c0 = 2 * qt;                       // first float4 block of registers touched
+    for (int j = 8 * qt; j < (qt == N / 8 - 1 ? N - 2 : 8 * qt + 8); ++j) {
       const float colj = MGET(Bm, j);
       const bool tr = row > j;
       const float x = tr ? colj : 0.f;
@@ -632,10 +632,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       if (t == 0.f) continue;  // uniform
       S.bvw[row] = v;
       wave_lds_sync();
+      // every read of a step is issued before its arithmetic: the broadcast reads are what a
+      // step waits on, and v is kept in registers for the update
+      float4 vb[N / 4];
+#pragma unroll
+      for (int c4 = c0; c4 < N / 4; ++c4) vb[c4] = reinterpret_cast<const float4*>(S.bvw)[c4];
+      __builtin_amdgcn_sched_barrier(0);
       float p4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c4 = c0; c4 < N / 4; ++c4) {
-        const float4 b4 = reinterpret_cast<const float4*>(S.bvw)[c4];
+        const float4 b4 = vb[c4];
         p4[0] += MGET(Bm, 4 * c4 + 0) * b4.x;
         p4[1] += MGET(Bm, 4 * c4 + 1) * b4.y;
         p4[2] += MGET(Bm, 4 * c4 + 2) * b4.z;
@@ -647,10 +653,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       const float w = tr ? p - K * v : 0.f;
       (S.bvw + N)[row] = w;
       wave_lds_sync();
+      float4 wb[N / 4];
+#pragma unroll
+      for (int c4 = c0; c4 < N / 4; ++c4) wb[c4] = reinterpret_cast<const float4*>((S.bvw + N))[c4];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c4 = c0; c4 < N / 4; ++c4) {
-        const float4 b4 = reinterpret_cast<const float4*>(S.bvw)[c4];
-        const float4 w4 = reinterpret_cast<const float4*>((S.bvw + N))[c4];
+        const float4 b4 = vb[c4];
+        const float4 w4 = wb[c4];
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ww[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -823,6 +833,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   // cluster give nearly the same vector): it is dropped, as dividing by its tiny residual would
   // blow rounding noise up into every direction.
   constexpr float kDep = 1e-4f;
+  // The twisted factorisation leaves two vectors orthogonal up to about the core's rounding over
+  // the gap between their eigenvalues, which for a gap above kClus times the largest is far
+  // below the factor formats' resolution. So Gram-Schmidt runs only within clusters: runs of
+  // consecutive eigenvalues (lane c32 holds the c32-th largest) whose gaps are at most kClus
+  // times the largest. Bit c of sb is set when eigenvalue c starts a cluster.
+  constexpr float kClus = 1e-3f;
+  uint64_t sb;
+  {
+    const float lp = __shfl(lam, lane - 1);
+    const bool start = c32 == 0 || !(lp - lam <= kClus * lmax);
+    sb = __ballot(start && h == 0);
+  }
   for (int c = 0; c < rl; c += 2) {
     const bool pair = c + 1 < rl;  // uniform
     float n4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -830,6 +852,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     for (int s = 0; s < N / 2; ++s) n4[s & 3] += Y[s] * Y[s];
     float nn = (n4[0] + n4[1]) + (n4[2] + n4[3]);
     nn += partner(nn);
+    // nothing to orthogonalise: c + 1 starts a cluster (or there is none), and so does c + 2
+    if ((!pair || ((sb >> (c + 1)) & 1ull)) && (c + 2 >= rl || ((sb >> (c + 2)) & 1ull))) {  // uniform
+      if (c32 == c || (pair && c32 == c + 1)) ys = nn > kDep ? 1.f / sqrtf(nn) : 0.f;
+      continue;
+    }
     if (c32 == c || c32 == c + 1) {
       float* buf = (c32 == c ? S.y2 : S.bvw) + N * h;
 #pragma unroll
@@ -845,6 +872,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       ya[4 * s4] = a4.x; ya[4 * s4 + 1] = a4.y; ya[4 * s4 + 2] = a4.z; ya[4 * s4 + 3] = a4.w;
       yb[4 * s4] = b4.x; yb[4 * s4 + 1] = b4.y; yb[4 * s4 + 2] = b4.z; yb[4 * s4 + 3] = b4.w;
     }
+    __builtin_amdgcn_sched_barrier(0);
     float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < N / 2; ++s) {
@@ -884,40 +912,46 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   // (i % 2) 32 + i / 2, so that each lane half reads its parity as 8 float4.
   {
     const int pos = (row & 1) * (N / 2) + (row >> 1);
-    for (int j = N - 3; j >= 0; j -= 2) {
-      const bool two = j >= 1;  // uniform
-      const float t1 = S.tau[j];
-      const float t0 = two ? S.tau[j - 1] : 0.f;
-      if (t1 == 0.f && t0 == 0.f) continue;  // uniform
-      const float v1 = MGET(Bm, j);
-      const float v0 = two ? MGET(Bm, j - 1) : 0.f;
-      const float kap = uni(rsum<N>(v0 * v1));
-      S.y2[pos] = v1;
-      S.bvw[pos] = v0;
-      wave_lds_sync();
-      float a1[N / 2], a0[N / 2];
+    // the pairs (j - 1, j) with j in [16 qb, 16 qb + 16) touch rows 16 qb.. only: slots 8 qb..
 #pragma unroll
-      for (int s4 = 0; s4 < N / 8; ++s4) {
-        const float4 x4 = reinterpret_cast<const float4*>(S.y2 + (N / 2) * h)[s4];
-        const float4 z4 = reinterpret_cast<const float4*>(S.bvw + (N / 2) * h)[s4];
-        a1[4 * s4] = x4.x; a1[4 * s4 + 1] = x4.y; a1[4 * s4 + 2] = x4.z; a1[4 * s4 + 3] = x4.w;
-        a0[4 * s4] = z4.x; a0[4 * s4 + 1] = z4.y; a0[4 * s4 + 2] = z4.z; a0[4 * s4 + 3] = z4.w;
+    for (int qb = N / 16 - 1; qb >= 0; --qb) {
+      const int s40 = 2 * qb;   // first float4 of the slots touched
+      for (int j = (qb == N / 16 - 1 ? N - 3 : 16 * qb + 15); j >= 16 * qb; j -= 2) {
+        const bool two = j >= 1;  // uniform
+        const float t1 = S.tau[j];
+        const float t0 = two ? S.tau[j - 1] : 0.f;
+        if (t1 == 0.f && t0 == 0.f) continue;  // uniform
+        const float v1 = MGET(Bm, j);
+        const float v0 = two ? MGET(Bm, j - 1) : 0.f;
+        const float kap = uni(rsum<N>(v0 * v1));
+        S.y2[pos] = v1;
+        S.bvw[pos] = v0;
+        wave_lds_sync();
+        float a1[N / 2], a0[N / 2];
+#pragma unroll
+        for (int s4 = s40; s4 < N / 8; ++s4) {
+          const float4 x4 = reinterpret_cast<const float4*>(S.y2 + (N / 2) * h)[s4];
+          const float4 z4 = reinterpret_cast<const float4*>(S.bvw + (N / 2) * h)[s4];
+          a1[4 * s4] = x4.x; a1[4 * s4 + 1] = x4.y; a1[4 * s4 + 2] = x4.z; a1[4 * s4 + 3] = x4.w;
+          a0[4 * s4] = z4.x; a0[4 * s4 + 1] = z4.y; a0[4 * s4 + 2] = z4.z; a0[4 * s4 + 3] = z4.w;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 4 * s40; s < N / 2; ++s) {
+          p4[s & 3] += a1[s] * Y[s];
+          q4[s & 3] += a0[s] * Y[s];
+        }
+        float g1 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+        float g0 = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+        g1 += partner(g1);
+        g0 += partner(g0);
+        const float f1 = t1 * g1;
+        const float f0 = t0 * (g0 - kap * f1);
+#pragma unroll
+        for (int s = 4 * s40; s < N / 2; ++s) Y[s] = fmaf(-f0, a0[s], fmaf(-f1, a1[s], Y[s]));
+        wave_lds_sync();
       }
-      float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < N / 2; ++s) {
-        p4[s & 3] += a1[s] * Y[s];
-        q4[s & 3] += a0[s] * Y[s];
-      }
-      float g1 = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-      float g0 = (q4[0] + q4[1]) + (q4[2] + q4[3]);
-      g1 += partner(g1);
-      g0 += partner(g0);
-      const float f1 = t1 * g1;
-      const float f0 = t0 * (g0 - kap * f1);
-#pragma unroll
-      for (int s = 0; s < N / 2; ++s) Y[s] = fmaf(-f0, a0[s], fmaf(-f1, a1[s], Y[s]));
-      wave_lds_sync();
     }
   }
 
