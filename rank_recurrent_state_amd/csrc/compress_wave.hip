@@ -532,47 +532,77 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   }
 
   // ---- pivoted Cholesky of G_U (L column s into column p_s of the LDS copy) --------------------
-  // The rank-one update of step s - 1 is applied to the registers during step s (its vector read
-  // back from the other LDS buffer), so that it overlaps the next pivot search; the pivot column
-  // of step s gets that update on its own: col = G[:, p] - l_{s-1} l_{s-1}[p].
+  // In panels of kPanel steps. Within a panel the Gram is not updated: the pivot search needs
+  // only the diagonal d (kept exactly, d -= l^2), and the pivot column is corrected for the
+  // panel's earlier columns (kept one entry per lane in lp) by one readlane and one FMA each.
+  // At the end of a panel its columns update the whole Gram at once, G -= Lp Lp^T, by MFMA
+  // 32x32x2 (two columns per K-step, one 32-row tile block at a time, subtracted row by row).
+  // A step thus reads no broadcast vector from LDS, which is what a rank-one update per step
+  // waited on.
   float d = du * (bal * bal);
   uint64_t chosen = 0;
   {
+    constexpr int kPanel = 8;
     const float tol = uni(kPivTol * wmax(d));
-    float lprev = 0.f;
-    for (int s = 0; s < N; ++s) {
-      const bool was = (chosen >> row) & 1ull;
-      // d is finite; with N = 32 the pivot is taken among lanes 0..31 (lanes 32.. hold copies)
-      const int key = (!was && d > 0.f && (N == 64 || lane < 32)) ? __float_as_int(d) : -1;
-      const int kmax = __builtin_amdgcn_readfirstlane(wmax_key(key));
-      const float vmax = __int_as_float(kmax);
-      if (kmax < 0 || !(vmax > tol) || !(tol > 0.f)) break;  // uniform
-      const uint64_t hit = __ballot(key == kmax);
-      const int p = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
-      const float rp = __builtin_amdgcn_rsqf(vmax);
-      const float piv = vmax * rp;
-      const float col = MGET(GU, p) - lprev * bcast(lprev, p);
-      float l = was ? 0.f : col * rp;
-      if (row == p) l = piv;
-      S.bvw[N * (s & 1) + row] = l;
-      S.Lp[row * LDL + p] = l;
-      if (s > 0) {  // uniform: the deferred update of step s - 1
-        const float* prv = S.bvw + N * ((s - 1) & 1);
+    bool done = !(tol > 0.f);
+    for (int pb = 0; pb < N / kPanel && !done; ++pb) {  // uniform
+      float lp[kPanel];
 #pragma unroll
-        for (int c4 = 0; c4 < N / 4; ++c4) {
-          const float4 b4 = reinterpret_cast<const float4*>(prv)[c4];
-          const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+      for (int k = 0; k < kPanel; ++k) lp[k] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = 4 * c4 + e;
-            MSET(GU, c, fmaf(-lprev, bb[e], MGET(GU, c)));
+      for (int k = 0; k < kPanel; ++k) {
+        if (done) break;  // uniform
+        const bool was = (chosen >> row) & 1ull;
+        // d is finite; with N = 32 the pivot is taken among lanes 0..31 (lanes 32.. hold copies)
+        const int key = (!was && d > 0.f && (N == 64 || lane < 32)) ? __float_as_int(d) : -1;
+        const int kmax = __builtin_amdgcn_readfirstlane(wmax_key(key));
+        const float vmax = __int_as_float(kmax);
+        if (kmax < 0 || !(vmax > tol)) {  // uniform
+          done = true;
+          break;
+        }
+        const uint64_t hit = __ballot(key == kmax);
+        const int p = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
+        const float rp = __builtin_amdgcn_rsqf(vmax);
+        const float piv = vmax * rp;
+        float col = MGET(GU, p);
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) col = fmaf(-lp[k2], bcast(lp[k2], p), col);
+        float l = was ? 0.f : col * rp;
+        if (row == p) l = piv;
+        S.Lp[row * LDL + p] = l;
+        lp[k] = l;
+        d -= l * l;
+        chosen |= 1ull << p;
+      }
+      if (done) break;  // uniform: the Gram is not needed once the factorisation stops
+#pragma unroll
+      for (int I = 0; I < N / 32; ++I) {
+        f32x16 t[2] = {zero16(), zero16()};
+#pragma unroll
+        for (int s2 = 0; s2 < kPanel / 2; ++s2) {
+          float x = lp[2 * s2], y = lp[2 * s2 + 1];
+          swap32(x, y);   // .x: rows of block 0, .y: block 1 (as rows_operand)
+          const float aI = I == 0 ? x : y;
+          t[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(aI, x, t[0], 0, 0, 0);
+          if constexpr (N == 64) t[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(aI, y, t[1], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int rho = 32 * I + 8 * (j >> 2) + (j & 3);
+          if constexpr (N == 64) {
+            float x = t[0][j], y = t[1][j];
+            swap32(x, y);
+            MSET(GU, rho, MGET(GU, rho) - x);
+            MSET(GU, rho + 4, MGET(GU, rho + 4) - y);
+          } else {
+            float x = t[0][j], y = t[0][j];
+            swap32(x, y);
+            MSET(GU, rho, MGET(GU, rho) - x);
+            MSET(GU, rho + 4, MGET(GU, rho + 4) - y);
           }
         }
       }
-      d -= l * l;
-      chosen |= 1ull << p;
-      lprev = l;
-      wave_lds_sync();
     }
   }
   const int k = __builtin_popcountll(chosen);
