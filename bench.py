@@ -46,7 +46,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 # Measured HBM traffic of the decode kernel (two rocprofv3 counter runs, scaled by a calibration
 # copy); used only while the kernel sources still hash to the digest recorded with it.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_gdn-stack36_hbm_traffic.txt")
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"k_decode_{workload}_hbm_traffic.txt")
 DECODE_SOURCES = ("rank_recurrent_state_amd/csrc/decode.hip", "rank_recurrent_state_amd/csrc/common.hpp",
                   "rank_recurrent_state_amd/csrc/kernels.hpp")
 MIN_WINDOWS = 5
@@ -113,7 +114,7 @@ def decode_source_digest() -> str:
 def recorded_traffic(workload: str):
     """Bytes per decode launch from the counter profile, if it matches the current sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
     except OSError:
         return None
