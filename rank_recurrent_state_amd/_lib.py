@@ -80,10 +80,16 @@ def hip_runtimes_mapped() -> list:
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m rank_recurrent_state_amd.build`")
+    # libseed binds to whichever HIP runtime the process already holds. Torch's wheel bundles
+    # its own copy, and the tensors handed to the library are torch's: torch is imported first,
+    # so that libseed's libamdhip64 dependency resolves to that copy. Loaded first, libseed would
+    # pull in the system runtime, torch would then map its own, and every launch would fail
+    # with tensors of one runtime handed to the other.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
-    # libseed binds to whichever HIP runtime the process already holds (torch's, when torch is
-    # imported first). Two copies would give two sets of streams and device state, and a
-    # stream of one handed to the other: refuse that outright.
+    # Two copies would give two sets of streams and device state, and a stream of one handed to
+    # the other: refuse that outright.
     rts = hip_runtimes_mapped()
     if len(rts) > 1:
         raise ImportError(f"more than one HIP runtime is mapped into this process: {rts}")

@@ -192,6 +192,24 @@ def test_one_hip_runtime_is_mapped():
     assert len(rrs.hip_runtimes_mapped()) <= 1
 
 
+def test_one_hip_runtime_when_the_package_is_imported_before_torch():
+    # the binding hands torch tensors to libseed, so libseed must bind to torch's HIP runtime
+    # even when the package is loaded first (in a fresh process: torch not yet imported)
+    import subprocess
+    import sys
+
+    _lib()
+    code = ("import rank_recurrent_state_amd as rrs\n"
+            "rrs.seed_version()\n"
+            "import torch\n"
+            "from rank_recurrent_state_amd import _lib\n"
+            "print(len(_lib.hip_runtimes_mapped()))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
+
+
 def test_normed_step_rejects_bad_norm_on_the_host():
     rrs = _lib()
     f = _Fake()
