@@ -408,12 +408,14 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
 // (two independent recurrences interleaved). e2 is floored at FLT_MIN, so a zero pivot gives an
 // infinite next pivot of the opposite sign (IEEE arithmetic) instead of NaN; pivots are counted
 // by their sign bit, so that +0 followed by -inf and -0 followed by +inf count once each.
+// The tridiagonal comes in registers (every lane holds all of it): read from LDS inside the
+// recurrence, each pair of steps waited for an LDS round trip.
 template <int N>
-__device__ __forceinline__ void sturm2(const float* __restrict__ dg, const float* __restrict__ e2, const float x1,
+__device__ __forceinline__ void sturm2(const float (&dg)[N], const float (&e2)[N], const float x1,
                                        const float x2, int& c1, int& c2) {
   float q1 = dg[0] - x1, q2 = dg[0] - x2;
   uint32_t n1 = __float_as_uint(q1) >> 31, n2 = __float_as_uint(q2) >> 31;
-#pragma unroll 8
+#pragma unroll
   for (int i = 1; i < N; ++i) {
     const float di = dg[i], ei = e2[i - 1];
     q1 = (di - x1) - ei * __builtin_amdgcn_rcpf(q1);
@@ -728,6 +730,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     lo -= pad;
     hi += pad;
     wave_lds_sync();
+    // the whole tridiagonal in registers for the Sturm recurrences (this phase has them free)
+    float dgr[N], e2r[N];
+#pragma unroll
+    for (int c4 = 0; c4 < N / 4; ++c4) {
+      const float4 d4 = reinterpret_cast<const float4*>(S.dg)[c4];
+      const float4 f4 = reinterpret_cast<const float4*>(S.e2)[c4];
+      dgr[4 * c4] = d4.x; dgr[4 * c4 + 1] = d4.y; dgr[4 * c4 + 2] = d4.z; dgr[4 * c4 + 3] = d4.w;
+      e2r[4 * c4] = f4.x; e2r[4 * c4 + 1] = f4.y; e2r[4 * c4 + 2] = f4.z; e2r[4 * c4 + 3] = f4.w;
+    }
     const int target = N - 1 - c32;  // the c32-th largest is the (N - 1 - c32)-th smallest
     {
       // first bracket from a shared grid of 128 points (two per lane, increasing with the lane):
@@ -736,7 +747,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       const float x1 = lo + static_cast<float>(2 * lane + 1) * step;
       const float x2 = lo + static_cast<float>(2 * lane + 2) * step;
       int n1, n2;
-      sturm2<N>(S.dg, S.e2, x1, x2, n1, n2);
+      sturm2<N>(dgr, e2r, x1, x2, n1, n2);
       float nlo = lo, nhi = hi;
       for (int g = 0; g < rr; ++g) {
         const int t = N - 1 - g;
@@ -754,7 +765,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       const float x1 = lo + static_cast<float>(2 * h + 1) * step;
       const float x2 = lo + static_cast<float>(2 * h + 2) * step;
       int n1, n2;
-      sturm2<N>(S.dg, S.e2, x1, x2, n1, n2);
+      sturm2<N>(dgr, e2r, x1, x2, n1, n2);
       const float clo = fmaxf(n1 <= target ? x1 : -FLT_MAX, n2 <= target ? x2 : -FLT_MAX);
       const float chi = fminf(n1 > target ? x1 : FLT_MAX, n2 > target ? x2 : FLT_MAX);
       lo = fmaxf(lo, fmaxf(clo, partner(clo)));
