@@ -950,33 +950,45 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   // ---- back-transformation Y <- H_0 H_1 ... H_{N-3} Y, two reflectors at a time --------------
   // H_{j-1} H_j Y = Y - t_j v_j g1 - t_{j-1} v_{j-1} (g0 - t_j kappa g1) with g1 = v_j^T Y,
   // g0 = v_{j-1}^T Y and kappa = v_{j-1}^T v_j. Vectors go through LDS with entry i at
-  // (i % 2) 32 + i / 2, so that each lane half reads its parity as 8 float4.
+  // (i % 2) 32 + i / 2, so that each lane half reads its parity as 8 float4. The loop is
+  // software-pipelined over two buffers: once a pair's reads are issued, the next pair's
+  // reflectors go to the other buffer and their kappa is reduced, so that neither the LDS round
+  // trip nor the reduction waits in front of the pair's products. A pair whose two taus are zero
+  // (columns that needed no reflection) is applied as it stands: f0 = f1 = 0 leave Y unchanged.
   {
     const int pos = (row & 1) * (N / 2) + (row >> 1);
+    float nt1, nt0, nkap;
+#define CW_PREP(J, B)                                                                              \
+  do {                                                                                             \
+    nt1 = S.tau[J];                                                                                \
+    nt0 = S.tau[(J) - 1];                                                                          \
+    const float pv1 = MGET(Bm, J), pv0 = MGET(Bm, (J) - 1);                                        \
+    nkap = uni(rsum<N>(pv0 * pv1));                                                                \
+    (S.y2 + (B) * N)[pos] = pv1;                                                                   \
+    (S.bvw + (B) * N)[pos] = pv0;                                                                  \
+  } while (0)
+    CW_PREP(N - 3, 0);
+    int buf = 0;
     // the pairs (j - 1, j) with j in [16 qb, 16 qb + 16) touch rows 16 qb.. only: slots 8 qb..
 #pragma unroll
     for (int qb = N / 16 - 1; qb >= 0; --qb) {
       const int s40 = 2 * qb;   // first float4 of the slots touched
       for (int j = (qb == N / 16 - 1 ? N - 3 : 16 * qb + 15); j >= 16 * qb; j -= 2) {
-        const bool two = j >= 1;  // uniform
-        const float t1 = S.tau[j];
-        const float t0 = two ? S.tau[j - 1] : 0.f;
-        if (t1 == 0.f && t0 == 0.f) continue;  // uniform
-        const float v1 = MGET(Bm, j);
-        const float v0 = two ? MGET(Bm, j - 1) : 0.f;
-        const float kap = uni(rsum<N>(v0 * v1));
-        S.y2[pos] = v1;
-        S.bvw[pos] = v0;
-        wave_lds_sync();
+        const float t1 = nt1, t0 = nt0, kap = nkap;
+        wave_lds_sync();   // this pair's vectors, written one iteration ahead, are visible
+        const float* __restrict__ y1p = S.y2 + buf * N + (N / 2) * h;
+        const float* __restrict__ y0p = S.bvw + buf * N + (N / 2) * h;
         float a1[N / 2], a0[N / 2];
 #pragma unroll
         for (int s4 = s40; s4 < N / 8; ++s4) {
-          const float4 x4 = reinterpret_cast<const float4*>(S.y2 + (N / 2) * h)[s4];
-          const float4 z4 = reinterpret_cast<const float4*>(S.bvw + (N / 2) * h)[s4];
+          const float4 x4 = reinterpret_cast<const float4*>(y1p)[s4];
+          const float4 z4 = reinterpret_cast<const float4*>(y0p)[s4];
           a1[4 * s4] = x4.x; a1[4 * s4 + 1] = x4.y; a1[4 * s4 + 2] = x4.z; a1[4 * s4 + 3] = x4.w;
           a0[4 * s4] = z4.x; a0[4 * s4 + 1] = z4.y; a0[4 * s4 + 2] = z4.z; a0[4 * s4 + 3] = z4.w;
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (j >= 3) CW_PREP(j - 2, buf ^ 1);  // uniform: the next pair, possibly the next block's
+        buf ^= 1;
         float p4[4] = {0.f, 0.f, 0.f, 0.f}, q4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 4 * s40; s < N / 2; ++s) {
@@ -991,9 +1003,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
         const float f0 = t0 * (g0 - kap * f1);
 #pragma unroll
         for (int s = 4 * s40; s < N / 2; ++s) Y[s] = fmaf(-f0, a0[s], fmaf(-f1, a1[s], Y[s]));
-        wave_lds_sync();
       }
     }
+#undef CW_PREP
+    wave_lds_sync();
   }
 
   const float q4 = live ? sqrtf(sqrtf(lam * bs)) : 1.f;   // of the unscaled eigenvalue
