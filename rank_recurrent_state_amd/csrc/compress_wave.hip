@@ -25,7 +25,7 @@
 //   B = L^T G_V L         MFMA 32x32x2 fp32, G_V and then L^T G_V from registers, L from LDS;
 //   eigenpairs of B       Householder tridiagonalisation in registers (reflectors kept in the
 //                         registers they zero), the r largest eigenvalues by Sturm counts
-//                         (a 128-point grid shared by all, then 5-section), one
+//                         (a 128-point grid shared by all, then trisection), one
 //                         eigenvector per eigenvalue from a twisted factorisation (computed on
 //                         both lanes of the pair, each keeping the even or the odd entries),
 //                         modified Gram-Schmidt, back-transformation by the reflectors;
@@ -54,7 +54,7 @@ namespace cw {
 // 64-lane form; sums over rows then stop at 32 lanes.
 constexpr int RX = 32;          // maximum rank on this path
 constexpr int kGrid = 128;      // points of the shared Sturm grid (two per lane)
-constexpr int NSEC = 7;         // 5-section steps after the 128-point grid (129 * 5^7 ~ 1e7)
+constexpr int NSEC = 11;        // trisection steps after the 128-point grid (129 * 3^11 ~ 2.3e7)
 constexpr float kPivTol = 1e-7f;
 constexpr float kReduceFloor = 1e-30f;  // squared column norm below which no reflector is built
 // Eigenvalues of the core below kEigFloor times the largest give zero columns. The fp32 core
@@ -427,6 +427,19 @@ __device__ __forceinline__ void sturm2(const float (&dg)[N], const float (&e2)[N
   c2 = static_cast<int>(n2);
 }
 
+// The Sturm count at one shift (the same recurrence and counting as sturm2).
+template <int N>
+__device__ __forceinline__ int sturm1(const float (&dg)[N], const float (&e2)[N], const float x) {
+  float q = dg[0] - x;
+  uint32_t n = __float_as_uint(q) >> 31;
+#pragma unroll
+  for (int i = 1; i < N; ++i) {
+    q = (dg[i] - x) - e2[i - 1] * __builtin_amdgcn_rcpf(q);
+    n += __float_as_uint(q) >> 31;
+  }
+  return static_cast<int>(n);
+}
+
 }  // namespace cw
 
 // The draws of one group of eight elements, as a call: inlined sixteen times per factor it
@@ -759,15 +772,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       lo = nlo;
       hi = nhi;
     }
+    // trisection: the two interior points of the bracket, one Sturm count per lane (lane half h
+    // probes point h + 1). Per Sturm count it narrows the bracket the most of the k-sections a
+    // lane pair can run (a factor 3 for one count per lane; 5-section gives 5 for two), and the
+    // phase is bound by the issue of the counts.
     for (int it = 0; it < NSEC; ++it) {
-      // four interior points of the bracket: lane half h probes points 2 h + 1 and 2 h + 2
-      const float step = (hi - lo) * 0.2f;
-      const float x1 = lo + static_cast<float>(2 * h + 1) * step;
-      const float x2 = lo + static_cast<float>(2 * h + 2) * step;
-      int n1, n2;
-      sturm2<N>(dgr, e2r, x1, x2, n1, n2);
-      const float clo = fmaxf(n1 <= target ? x1 : -FLT_MAX, n2 <= target ? x2 : -FLT_MAX);
-      const float chi = fminf(n1 > target ? x1 : FLT_MAX, n2 > target ? x2 : FLT_MAX);
+      const float step = (hi - lo) * (1.f / 3.f);
+      const float x = lo + static_cast<float>(h + 1) * step;
+      const int n = sturm1<N>(dgr, e2r, x);
+      const float clo = n <= target ? x : -FLT_MAX;
+      const float chi = n > target ? x : FLT_MAX;
       lo = fmaxf(lo, fmaxf(clo, partner(clo)));
       hi = fminf(hi, fminf(chi, partner(chi)));
     }
