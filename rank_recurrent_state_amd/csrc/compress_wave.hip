@@ -25,7 +25,7 @@
 //   B = L^T G_V L         MFMA 32x32x2 fp32, G_V and then L^T G_V from registers, L from LDS;
 //   eigenpairs of B       Householder tridiagonalisation in registers (reflectors kept in the
 //                         registers they zero), the r largest eigenvalues by Sturm counts
-//                         (a 128-point grid shared by all, then trisection), one
+//                         (a 64-point grid shared by all, then trisection), one
 //                         eigenvector per eigenvalue from a twisted factorisation (computed on
 //                         both lanes of the pair, each keeping the even or the odd entries),
 //                         modified Gram-Schmidt, back-transformation by the reflectors;
@@ -53,8 +53,8 @@ namespace cw {
 // c + 32 hold the same row c, so that the MFMA tiles and the lane-pair phases keep their
 // 64-lane form; sums over rows then stop at 32 lanes.
 constexpr int RX = 32;          // maximum rank on this path
-constexpr int kGrid = 128;      // points of the shared Sturm grid (two per lane)
-constexpr int NSEC = 11;        // trisection steps after the 128-point grid (129 * 3^11 ~ 2.3e7)
+constexpr int kGrid = 64;       // points of the shared Sturm grid (one per lane)
+constexpr int NSEC = 11;        // trisection steps after the 64-point grid (65 * 3^11 ~ 1.15e7)
 constexpr float kPivTol = 1e-7f;
 constexpr float kReduceFloor = 1e-30f;  // squared column norm below which no reflector is built
 // Eigenvalues of the core below kEigFloor times the largest give zero columns. The fp32 core
@@ -404,30 +404,12 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
   }
 }
 
-// Sturm counts at two shifts: eigenvalues of the tridiagonal (dg, e2 = e^2) below x1 and x2
-// (two independent recurrences interleaved). e2 is floored at FLT_MIN, so a zero pivot gives an
-// infinite next pivot of the opposite sign (IEEE arithmetic) instead of NaN; pivots are counted
-// by their sign bit, so that +0 followed by -inf and -0 followed by +inf count once each.
-// The tridiagonal comes in registers (every lane holds all of it): read from LDS inside the
-// recurrence, each pair of steps waited for an LDS round trip.
-template <int N>
-__device__ __forceinline__ void sturm2(const float (&dg)[N], const float (&e2)[N], const float x1,
-                                       const float x2, int& c1, int& c2) {
-  float q1 = dg[0] - x1, q2 = dg[0] - x2;
-  uint32_t n1 = __float_as_uint(q1) >> 31, n2 = __float_as_uint(q2) >> 31;
-#pragma unroll
-  for (int i = 1; i < N; ++i) {
-    const float di = dg[i], ei = e2[i - 1];
-    q1 = (di - x1) - ei * __builtin_amdgcn_rcpf(q1);
-    q2 = (di - x2) - ei * __builtin_amdgcn_rcpf(q2);
-    n1 += __float_as_uint(q1) >> 31;
-    n2 += __float_as_uint(q2) >> 31;
-  }
-  c1 = static_cast<int>(n1);
-  c2 = static_cast<int>(n2);
-}
-
-// The Sturm count at one shift (the same recurrence and counting as sturm2).
+// The Sturm count at shift x: the number of eigenvalues of the tridiagonal (dg, e2 = e^2) below
+// x. e2 is floored at FLT_MIN, so a zero pivot gives an infinite next pivot of the opposite sign
+// (IEEE arithmetic) instead of NaN; pivots are counted by their sign bit, so that +0 followed by
+// -inf and -0 followed by +inf count once each. The tridiagonal comes in registers (every lane
+// holds all of it): read from LDS inside the recurrence, each pair of steps waited for an LDS
+// round trip.
 template <int N>
 __device__ __forceinline__ int sturm1(const float (&dg)[N], const float (&e2)[N], const float x) {
   float q = dg[0] - x;
@@ -754,17 +736,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     }
     const int target = N - 1 - c32;  // the c32-th largest is the (N - 1 - c32)-th smallest
     {
-      // first bracket from a shared grid of 128 points (two per lane, increasing with the lane):
-      // the points with at most t eigenvalues below them are a prefix of the grid
-      const float step = (hi - lo) * (1.f / 129.f);
-      const float x1 = lo + static_cast<float>(2 * lane + 1) * step;
-      const float x2 = lo + static_cast<float>(2 * lane + 2) * step;
-      int n1, n2;
-      sturm2<N>(dgr, e2r, x1, x2, n1, n2);
+      // first bracket from a shared grid of 64 points (one per lane, increasing with the lane):
+      // the points with at most t eigenvalues below them are a prefix of the grid. One count
+      // per lane here and then eleven trisection steps reach a finer bracket than two counts
+      // per lane and ten steps, for one count less.
+      const float step = (hi - lo) * (1.f / static_cast<float>(kGrid + 1));
+      const float x1 = lo + static_cast<float>(lane + 1) * step;
+      const int n1 = sturm1<N>(dgr, e2r, x1);
       float nlo = lo, nhi = hi;
       for (int g = 0; g < rr; ++g) {
         const int t = N - 1 - g;
-        const int cnt = __builtin_popcountll(__ballot(n1 <= t)) + __builtin_popcountll(__ballot(n2 <= t));
+        const int cnt = __builtin_popcountll(__ballot(n1 <= t));
         const float glo = cnt > 0 ? lo + static_cast<float>(cnt) * step : lo;
         const float ghi = cnt < kGrid ? lo + static_cast<float>(cnt + 1) * step : hi;
         if (c32 == g) { nlo = glo; nhi = ghi; }
