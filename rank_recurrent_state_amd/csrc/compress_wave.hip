@@ -288,22 +288,43 @@ struct Smem {
 };
 
 // Gram of the stored columns 0..m-1 (rows of length D, bf16), as row-per-lane registers. With
-// ROWSCALE the A operand carries gam^2 along d (KDA's per-channel lazy decay).
-template <int D, bool ROWSCALE, int N, int FDT>
-__device__ __forceinline__ M64 gram(const uint16_t* __restrict__ base, const int m, const float* __restrict__ gam) {
-  using MF = Mf16<FDT>;
-  using V8 = typename MF::V8;
+// ROWSCALE the A operand carries gam^2 along d (KDA's per-channel lazy decay). The column reads
+// are issued first, all of them (gram_load; the caller issues both factors' before either
+// product), and masked at their use: issued a few at a time beside the MFMAs, each group waited
+// for a memory round trip of its own.
+template <int D, int N>
+struct GramLoads {
+  uint4 u0[D / 16], u1[N == 64 ? D / 16 : 1];
+};
+
+template <int D, int N>
+__device__ __forceinline__ void gram_load(const uint16_t* __restrict__ base, const int m, GramLoads<D, N>& L) {
   const int lane = threadIdx.x;
   const int c0 = lane & 31, kh = lane >> 5;
   const bool ok0 = c0 < m, ok1 = N == 64 && c0 + 32 < m;
   const uint16_t* p0 = base + (ok0 ? c0 : 0) * D + 8 * kh;
   const uint16_t* p1 = base + (ok1 ? c0 + 32 : 0) * D + 8 * kh;
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) {
+    L.u0[k] = *reinterpret_cast<const uint4*>(p0 + 16 * k);
+    if constexpr (N == 64) L.u1[k] = *reinterpret_cast<const uint4*>(p1 + 16 * k);
+  }
+}
+
+template <int D, bool ROWSCALE, int N, int FDT>
+__device__ __forceinline__ M64 gram(const GramLoads<D, N>& L, const int m, const float* __restrict__ gam) {
+  using MF = Mf16<FDT>;
+  using V8 = typename MF::V8;
+  const int lane = threadIdx.x;
+  const int c0 = lane & 31, kh = lane >> 5;
+  const bool ok0 = c0 < m, ok1 = N == 64 && c0 + 32 < m;
   f32x16 t[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
 #pragma unroll
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    uint4 u0 = *reinterpret_cast<const uint4*>(p0 + k0);
+  for (int k = 0; k < D / 16; ++k) {
+    const int k0 = 16 * k;
+    uint4 u0 = L.u0[k];
     uint4 u1 = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (N == 64) u1 = *reinterpret_cast<const uint4*>(p1 + k0);
+    if constexpr (N == 64) u1 = L.u1[k];
     if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
     if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
     const V8 b0 = __builtin_bit_cast(V8, u0);
@@ -372,6 +393,22 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
 #pragma unroll
     for (int I = 0; I < NT; ++I) fold[I] = 0.f;
   }
+  // every column read is issued before the products (masked at its use): issued four at a time
+  // beside the MFMAs, each group waited for a memory round trip of its own
+  uint32_t raw[N / 2][NT / 2];
+#pragma unroll
+  for (int s = 0; s < N / 2; ++s) {
+    const int col = 2 * s + kh;
+    const uint16_t* p = base + (col < m ? col : 0) * D + NT * c;
+    if constexpr (NT == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      raw[s][0] = u.x;
+      raw[s][1] = u.y;
+    } else {
+      raw[s][0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s4 = 0; s4 < N / 8; ++s4) {
     float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -382,17 +419,9 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
       const int s = 4 * s4 + s1;
       const int col = 2 * s + kh;
       const bool ok = col < m;
-      const uint16_t* p = base + (ok ? col : 0) * D + NT * c;
       uint32_t w[2];
-      if constexpr (NT == 4) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p);
-        w[0] = ok ? u.x : 0u;
-        w[1] = ok ? u.y : 0u;
-      } else {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-        w[0] = ok ? u : 0u;
-        w[1] = 0u;
-      }
+      w[0] = ok ? raw[s][0] : 0u;
+      w[1] = (NT == 4 && ok) ? raw[s][NT / 2 - 1] : 0u;
 #pragma unroll
       for (int I = 0; I < NT; ++I) {
         const uint32_t wi = w[I >> 1];
@@ -495,8 +524,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   // ---- Grams of the stored columns -------------------------------------------------------------
   f32x32 GU_lo, GU_hi, GV_lo, GV_hi;
   {
-    const M64 gu = gram<DK, DIAG, N, FDT>(Ub, m, S.gam);
-    const M64 gv = gram<DV, false, N, FDT>(Vb, m, nullptr);
+    GramLoads<DK, N> lu;
+    GramLoads<DV, N> lv;
+    gram_load<DK, N>(Ub, m, lu);
+    gram_load<DV, N>(Vb, m, lv);
+    __builtin_amdgcn_sched_barrier(0);
+    const M64 gu = gram<DK, DIAG, N, FDT>(lu, m, S.gam);
+    const M64 gv = gram<DV, false, N, FDT>(lv, m, nullptr);
     GU_lo = gu.lo; GU_hi = gu.hi; GV_lo = gv.lo; GV_hi = gv.hi;
   }
 
@@ -1083,12 +1117,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
     const bool ok0 = c32 < m, ok1 = N == 64 && c32 + 32 < m;
     const uint16_t* p0 = Vb + (ok0 ? c32 : 0) * DV + 4 * NV * h;
     const uint16_t* p1 = Vb + (ok1 ? c32 + 32 : 0) * DV + 4 * NV * h;
+    // every read of V_s first (masked at its use), as in factor_times
+    uint4 r0[DV / 16], r1[N == 64 ? DV / 16 : 1];
 #pragma unroll
     for (int s = 0; s < DV / 16; ++s) {
       const int q = s / (NV / 2), u = s % (NV / 2);
       const int off = 8 * NV * q + 8 * u;
-      uint4 u0 = *reinterpret_cast<const uint4*>(p0 + off);
-      uint4 u1 = *reinterpret_cast<const uint4*>(p1 + off);
+      r0[s] = *reinterpret_cast<const uint4*>(p0 + off);
+      if constexpr (N == 64) r1[s] = *reinterpret_cast<const uint4*>(p1 + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < DV / 16; ++s) {
+      uint4 u0 = r0[s];
+      uint4 u1 = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (N == 64) u1 = r1[s];
       if (!ok0) u0 = make_uint4(0u, 0u, 0u, 0u);
       if (!ok1) u1 = make_uint4(0u, 0u, 0u, 0u);
       const uint4 bw4 = make_uint4(vw[4 * s], vw[4 * s + 1], vw[4 * s + 2], vw[4 * s + 3]);
@@ -1230,8 +1273,13 @@ __global__ __launch_bounds__(64) void k_energy_wave(const EnergyArgs A) {
   // content: the Grams (zero beyond m), then sum over rho of c_rho G_U[rho][col] G_V[rho][col]
   float content;
   {
-    const M64 gu = gram<DK, DIAG, N, FDT>(Ub, m, gam);
-    const M64 gv = gram<DV, false, N, FDT>(Vb, m, nullptr);
+    GramLoads<DK, N> lu;
+    GramLoads<DV, N> lv;
+    gram_load<DK, N>(Ub, m, lu);
+    gram_load<DV, N>(Vb, m, lv);
+    __builtin_amdgcn_sched_barrier(0);
+    const M64 gu = gram<DK, DIAG, N, FDT>(lu, m, gam);
+    const M64 gv = gram<DV, false, N, FDT>(lv, m, nullptr);
     const f32x32 GU_lo = gu.lo, GU_hi = gu.hi, GV_lo = gv.lo, GV_hi = gv.hi;
     float p = 0.f;
 #pragma unroll
