@@ -371,6 +371,37 @@ __device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, con
   return tiles_to_rows<N>(t);
 }
 
+// The column reads of factor_times, issued by the caller ahead of the product (all of them at
+// once, and as early as registers allow: issued four at a time beside the MFMAs, each group
+// waited for a memory round trip of its own). Lane (c, kh) reads the NT elements d = NT c ..
+// NT c + NT - 1 of column 2 s + kh for every K-step s (column 0 stands in past m; it is masked at
+// its use).
+template <int D, int N>
+struct FactorLoads {
+  uint32_t raw[N / 2][D / 64];
+};
+
+template <int D, int N>
+__device__ __forceinline__ void factor_load(const uint16_t* __restrict__ base, const int m, FactorLoads<D, N>& L) {
+  constexpr int NT = D / 32;
+  static_assert(NT == 2 || NT == 4, "d of 64 or 128");
+  const int lane = threadIdx.x;
+  const int c = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < N / 2; ++s) {
+    const int col = 2 * s + kh;
+    const uint16_t* p = base + (col < m ? col : 0) * D + NT * c;
+    if constexpr (NT == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      L.raw[s][0] = u.x;
+      L.raw[s][1] = u.y;
+    } else {
+      L.raw[s][0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Y = F X for F (D x 64: the stored bf16 columns 0..m-1 of a factor) and X given as MFMA
 // 32x32x2 B operands (rows 2 s + lane / 32 of column lane % 32). With NT = D / 32 tiles, row i
 // of tile I is d = NT i + I, so that one lane's A operands of a column are NT consecutive
@@ -378,37 +409,20 @@ __device__ __forceinline__ M64 times_L(const f32x32 X_lo, const f32x32 X_hi, con
 // d = NT (8 (j / 4) + 4 (lane / 32) + j % 4) + I.
 // With FOLD, the same A operands also give F f for the vector f (cf: f_j at (j % 2) N / 2 + j / 2):
 // fold[I] is lane half lane / 32's share of (F f)[NT (lane % 32) + I] (the other half's share is
-// in the partner lane).
+// in the partner lane). L holds the columns' reads, issued by factor_load.
 template <int D, int N, int FDT, bool FOLD = false>
-__device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, const int m, const float (&xop)[N / 2],
+__device__ __forceinline__ void factor_times(const FactorLoads<D, N>& L, const int m, const float (&xop)[N / 2],
                                              f32x16 (&y)[D / 32], const float* __restrict__ cf = nullptr,
                                              float* fold = nullptr) {
   constexpr int NT = D / 32;
-  static_assert(NT == 2 || NT == 4, "d of 64 or 128");
   const int lane = threadIdx.x;
-  const int c = lane & 31, kh = lane >> 5;
+  const int kh = lane >> 5;
 #pragma unroll
   for (int I = 0; I < NT; ++I) y[I] = zero16();
   if constexpr (FOLD) {
 #pragma unroll
     for (int I = 0; I < NT; ++I) fold[I] = 0.f;
   }
-  // every column read is issued before the products (masked at its use): issued four at a time
-  // beside the MFMAs, each group waited for a memory round trip of its own
-  uint32_t raw[N / 2][NT / 2];
-#pragma unroll
-  for (int s = 0; s < N / 2; ++s) {
-    const int col = 2 * s + kh;
-    const uint16_t* p = base + (col < m ? col : 0) * D + NT * c;
-    if constexpr (NT == 4) {
-      const uint2 u = *reinterpret_cast<const uint2*>(p);
-      raw[s][0] = u.x;
-      raw[s][1] = u.y;
-    } else {
-      raw[s][0] = *reinterpret_cast<const uint32_t*>(p);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s4 = 0; s4 < N / 8; ++s4) {
     float4 f4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -420,8 +434,8 @@ __device__ __forceinline__ void factor_times(const uint16_t* __restrict__ base, 
       const int col = 2 * s + kh;
       const bool ok = col < m;
       uint32_t w[2];
-      w[0] = ok ? raw[s][0] : 0u;
-      w[1] = (NT == 4 && ok) ? raw[s][NT / 2 - 1] : 0u;
+      w[0] = ok ? L.raw[s][0] : 0u;
+      w[1] = (NT == 4 && ok) ? L.raw[s][NT / 2 - 1] : 0u;
 #pragma unroll
       for (int I = 0; I < NT; ++I) {
         const uint32_t wi = w[I >> 1];
@@ -1078,7 +1092,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   uint32_t vw[16 * NV / 2];
   {
     f32x16 vt[NV];
-    factor_times<DV, N, FDT>(Vb, m, xop, vt);
+    FactorLoads<DV, N> fv;
+    factor_load<DV, N>(Vb, m, fv);
+    factor_times<DV, N, FDT>(fv, m, xop, vt);
     // elements d = NV i + (0 .. NV - 1) of column c32, i = 8 (j / 4) + 4 h + j % 4: the 8 / NV
     // values of j from a multiple of 8 / NV share one group of 8 (one draw call)
     uint4 dr = make_uint4(0u, 0u, 0u, 0u);
@@ -1112,6 +1128,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
   }
   vss += partner(vss);
   const float qu = (live && vss > 0.f) ? fminf(ql, 1.f / vss) : 0.f;
+  FactorLoads<DK, N> fu;   // U_s's reads for U', issued once W's products are
   {
     f32x16 w[2] = {zero16(), zero16()};
     const bool ok0 = c32 < m, ok1 = N == 64 && c32 + 32 < m;
@@ -1141,6 +1158,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       w[0] = MF::mfma(__builtin_bit_cast(V8, u0), bop, w[0]);
       if constexpr (N == 64) w[1] = MF::mfma(__builtin_bit_cast(V8, u1), bop, w[1]);
     }
+    factor_load<DK, N>(Ub, m, fu);
     // X_U = diag(colsc) W / |V'|^2 (U' = U_s D_c V_s^T V' / sigma), as B operands
 #pragma unroll
     for (int I = 0; I < NTI; ++I) {
@@ -1186,7 +1204,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(N == 64 ? 2 
       }
     }
     const float s0 = sc[0];
-    factor_times<DK, N, FDT, true>(Ub, m, xop, ut, S.cf, fold);
+    factor_times<DK, N, FDT, true>(fu, m, xop, ut, S.cf, fold);
 #pragma unroll
     for (int I = 0; I < NU; ++I) fold[I] += partner(fold[I]);
     if (h == 0) {
